@@ -1,0 +1,324 @@
+"""Pins of the CPU oracle: checks against what the pages and the mathematics fix,
+never against the oracle itself.
+
+Each ``pin_*`` takes an ``oracle.ref.Oracle`` and raises AssertionError when the
+oracle disagrees with:
+
+* values the pages print for worked examples (tests/golden/, each file citing
+  its page and section);
+* library routines for special cases (numpy's float16 conversions, torch's
+  bfloat16 conversions, torch's scaled_dot_product_attention in float64 on the
+  contiguous layout);
+* closed forms (one token, zero query, equal keys);
+* invariants (any permutation of physical blocks, a shared versus a copied
+  prefix, split-K versus unsplit, NaN in slots that no sequence owns);
+* an independent construction of the paged layout (``sequential_fill``).
+
+test_oracle_pins.py runs every pin on the real oracle; test_oracle_mutants.py
+plants plausible mistakes in copies of the oracle's source and checks that some
+pin fails for each.
+"""
+import numpy as np
+import torch
+
+from pkv_testutil import (BF16, F16, F32, from_storage, ints, poison_unused, random_problem,
+                          read_golden, sequential_fill, to_storage)
+
+
+def _close(a, b, tol, what):
+    err = float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+    assert np.all(np.isfinite(a)), "%s: non-finite values" % what
+    assert err <= tol, "%s: max abs error %.3g > %.3g" % (what, err, tol)
+
+
+# ---------------------------------------------------------------------------
+# Storage formats
+# ---------------------------------------------------------------------------
+
+def pin_f16_decode_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.to_double(bits, F16)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "f16 decode: NaN patterns differ"
+    assert np.array_equal(got[~nan], want[~nan]), "f16 decode differs from numpy"
+
+
+def pin_bf16_decode_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.to_double(bits, BF16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "bf16 decode: NaN patterns differ"
+    assert np.array_equal(got[~nan], want[~nan]), "bf16 decode differs from torch"
+
+
+def _encode_samples(rng):
+    mags = np.concatenate([
+        rng.uniform(-1, 1, 4000),
+        rng.standard_normal(4000) * 2.0 ** rng.integers(-30, 20, 4000),
+        rng.uniform(-7e4, 7e4, 1000),                       # around the f16 overflow point
+        rng.standard_normal(1000) * 2.0 ** -24,             # f16 subnormals
+    ])
+    # exact midpoints between neighbouring f16 values (ties go to even)
+    h = rng.integers(0, 0x7BFF, 2000).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    return np.concatenate([mags, (lo + hi) / 2, -(lo + hi) / 2, [0.0, -0.0, 65504.0, 65520.0,
+                                                              65519.99, 6e-8, 3e-8, 2.9e-8]])
+
+
+def pin_f16_encode(orc):
+    x = _encode_samples(np.random.default_rng(11))
+    got = orc.cast(x, F16)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "f16 encode differs from numpy at %r" % (x[bad[:4]],)
+
+
+def pin_bf16_encode(orc):
+    rng = np.random.default_rng(12)
+    # values exactly representable in float32: torch's float32 -> bfloat16 is a single rounding
+    f = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        (rng.standard_normal(2000) * 2.0 ** rng.integers(-130, 120, 2000)).astype(np.float32),
+                        np.array([0, -0.0, 3.3895314e38, 3.39e38, 1e-40, -1e-45], np.float32)])
+    got = orc.cast(f.astype(np.float64), BF16)
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want), "bf16 encode differs from torch"
+    # rounding straight from double: 1 + 2^-8 + 2^-30 lies above the midpoint of
+    # 1 and 1 + 2^-7, so it rounds up (via binary32 it would tie down to 1.0)
+    assert orc.double_to_bf16_bits(1 + 2.0 ** -8 + 2.0 ** -30) == 0x3F81
+    assert orc.double_to_bf16_bits(1 + 2.0 ** -8) == 0x3F80          # tie -> even
+    assert orc.double_to_bf16_bits(1 + 3 * 2.0 ** -8) == 0x3F82      # tie -> even
+    assert orc.double_to_bf16_bits(-2.0 ** 128) == 0xFF80            # overflow -> -inf
+
+
+def pin_f32_cast(orc):
+    x = np.random.default_rng(13).standard_normal(5000) * 1e3
+    assert np.array_equal(orc.cast(x, F32), x.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Address translation and append
+# ---------------------------------------------------------------------------
+
+def pin_slots_block_table_example(orc):
+    g = read_golden("block_table_b4.txt")
+    B = ints(g["block_size"][0])[0]
+    table = ints(g["table_after"][-1][1:])
+    want = ints(g["slots"][0])
+    got = [orc.physical_slot(table, B, i) for i in range(len(want))]
+    assert got == want, "slots %r != printed example %r" % (got, want)
+
+
+def pin_slot_out_of_blocks_example(orc):
+    g = read_golden("out_of_blocks_b16.txt")
+    B = ints(g["block_size"][0])[0]
+    table = ints(g["seq0_table_after_append"][0])
+    n = ints(g["seq0_n_tokens_after_append"][0])[0]
+    assert orc.physical_slot(table, B, n - 1) == ints(g["slot_token32"][0])[0]
+
+
+def pin_gather_sequential_fill(orc):
+    rng = np.random.default_rng(21)
+    for B, Hkv, D, L in [(1, 1, 3, 5), (3, 2, 4, 10), (4, 3, 5, 13), (16, 2, 8, 33), (16, 1, 4, 16)]:
+        nb = -(-L // B) + 4
+        table = rng.permutation(nb)[: -(-L // B)]
+        rows = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+        pool = sequential_fill(np.zeros((nb, B, Hkv, D), np.float32), table, rows)
+        got = orc.gather(pool, table, L, F32)
+        assert np.array_equal(got, rows.transpose(1, 0, 2).astype(np.float64)), \
+            "gather != sequential fill (B=%d)" % B
+
+
+def pin_append_one_token_at_a_time(orc):
+    """Appending tokens 0..L-1 one call each builds the sequential-fill layout."""
+    rng = np.random.default_rng(22)
+    for dtype in (F32, BF16):
+        B, Hkv, D, S = 4, 3, 8, 3
+        lens = [9, 4, 13]
+        need = [-(-L // B) for L in lens]
+        nb = sum(need) + 2
+        perm = rng.permutation(nb)
+        tables, off = [], 0
+        for n in need:
+            tables.append(perm[off:off + n])
+            off += n
+        bt = np.full((S, max(need)), -1, np.int32)
+        for s, t in enumerate(tables):
+            bt[s, :len(t)] = t
+        rows = [to_storage(rng.standard_normal((L, Hkv, D)), dtype) for L in lens]
+        want_k = np.zeros((nb, B, Hkv, D), rows[0].dtype)
+        for s in range(S):
+            sequential_fill(want_k, tables[s], rows[s])
+        kc = np.zeros_like(want_k)
+        vc = np.zeros_like(want_k)
+        for i in range(max(lens)):
+            active = [s for s in range(S) if i < lens[s]]
+            kn = np.ascontiguousarray(np.stack([rows[s][i] for s in active]))
+            orc.append(kn, kn.copy(), kc, vc, bt[active], np.full(len(active), i, np.int32), dtype)
+        assert np.array_equal(kc, want_k) and np.array_equal(vc, want_k), "append layout"
+
+
+def pin_append_overwrites_only_its_slot(orc):
+    rng = np.random.default_rng(23)
+    B, Hkv, D = 16, 2, 8
+    p = random_problem(rng, F16, 3, 2, Hkv, D, B, [5, 16, 17])
+    kc, vc = p["k_cache"].copy(), p["v_cache"].copy()
+    S = 3
+    pos = p["context_lens"] - 1
+    kn = to_storage(rng.standard_normal((S, Hkv, D)), F16)
+    vn = to_storage(rng.standard_normal((S, Hkv, D)), F16)
+    orc.append(kn, vn, kc, vc, p["block_tables"], pos, F16)
+    for s in range(S):
+        rows_k = list(p["dense_k"][s])
+        rows_v = list(p["dense_v"][s])
+        rows_k[pos[s]] = kn[s]
+        rows_v[pos[s]] = vn[s]
+        sequential_fill(p["k_cache"], p["tables"][s], rows_k)
+        sequential_fill(p["v_cache"], p["tables"][s], rows_v)
+    assert np.array_equal(kc, p["k_cache"]) and np.array_equal(vc, p["v_cache"])
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _sdpa_dense(p, scale, Hq):
+    """torch scaled_dot_product_attention (float64, CPU) on the contiguous layout."""
+    dtype = p["dtype"]
+    out = []
+    for s in range(len(p["dense_k"])):
+        q = torch.from_numpy(from_storage(p["q"][s], dtype))[None, :, None, :]        # [1,Hq,1,D]
+        k = torch.from_numpy(from_storage(p["dense_k"][s], dtype).transpose(1, 0, 2).copy())[None]
+        v = torch.from_numpy(from_storage(p["dense_v"][s], dtype).transpose(1, 0, 2).copy())[None]
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale, enable_gqa=True)
+        out.append(o[0, :, 0, :].numpy())
+    return np.stack(out)
+
+
+def _oracle(orc, p, scale, **kw):
+    return orc.attention_decode(p["q"], p["k_cache"], p["v_cache"], p["block_tables"],
+                                p["context_lens"], scale, p["dtype"], **kw)
+
+
+def pin_attention_matches_sdpa(orc):
+    rng = np.random.default_rng(31)
+    cases = [(F32, 4, 4, 16, 16, [5, 16, 17, 33]),
+             (F16, 8, 2, 8, 4, [1, 4, 5, 9]),
+             (BF16, 8, 1, 16, 16, [2, 31, 48]),
+             (BF16, 6, 3, 8, 3, [7, 1, 12])]
+    for dtype, Hq, Hkv, D, B, lens in cases:
+        p = random_problem(rng, dtype, len(lens), Hq, Hkv, D, B, lens)
+        scale = 1.0 / np.sqrt(D)
+        _close(_oracle(orc, p, scale), _sdpa_dense(p, scale, Hq), 1e-12,
+               "oracle vs SDPA (dtype %d, %d/%d heads)" % (dtype, Hq, Hkv))
+
+
+def pin_closed_forms(orc):
+    rng = np.random.default_rng(32)
+    # one token: the output is that token's value row, exactly
+    p = random_problem(rng, F32, 2, 4, 2, 8, 16, [1, 1])
+    got = _oracle(orc, p, 0.3)
+    for s in range(2):
+        want = np.repeat(p["dense_v"][s][0].astype(np.float64), 2, axis=0)
+        assert np.array_equal(got[s], want), "L=1 must return V_0"
+    # zero query, or all keys equal: the plain mean of the value rows
+    p = random_problem(rng, F32, 2, 2, 2, 8, 4, [7, 13])
+    p["q"][:] = 0
+    got = _oracle(orc, p, 1.0)
+    for s in range(2):
+        want = np.repeat(p["dense_v"][s].astype(np.float64).mean(axis=0), 1, axis=0)
+        _close(got[s], want, 1e-14, "q = 0 gives the mean of V")
+    p = random_problem(rng, F32, 1, 3, 1, 8, 4, [11])
+    row = p["dense_k"][0][0].copy()
+    sequential_fill(p["k_cache"], p["tables"][0], [row] * 11)
+    got = _oracle(orc, p, 0.7)
+    want = np.repeat(p["dense_v"][0].astype(np.float64).mean(axis=0), 3, axis=0)
+    _close(got[0], want, 1e-14, "equal keys give the mean of V")
+
+
+def pin_block_permutation_invariance(orc):
+    rng = np.random.default_rng(33)
+    p = random_problem(rng, BF16, 3, 8, 2, 16, 16, [20, 47, 3])
+    base = _oracle(orc, p, 0.25)
+    nb = p["k_cache"].shape[0]
+    pi = rng.permutation(nb)
+    k2 = np.empty_like(p["k_cache"])
+    v2 = np.empty_like(p["v_cache"])
+    k2[pi] = p["k_cache"]
+    v2[pi] = p["v_cache"]
+    bt = p["block_tables"].copy()
+    bt[bt >= 0] = pi[bt[bt >= 0]]
+    q = dict(p, k_cache=k2, v_cache=v2, block_tables=bt)
+    assert np.array_equal(_oracle(orc, q, 0.25), base), "output moved with the physical layout"
+
+
+def pin_shared_vs_copied_prefix(orc):
+    rng = np.random.default_rng(34)
+    B, Hkv, D, S, pre = 4, 2, 8, 3, 8
+    suffix = [3, 5, 1]
+    pre_k = to_storage(rng.standard_normal((pre, Hkv, D)), F16)
+    pre_v = to_storage(rng.standard_normal((pre, Hkv, D)), F16)
+    suf_k = [to_storage(rng.standard_normal((n, Hkv, D)), F16) for n in suffix]
+    suf_v = [to_storage(rng.standard_normal((n, Hkv, D)), F16) for n in suffix]
+    q = to_storage(rng.standard_normal((S, 4, D)), F16)
+    lens = np.array([pre + n for n in suffix], np.int32)
+    outs = []
+    for shared in (True, False):
+        nb = 40
+        order = list(rng.permutation(nb))
+        kc = np.zeros((nb, B, Hkv, D), np.uint16)
+        vc = np.zeros_like(kc)
+        pre_blocks = [order.pop() for _ in range(pre // B)]
+        bt = np.full((S, 8), -1, np.int32)
+        for s in range(S):
+            mine = pre_blocks if shared else [order.pop() for _ in range(pre // B)]
+            mine = mine + [order.pop() for _ in range(-(-suffix[s] // B))]
+            sequential_fill(kc, mine, list(pre_k) + list(suf_k[s]))
+            sequential_fill(vc, mine, list(pre_v) + list(suf_v[s]))
+            bt[s, :len(mine)] = mine
+        outs.append(orc.attention_decode(q, kc, vc, bt, lens, 0.35, F16))
+    assert np.array_equal(outs[0], outs[1]), "shared and copied prefix differ"
+
+
+def pin_split_k_identity(orc):
+    rng = np.random.default_rng(35)
+    p = random_problem(rng, BF16, 3, 8, 2, 16, 16, [600, 77, 1030])
+    whole = _oracle(orc, p, 0.25)
+    for P in (1, 5, 16, 64, 512, 2048):
+        _close(_oracle(orc, p, 0.25, part_tokens=P), whole, 1e-12, "split-K P=%d" % P)
+    # also against the library on the contiguous layout
+    _close(_oracle(orc, p, 0.25, part_tokens=64), _sdpa_dense(p, 0.25, 8), 1e-12, "split-K vs SDPA")
+
+
+def pin_unused_slots_never_read(orc):
+    rng = np.random.default_rng(36)
+    for dtype in (F32, F16, BF16):
+        p = random_problem(rng, dtype, 4, 4, 2, 8, 16, [5, 16, 17, 33], pool_extra=5)
+        base = _oracle(orc, p, 0.5)
+        poison_unused(p["k_cache"], p["block_tables"], p["context_lens"], dtype)
+        poison_unused(p["v_cache"], p["block_tables"], p["context_lens"], dtype)
+        got = _oracle(orc, p, 0.5)
+        assert np.array_equal(got, base), "a slot past the context changed the output"
+
+
+def pin_zero_length(orc):
+    rng = np.random.default_rng(37)
+    p = random_problem(rng, F32, 2, 2, 2, 8, 4, [0, 3])
+    got = _oracle(orc, p, 1.0)
+    assert np.array_equal(got[0], np.zeros((2, 8))), "L = 0 gives zeros"
+    assert np.all(np.isfinite(got[1]))
+
+
+def pin_sampled_sequences(orc):
+    rng = np.random.default_rng(38)
+    p = random_problem(rng, F16, 5, 4, 4, 8, 16, [3, 40, 17, 1, 22])
+    full = _oracle(orc, p, 0.5)
+    part = _oracle(orc, p, 0.5, seq_ids=[3, 1])
+    assert np.array_equal(part[[1, 3]], full[[1, 3]])
+    assert np.all(np.isnan(part[[0, 2, 4]]))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
