@@ -1,0 +1,282 @@
+"""Benchmark of the paged KV decode path on one MI355X.
+
+One step = the whole hot path over one batch: append each sequence's new K/V
+row into its paged slot, the split-K partition pass of decode attention, and
+the log-sum-exp merge, all through the C ABI on torch's current stream.
+
+Default workload: one Llama-2-7B-shaped layer (32 query / 32 KV heads,
+head_dim 128, fp16, block size 16, a pool of 5,120 blocks), 64 sequences with
+context lengths uniform in [128, 2048], physical blocks in seeded shuffled
+order, synthetic N(0,1)/sqrt(128) data.
+
+Printed (one JSON line): KV-read GB/s over the whole step (value), tokens/s,
+the partition kernel's roofline (algorithmic KV bytes per launch / its mean
+duration from HIP events, against the 8 TB/s HBM peak), the oracle on the host
+cores as a CPU baseline, and context figures (merge and append times, a
+streaming-read probe, shuffled vs in-order block tables).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                    [--no-cpu-baseline] [--no-extras]
+    python bench.py --summarize-pmc DIR     # condense rocprofv3 --pmc output
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged-attn decode: KV-read GB/s (% of HBM peak), tokens/s at Llama-2-7B shape"
+KERNEL_SOURCES = ["paged_kv_cache_227_amd/csrc/decode.hip", "paged_kv_cache_227_amd/csrc/pkv_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{config}.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config, n_bytes):
+    """HBM traffic of the partition kernel from committed counter summaries,
+    or None when absent or taken on different kernel sources."""
+    path = TRAFFIC_FILE.format(config=config)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t
+
+
+def make_workload(name):
+    from paged_kv_cache_227_amd import workloads as W
+    return W.CONFIGS[name]()
+
+
+def run_gpu(w, steps, warmup, extras):
+    import torch
+    import paged_kv_cache_227_amd as P
+    from paged_kv_cache_227_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    T = W.to_torch(w, dev)
+    q, kc, vc, bt, lens = T["q"], T["k_cache"], T["v_cache"], T["block_tables"], T["context_lens"]
+    out = torch.empty_like(q)
+    layout = P.layout_of(kc)
+    part = w.part_tokens or P.partition_tokens_for(w.num_seqs, w.n_q_heads, w.max_blocks_per_seq, layout)
+    ws = P.alloc_workspace(q, kc, bt, part)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        P.paged_kv_append(T["k_new"], T["v_new"], kc, vc, bt, T["positions"])
+        if ev:
+            ev[1].record()
+        P.paged_attention_partitions(q, kc, vc, bt, lens, w.scale, out, part, ws)
+        if ev:
+            ev[2].record()
+        P.paged_attention_merge(kc, bt, lens, out, part, ws)
+        if ev:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    t_app = [e[0].elapsed_time(e[1]) for e in events]
+    t_part = [e[1].elapsed_time(e[2]) for e in events]
+    t_merge = [e[2].elapsed_time(e[3]) for e in events]
+    res = dict(ms_per_step=ms_step, part_tokens=part,
+               partition_ms_mean=statistics.fmean(t_part), partition_ms_median=statistics.median(t_part),
+               partition_ms_p10=sorted(t_part)[len(t_part) // 10],
+               partition_ms_p90=sorted(t_part)[(len(t_part) * 9) // 10],
+               merge_ms_mean=statistics.fmean(t_merge), append_ms_mean=statistics.fmean(t_app))
+
+    if extras:
+        # a plain streaming read of 4 GiB: what a simple coalesced kernel reaches
+        buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        sink = torch.empty(4096, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            P.probe_read(buf, sink)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(10):
+            P.probe_read(buf, sink)
+        s1.record()
+        torch.cuda.synchronize()
+        res["probe_read_gbs"] = buf.numel() * 10 / (s0.elapsed_time(s1) * 1e-3) / 1e9
+        del buf, sink
+    del T, q, kc, vc, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_partitions_only(w, iters=30):
+    """Mean partition-pass time (ms) for a workload, e.g. in-order block tables."""
+    import torch
+    import paged_kv_cache_227_amd as P
+    from paged_kv_cache_227_amd import workloads as W
+    T = W.to_torch(w, "cuda:0")
+    out = torch.empty_like(T["q"])
+    layout = P.layout_of(T["k_cache"])
+    part = w.part_tokens or P.partition_tokens_for(w.num_seqs, w.n_q_heads, w.max_blocks_per_seq, layout)
+    ws = P.alloc_workspace(T["q"], T["k_cache"], T["block_tables"], part)
+    args = (T["q"], T["k_cache"], T["v_cache"], T["block_tables"], T["context_lens"], w.scale, out, part, ws)
+    for _ in range(5):
+        P.paged_attention_partitions(*args)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        P.paged_attention_partitions(*args)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle (append + decode, fp64) on a bounded sample of the workload's
+    sequences, on every host core it may use."""
+    import numpy as np
+    from oracle import ref
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    orc = ref.default()
+    threads = orc.num_threads()
+    order = list(range(w.num_seqs))
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    t0 = time.perf_counter()
+    orc.append(w.k_new, w.v_new, kc, vc, w.block_tables, w.positions, w.dtype_code)
+    t_append = time.perf_counter() - t0
+    done, elapsed, tokens = [], 0.0, 0
+    # sequences one batch at a time until the budget is spent
+    batch = max(1, w.num_seqs // 16)
+    while order and elapsed < budget_s:
+        ids, order = order[:batch], order[batch:]
+        t0 = time.perf_counter()
+        orc.attention_decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.dtype_code, seq_ids=ids)
+        elapsed += time.perf_counter() - t0
+        done += ids
+        tokens += int(np.sum(w.context_lens[ids]))
+    kv_bytes = tokens * w.n_kv_heads * 2 * w.head_dim * (4 if w.dtype == "f32" else 2)
+    return {"value": kv_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences (%d tokens, %.1f s of decode), append of all %d sequences %.3f s"
+                      % (len(done), w.num_seqs, tokens, elapsed, w.num_seqs, t_append),
+            "tokens_per_s": len(done) / elapsed}
+
+
+def summarize_pmc(d):
+    """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
+    --pmc CSV output under directory d."""
+    import csv
+    rows = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", "")
+                key = (name, r.get("Counter_Name", ""))
+                rows.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+    out = {}
+    for (name, ctr), vals in rows.items():
+        out.setdefault(name, {})[ctr] = {"mean": statistics.fmean(vals), "dispatches": len(vals)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama2_7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    a = ap.parse_args()
+
+    if a.summarize_pmc:
+        print(json.dumps(summarize_pmc(a.summarize_pmc), indent=1))
+        return 0
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    t = time.perf_counter()
+    w = make_workload(a.config)
+    log("workload %s: %d sequences, %d tokens, KV bytes %.3f GB (generated in %.1f s)"
+        % (w.name, w.num_seqs, int(w.context_lens.sum()), w.kv_read_bytes() / 1e9, time.perf_counter() - t))
+    kv = w.kv_read_bytes()
+    g = run_gpu(w, a.steps, a.warmup, not a.no_extras)
+    log("gpu: %.4f ms/step, partition %.4f ms, merge %.4f ms, append %.4f ms"
+        % (g["ms_per_step"], g["partition_ms_mean"], g["merge_ms_mean"], g["append_ms_mean"]))
+
+    achieved = kv / (g["partition_ms_mean"] * 1e-3) / 1e9
+    traffic = load_traffic(w.name, kv)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
+                "kernel": "decode_partition_kernel", "algorithmic_bytes_per_launch": kv,
+                "mean_launch_ms": round(g["partition_ms_mean"], 5)}
+    value = kv / (g["ms_per_step"] * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(g["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "num_blocks": w.num_blocks, "total_context_tokens": int(w.context_lens.sum()),
+                   "kv_read_bytes": kv, "partition_tokens": g["part_tokens"], "seed": w.seed},
+        "roofline": roofline,
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.num_seqs / (g["ms_per_step"] * 1e-3), 1),
+        "tokens_per_s_32_layers": round(w.num_seqs / (32 * g["ms_per_step"] * 1e-3), 1),
+        "kernel_ms": {k: round(g[k], 5) for k in ("partition_ms_mean", "partition_ms_median",
+                                                  "partition_ms_p10", "partition_ms_p90",
+                                                  "merge_ms_mean", "append_ms_mean")},
+    }
+    if not a.no_extras:
+        from paged_kv_cache_227_amd import workloads as W
+        res["probe_read_gbs"] = round(g["probe_read_gbs"], 1)
+        if a.config == "llama2_7b":
+            import math
+            lens = w.context_lens
+            seq = W.build("llama2_7b_in_order", lens, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, w.seed,
+                          num_blocks=w.num_blocks, data_mult=1.0 / math.sqrt(128.0), shuffle=False)
+            t_seq = time_partitions_only(seq)
+            res["shuffled_vs_in_order_throughput"] = round(t_seq / g["partition_ms_mean"], 4)
+            del seq
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,226 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV cache decode path.
+ *
+ * The operations are the two a paged KV cache needs on every decode step:
+ *
+ *   append  -- write each sequence's new key/value row into the slot its
+ *              block table gives for the token's logical position;
+ *   decode  -- attention of each sequence's query over its cached keys and
+ *              values, read in place through the block table.
+ *
+ * Both use the address translation of "How a serving engine actually works"
+ * (paperfordummies.in), section "The one formula":
+ *
+ *     slot(seq, i) = block_table[seq][i / B] * B + (i mod B)
+ *
+ * and the per-layer cache layout of "Paged-KV + Continuous Batching From
+ * Scratch" (henryhe.ai), section 1, and "Paged Attention and the Block
+ * Manager" (snowch.github.io ch08), section "The build": one tensor per layer,
+ * indexed by physical block,
+ *
+ *     k_cache, v_cache : [num_blocks][block_size][n_kv_heads][head_dim]
+ *
+ * contiguous, element type `dtype`.  Attention itself is unchanged by paging
+ * (henryhe.ai, "What's deliberately still missing": the same maths as a
+ * FlashAttention forward with different addressing): for query head h of
+ * sequence s, with L = context_lens[s] and KV head g = h / (n_q_heads /
+ * n_kv_heads),
+ *
+ *     out[s][h] = sum_i softmax_i(scale * <q[s][h], K_i>) * V_i,   i < L,
+ *
+ * with no causal mask (a decode query attends to every cached token,
+ * including its own), accumulated in fp32 and rounded to `dtype` with
+ * round-to-nearest-even.  L = 0 gives a zero row.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device pointers unless a parameter says "host".  The caller
+ *     owns every buffer it passes in; the library never allocates or frees KV
+ *     blocks (that is the host block manager's job).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return once the work is enqueued.  PKV_OK means "validated
+ *     and enqueued"; faults in enqueued work surface at the caller's next
+ *     synchronisation as HIP errors.
+ *   - Invalid arguments return a status and leave every buffer untouched; the
+ *     message of the last non-OK call on this thread is pkv_last_error().
+ *     Nothing throws across this boundary.
+ *   - block_tables is [num_seqs][max_blocks_per_seq] int32, row-major; entries
+ *     past a sequence's last block are ignored.  Table entries outside
+ *     [0, num_blocks) are a precondition violation: the kernels skip such a
+ *     block (no out-of-bounds access) and the result is unspecified;
+ *     pkv_validate() reports them.
+ *   - Supported by the GPU path: dtype f32 / f16 / bf16, block_size 16,
+ *     head_dim 64 or 128, n_q_heads / n_kv_heads in {1, 2, 4, 8}.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_EINVAL = 1,  /* bad pointer, size, shape or layout */
+    PKV_ENOTSUP = 2, /* valid, but a dtype / head_dim / group size this build does not serve */
+    PKV_EHIP = 3,    /* the HIP runtime returned an error */
+    PKV_EOOB = 4     /* pkv_validate: a table entry or position out of range */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Shape of one layer's cache pair (host struct, read during the call only). */
+typedef struct {
+    int32_t num_blocks; /* physical blocks in the pool */
+    int32_t block_size; /* tokens per block (B); 16 on the GPU path */
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t dtype; /* pkv_dtype */
+} pkv_layout;
+
+/*
+ * paged_kv_append -- scatter each sequence's new token into its slot.
+ *
+ * For every s < num_seqs, with p = positions[s]:
+ *     k_cache[slot(s, p)][:][:] = k_new[s][:][:]   (and likewise for v)
+ * a bit-exact copy.  Nothing else in the caches changes.
+ *
+ *   k_new, v_new  [num_seqs][n_kv_heads][head_dim], element type layout->dtype
+ *   k_cache, v_cache  the layer's caches (see top of file), written in place
+ *   layout        host pointer
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32
+ *   positions     [num_seqs] int32: logical index of each new token; the host
+ *                 must have grown the table to cover it (p / B < blocks held)
+ *
+ * Preconditions: the target slots are pairwise distinct (a writer owns its
+ * block: copy-on-write happens on the host before the append).  A position
+ * outside [0, max_blocks_per_seq * B) or a table entry outside the pool makes
+ * the kernel skip that sequence.
+ */
+pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const pkv_layout* layout, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* positions, int32_t num_seqs,
+                           void* stream);
+
+/*
+ * paged_attention_decode -- one decode step of attention through block tables.
+ *
+ *   q             [num_seqs][n_q_heads][head_dim], element type layout->dtype
+ *   k_cache, v_cache, layout, block_tables, max_blocks_per_seq  as above
+ *   context_lens  [num_seqs] int32: tokens attended (0 <= L <= max_blocks_per_seq * B)
+ *   n_q_heads     a multiple of layout->n_kv_heads
+ *   scale         multiplies every score (usually 1 / sqrt(head_dim))
+ *   out           [num_seqs][n_q_heads][head_dim], element type layout->dtype
+ *
+ * Long contexts are split into partitions of P tokens (a multiple of B; chosen
+ * by the library, see pkv_set_partition_tokens) whose partial softmax states
+ * are combined by the log-sum-exp rule.  The split-K workspace is owned by the
+ * library (one per device, grown on demand with hipMalloc, freed at unload);
+ * callers that must not allocate use paged_attention_decode_ws.  Calls that
+ * share the library workspace must be ordered (same stream, or synchronised).
+ */
+pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const pkv_layout* layout, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                                  void* stream);
+
+/*
+ * Bytes of split-K workspace paged_attention_decode_ws needs for these sizes
+ * with partition length part_tokens (0 = the library's choice).  Returns 0 for
+ * invalid sizes.
+ */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads,
+                                      int32_t max_blocks_per_seq, const pkv_layout* layout,
+                                      int32_t part_tokens);
+
+/*
+ * paged_attention_decode_ws -- paged_attention_decode with an explicit
+ * partition length and a caller-owned workspace.
+ *
+ *   part_tokens  partition length in tokens, a positive multiple of
+ *                layout->block_size, or 0 for the library's choice
+ *   workspace    device buffer of at least
+ *                paged_attention_workspace_size(..., part_tokens) bytes,
+ *                256-byte aligned; may be NULL when that size is 0
+ *
+ * Runs two kernels: the partition pass (paged_attention_partitions) and, for
+ * sequences with more than one partition, the merge (paged_attention_merge).
+ */
+pkv_status paged_attention_decode_ws(const void* q, const void* k_cache, const void* v_cache,
+                                     const pkv_layout* layout, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                                     int32_t part_tokens, void* workspace, size_t ws_bytes,
+                                     void* stream);
+
+/*
+ * The two passes of paged_attention_decode_ws, callable separately (same
+ * arguments).  The partition pass writes `out` directly for sequences whose
+ * context fits one partition and the per-partition softmax state
+ * (running max, sum of exponentials, unnormalised weighted sum of values) to
+ * the workspace for the others; the merge pass combines those states,
+ *     M = max_j m_j,   out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
+ * and writes their rows of `out`.  The workspace layout is internal.
+ */
+pkv_status paged_attention_partitions(const void* q, const void* k_cache, const void* v_cache,
+                                      const pkv_layout* layout, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                                      int32_t part_tokens, void* workspace, size_t ws_bytes,
+                                      void* stream);
+
+pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                 void* out, int32_t part_tokens, const void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * Process-wide partition length used when a call passes 0 (and by
+ * paged_attention_decode): a positive multiple of the block size, or 0 to
+ * restore the library's automatic choice.  Returns PKV_EINVAL otherwise.
+ */
+pkv_status pkv_set_partition_tokens(int32_t tokens);
+
+/* Partition length the library would use for these sizes (after the above). */
+int32_t pkv_partition_tokens_for(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks_per_seq,
+                                 const pkv_layout* layout);
+
+/*
+ * pkv_validate -- host-side debugging check of a step's bookkeeping (no GPU
+ * work).  All pointers are HOST pointers.  Checks that every table entry a
+ * sequence uses (its first ceil(L / B) entries, L = context_lens[s]) lies in
+ * [0, num_blocks), that 0 <= L <= max_blocks_per_seq * B, and, when positions
+ * is non-NULL, that every append slot lies inside the sequence's blocks and
+ * that no two sequences append to the same slot.  Returns PKV_OK, PKV_EOOB
+ * (range) or PKV_EINVAL (shape, or duplicate append slots) with a message.
+ */
+pkv_status pkv_validate(const pkv_layout* layout, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        const int32_t* positions, int32_t num_seqs);
+
+/* Message of this thread's last non-OK call ("" if none).  Owned by the library. */
+const char* pkv_last_error(void);
+
+/* Library version string, e.g. "pagedkv 0.1 gfx950". */
+const char* pkv_version(void);
+
+/*
+ * Measurement helpers (not part of the decode path):
+ *   pkv_probe_read  -- streams `bytes` (a multiple of 16) from `src` with
+ *                      16-byte loads and writes one checksum word per
+ *                      workgroup to `sink` (>= 4096 floats); gives the
+ *                      achievable HBM read rate;
+ *   pkv_probe_copy  -- copies `bytes` (a multiple of 16) from src to dst; a
+ *                      plain kernel of known traffic for calibrating counters.
+ */
+pkv_status pkv_probe_read(const void* src, size_t bytes, float* sink, void* stream);
+pkv_status pkv_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

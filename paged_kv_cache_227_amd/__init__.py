@@ -1,0 +1,15 @@
+"""MI355X-native paged KV cache decode path.
+
+The compute path is the HIP library libpagedkv.so (C ABI in include/pagedkv.h);
+this package binds it (``_lib``), and holds the host block manager
+(``blocks``) and the seeded input generator (``workloads``).
+"""
+from ._lib import (PagedKVCache, alloc_workspace, last_error, layout_of, paged_attention_decode,
+                   paged_attention_merge, paged_attention_partitions, paged_kv_append,
+                   partition_tokens_for, probe_copy, probe_read, set_partition_tokens, validate,
+                   version, workspace_size)
+
+__all__ = ["PagedKVCache", "alloc_workspace", "last_error", "layout_of", "paged_attention_decode",
+           "paged_attention_merge", "paged_attention_partitions", "paged_kv_append",
+           "partition_tokens_for", "probe_copy", "probe_read", "set_partition_tokens", "validate",
+           "version", "workspace_size"]

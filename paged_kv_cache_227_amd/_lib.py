@@ -1,0 +1,284 @@
+"""ctypes binding of libpagedkv.so (include/pagedkv.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the decode path runs in the library's HIP
+kernels.  There is no fallback: if the library is not built, or a tensor is
+not on a GPU, the call raises.
+
+Errors: misuse detected here (device, dtype, shape, contiguity) raises
+ValueError; a non-OK status from the library raises ValueError for
+PKV_EINVAL / PKV_EOOB, NotImplementedError for PKV_ENOTSUP and RuntimeError
+for PKV_EHIP, each carrying pkv_last_error().
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_EHIP, PKV_EOOB = 0, 1, 2, 3, 4
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+# Every symbol include/pagedkv.h declares, with its ctypes signature.
+_P, _I32, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_LP = ctypes.POINTER(Layout)
+SIGNATURES = {
+    "paged_kv_append": (ctypes.c_int, [_P, _P, _P, _P, _LP, _P, _I32, _P, _I32, _P]),
+    "paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _I32, _I32, _F32, _P, _P]),
+    "paged_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _LP, _I32]),
+    "paged_attention_decode_ws": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _I32, _I32, _F32, _P,
+                                                 _I32, _P, _SZ, _P]),
+    "paged_attention_partitions": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _I32, _I32, _F32, _P,
+                                                  _I32, _P, _SZ, _P]),
+    "paged_attention_merge": (ctypes.c_int, [_LP, _I32, _P, _I32, _I32, _P, _I32, _P, _SZ, _P]),
+    "pkv_set_partition_tokens": (ctypes.c_int, [_I32]),
+    "pkv_partition_tokens_for": (_I32, [_I32, _I32, _I32, _LP]),
+    "pkv_validate": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _I32]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_probe_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "pkv_probe_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpagedkv.so is not built (%s); run __graft_entry__.build() or "
+                               "python paged_kv_cache_227_amd/build_lib.py" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().pkv_last_error().decode()
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+def _check(status: int, what: str):
+    if status == PKV_OK:
+        return
+    msg = "%s: %s" % (what, last_error())
+    if status in (PKV_EINVAL, PKV_EOOB):
+        raise ValueError(msg)
+    if status == PKV_ENOTSUP:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+# ---- tensor helpers -------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in m:
+        raise ValueError("unsupported dtype %s (float32, float16 or bfloat16)" % t.dtype)
+    return m[t.dtype]
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise ValueError("%s must be int32" % name)
+    return _dev(t, name)
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def layout_of(k_cache) -> Layout:
+    """Layout of a [num_blocks][block_size][n_kv_heads][head_dim] cache tensor."""
+    if k_cache.dim() != 4:
+        raise ValueError("a cache is [num_blocks][block_size][n_kv_heads][head_dim]")
+    nb, bs, hkv, d = k_cache.shape
+    return Layout(nb, bs, hkv, d, _dtype_code(k_cache))
+
+
+def _check_caches(k_cache, v_cache):
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or v_cache.device != k_cache.device:
+        raise ValueError("k_cache and v_cache must match in shape, dtype and device")
+
+
+def _check_tables(block_tables, per_seq, num_seqs, names):
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    if per_seq.dim() != 1 or per_seq.shape[0] != num_seqs:
+        raise ValueError("%s must be [num_seqs]" % names)
+
+
+# ---- the path --------------------------------------------------------------------
+
+def paged_kv_append(k_new, v_new, k_cache, v_cache, block_tables, positions, stream=None) -> None:
+    """k_cache[slot(s, positions[s])] = k_new[s] (and v), for every sequence s."""
+    _check_caches(k_cache, v_cache)
+    L = layout_of(k_cache)
+    S = positions.shape[0]
+    want = (S, L.n_kv_heads, L.head_dim)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+        raise ValueError("k_new / v_new must be %r" % (want,))
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("k_new / v_new must have the cache dtype")
+    _check_tables(block_tables, positions, S, "positions")
+    _check(lib().paged_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+                                 _dev(v_cache, "v_cache"), ctypes.byref(L), _i32(block_tables, "block_tables"),
+                                 block_tables.shape[1], _i32(positions, "positions"), S,
+                                 _stream(stream, k_cache.device)), "paged_kv_append")
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
+    _check_caches(k_cache, v_cache)
+    L = layout_of(k_cache)
+    if q.dim() != 3 or q.shape[2] != L.head_dim:
+        raise ValueError("q must be [num_seqs][n_q_heads][head_dim]")
+    S, Hq = q.shape[0], q.shape[1]
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise ValueError("q and out must have the cache dtype")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be shaped like q")
+    _check_tables(block_tables, context_lens, S, "context_lens")
+    return L, S, Hq
+
+
+def workspace_size(num_seqs, n_q_heads, max_blocks_per_seq, layout: Layout, part_tokens=0) -> int:
+    return int(lib().paged_attention_workspace_size(num_seqs, n_q_heads, max_blocks_per_seq,
+                                                    ctypes.byref(layout), part_tokens))
+
+
+def alloc_workspace(q, k_cache, block_tables, part_tokens=0):
+    """A device workspace for paged_attention_decode(..., workspace=...)."""
+    torch = _torch()
+    L = layout_of(k_cache)
+    n = workspace_size(q.shape[0], q.shape[1], block_tables.shape[1], L, part_tokens)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           part_tokens: int = 0, workspace=None, stream=None) -> None:
+    """out[s][h] = attention of q[s][h] over the first context_lens[s] tokens of
+    sequence s, read through its block table.  With workspace=None and
+    part_tokens=0 the library plans the split and owns the workspace."""
+    L, S, Hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out)
+    st = _stream(stream, q.device)
+    if workspace is None and part_tokens == 0:
+        _check(lib().paged_attention_decode(
+            _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L),
+            _i32(block_tables, "block_tables"), block_tables.shape[1], _i32(context_lens, "context_lens"),
+            S, Hq, float(scale), _dev(out, "out"), st), "paged_attention_decode")
+        return
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, block_tables, part_tokens)
+    _check(lib().paged_attention_decode_ws(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L),
+        _i32(block_tables, "block_tables"), block_tables.shape[1], _i32(context_lens, "context_lens"),
+        S, Hq, float(scale), _dev(out, "out"), part_tokens, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), st), "paged_attention_decode_ws")
+
+
+def paged_attention_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, out, part_tokens,
+                               workspace, stream=None) -> None:
+    L, S, Hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out)
+    _check(lib().paged_attention_partitions(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L),
+        _i32(block_tables, "block_tables"), block_tables.shape[1], _i32(context_lens, "context_lens"),
+        S, Hq, float(scale), _dev(out, "out"), part_tokens, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream, q.device)),
+        "paged_attention_partitions")
+
+
+def paged_attention_merge(k_cache, block_tables, context_lens, out, part_tokens, workspace, stream=None) -> None:
+    L = layout_of(k_cache)
+    S, Hq = out.shape[0], out.shape[1]
+    _check(lib().paged_attention_merge(
+        ctypes.byref(L), block_tables.shape[1], _i32(context_lens, "context_lens"), S, Hq,
+        _dev(out, "out"), part_tokens, _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream, out.device)), "paged_attention_merge")
+
+
+def set_partition_tokens(tokens: int) -> None:
+    _check(lib().pkv_set_partition_tokens(int(tokens)), "pkv_set_partition_tokens")
+
+
+def partition_tokens_for(num_seqs, n_q_heads, max_blocks_per_seq, layout: Layout) -> int:
+    return int(lib().pkv_partition_tokens_for(num_seqs, n_q_heads, max_blocks_per_seq, ctypes.byref(layout)))
+
+
+def validate(layout: Layout, block_tables: np.ndarray, context_lens: np.ndarray,
+             positions: Optional[np.ndarray] = None) -> None:
+    """Host-side check of tables / lengths / append slots (numpy int32 arrays)."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    pos = None if positions is None else np.ascontiguousarray(positions, dtype=np.int32)
+    if bt.ndim != 2 or lens.shape != (bt.shape[0],) or (pos is not None and pos.shape != lens.shape):
+        raise ValueError("block_tables [S][max_blocks], context_lens [S], positions [S]")
+    _check(lib().pkv_validate(ctypes.byref(layout), ctypes.c_void_p(bt.ctypes.data), bt.shape[1],
+                              ctypes.c_void_p(lens.ctypes.data),
+                              None if pos is None else ctypes.c_void_p(pos.ctypes.data), bt.shape[0]),
+           "pkv_validate")
+
+
+def probe_read(buf, sink, stream=None) -> None:
+    _check(lib().pkv_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
+                                _stream(stream, buf.device)), "pkv_probe_read")
+
+
+def probe_copy(src, dst, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(lib().pkv_probe_copy(_dev(src, "src"), _dev(dst, "dst"), n, _stream(stream, src.device)),
+           "pkv_probe_copy")
+
+
+class PagedKVCache:
+    """One layer's K/V caches, [num_blocks][block_size][n_kv_heads][head_dim]."""
+
+    def __init__(self, k_cache, v_cache):
+        _check_caches(k_cache, v_cache)
+        self.k_cache = k_cache
+        self.v_cache = v_cache
+        self.layout = layout_of(k_cache)
+
+    def append(self, k_new, v_new, block_tables, positions, stream=None) -> None:
+        paged_kv_append(k_new, v_new, self.k_cache, self.v_cache, block_tables, positions, stream)
+
+    def decode(self, q, block_tables, context_lens, scale, out, **kw) -> None:
+        paged_attention_decode(q, self.k_cache, self.v_cache, block_tables, context_lens, scale, out, **kw)

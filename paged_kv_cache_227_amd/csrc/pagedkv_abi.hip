@@ -1,0 +1,416 @@
+// pagedkv_abi.hip -- the C ABI declared in include/pagedkv.h: argument
+// checks, dtype / head_dim / group dispatch, split-K planning, the library's
+// workspace, status codes and the per-thread error message.  Host code only;
+// every step of the decode path runs in the kernels of append.hip and
+// decode.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "pagedkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int32_t> g_part_tokens{0};
+
+constexpr int kGpuBlockSize = 16;
+constexpr int32_t kDefaultPartTokens = 512;
+constexpr size_t kWsAlign = 256;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+pkv_status ok() {
+    return PKV_OK;
+}
+
+int elt_bytes(int32_t dtype) {
+    return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2 : 0;
+}
+
+pkv_status check_layout(const pkv_layout* L) {
+    if (!L) return fail(PKV_EINVAL, "layout is NULL");
+    if (L->num_blocks < 1 || L->block_size < 1 || L->n_kv_heads < 1 || L->head_dim < 1)
+        return fail(PKV_EINVAL, "layout sizes must be positive (num_blocks %d, block_size %d, "
+                                "n_kv_heads %d, head_dim %d)",
+                    L->num_blocks, L->block_size, L->n_kv_heads, L->head_dim);
+    if (elt_bytes(L->dtype) == 0) return fail(PKV_EINVAL, "unknown dtype code %d", L->dtype);
+    const int64_t row = (int64_t)L->n_kv_heads * L->head_dim * elt_bytes(L->dtype);
+    if (row > (1 << 24)) return fail(PKV_EINVAL, "a token row of %lld bytes is too large", (long long)row);
+    return PKV_OK;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+    return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t auto_partition_tokens(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks,
+                              const pkv_layout* L) {
+    (void)num_seqs;
+    (void)n_q_heads;
+    (void)max_blocks;
+    (void)L;
+    return kDefaultPartTokens;
+}
+
+pkv_status resolve_partition(int32_t requested, int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks,
+                             const pkv_layout* L, int32_t* out) {
+    int32_t P = requested;
+    if (P == 0) P = g_part_tokens.load();
+    if (P == 0) P = auto_partition_tokens(num_seqs, n_q_heads, max_blocks, L);
+    if (P < 0 || P % L->block_size != 0)
+        return fail(PKV_EINVAL, "partition length %d is not a positive multiple of block_size %d", P,
+                    L->block_size);
+    *out = P;
+    return PKV_OK;
+}
+
+struct Plan {
+    int32_t part_tokens;
+    int32_t n_parts_max;
+    size_t acc_bytes;  // ws_acc, rounded up to kWsAlign
+    size_t ws_bytes;   // total; 0 when no sequence can need a second partition
+};
+
+Plan make_plan(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks, const pkv_layout* L, int32_t P) {
+    Plan pl{};
+    pl.part_tokens = P;
+    const int64_t max_tokens = (int64_t)max_blocks * L->block_size;
+    pl.n_parts_max = (int32_t)std::max<int64_t>(1, (max_tokens + P - 1) / P);
+    if (pl.n_parts_max <= 1) return pl;
+    const size_t slots = (size_t)num_seqs * n_q_heads * pl.n_parts_max;
+    pl.acc_bytes = (slots * L->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+    pl.ws_bytes = pl.acc_bytes + slots * 2 * sizeof(float);
+    return pl;
+}
+
+pkv_status check_decode(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* L,
+                        const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t n_q_heads, float scale, const void* out) {
+    pkv_status st = check_layout(L);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
+    if (max_blocks < 1) return fail(PKV_EINVAL, "max_blocks_per_seq %d < 1", max_blocks);
+    if (n_q_heads < 1 || n_q_heads % L->n_kv_heads != 0)
+        return fail(PKV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads,
+                    L->n_kv_heads);
+    if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+    if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out))
+        return fail(PKV_EINVAL, "a required pointer is NULL");
+    if ((int64_t)max_blocks * L->block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "max_blocks_per_seq * block_size overflows int32");
+    if ((int64_t)num_seqs * n_q_heads > INT32_MAX / 4)
+        return fail(PKV_EINVAL, "num_seqs * n_q_heads is too large");
+    if (L->block_size != kGpuBlockSize)
+        return fail(PKV_ENOTSUP, "the GPU path serves block_size %d only (got %d)", kGpuBlockSize,
+                    L->block_size);
+    const int group = n_q_heads / L->n_kv_heads;
+    if (!pkv::decode_supported(L->dtype, L->head_dim, group))
+        return fail(PKV_ENOTSUP, "no kernel for dtype %d, head_dim %d, group %d", L->dtype, L->head_dim,
+                    group);
+    if (num_seqs > 65535) return fail(PKV_ENOTSUP, "num_seqs %d exceeds 65535", num_seqs);
+    if (L->n_kv_heads > 65535) return fail(PKV_ENOTSUP, "n_kv_heads %d exceeds 65535", L->n_kv_heads);
+    return PKV_OK;
+}
+
+pkv::DecodeParams make_params(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* L,
+                              const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                              const Plan& pl, void* workspace) {
+    pkv::DecodeParams p{};
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.ws_acc = static_cast<float*>(workspace);
+    p.ws_ml = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.acc_bytes) : nullptr;
+    p.num_blocks = L->num_blocks;
+    p.n_kv_heads = L->n_kv_heads;
+    p.n_q_heads = n_q_heads;
+    p.max_blocks = max_blocks;
+    p.num_seqs = num_seqs;
+    p.part_tokens = pl.part_tokens;
+    p.n_parts_max = pl.n_parts_max;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return p;
+}
+
+pkv_status check_workspace(const Plan& pl, const void* workspace, size_t ws_bytes) {
+    if (pl.ws_bytes == 0) return PKV_OK;
+    if (!workspace) return fail(PKV_EINVAL, "workspace is NULL but %zu bytes are needed", pl.ws_bytes);
+    if (ws_bytes < pl.ws_bytes)
+        return fail(PKV_EINVAL, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, pl.ws_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % kWsAlign != 0)
+        return fail(PKV_EINVAL, "workspace is not %zu-byte aligned", kWsAlign);
+    return PKV_OK;
+}
+
+// The library's own split-K workspace, one per device, grown on demand.
+struct DeviceWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<DeviceWorkspace> g_ws;
+
+struct WorkspaceReleaser {
+    ~WorkspaceReleaser() {
+        // Process teardown: the runtime may already be gone, so errors are ignored.
+        for (auto& w : g_ws)
+            if (w.ptr) (void)hipFree(w.ptr);
+    }
+} g_ws_releaser;
+
+pkv_status library_workspace(size_t need, void** out) {
+    *out = nullptr;
+    if (need == 0) return PKV_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+    DeviceWorkspace& w = g_ws[dev];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            e = hipFree(w.ptr);  // synchronises the device: in-flight users finish first
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+        }
+        const size_t grown = std::max(need, need + need / 4);
+        e = hipMalloc(&w.ptr, grown);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return hip_fail(e, "hipMalloc(workspace)");
+        }
+        w.bytes = grown;
+    }
+    *out = w.ptr;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const pkv_layout* layout, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* positions, int32_t num_seqs,
+                           void* stream) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
+    if (max_blocks_per_seq < 1) return fail(PKV_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+    if (num_seqs == 0) return ok();
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !positions)
+        return fail(PKV_EINVAL, "a required pointer is NULL");
+    if (num_seqs > INT32_MAX / 2) return fail(PKV_EINVAL, "num_seqs too large");
+    pkv::AppendParams p{};
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.positions = positions;
+    p.num_blocks = layout->num_blocks;
+    p.block_size = layout->block_size;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_seqs = num_seqs;
+    p.row_bytes = layout->n_kv_heads * layout->head_dim * elt_bytes(layout->dtype);
+    hipError_t e = pkv::launch_append(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    return ok();
+}
+
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks_per_seq,
+                                      const pkv_layout* layout, int32_t part_tokens) {
+    if (check_layout(layout) != PKV_OK || num_seqs < 0 || n_q_heads < 1 || max_blocks_per_seq < 1) return 0;
+    int32_t P = 0;
+    if (resolve_partition(part_tokens, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P) != PKV_OK)
+        return 0;
+    return make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P).ws_bytes;
+}
+
+pkv_status paged_attention_partitions(const void* q, const void* k_cache, const void* v_cache,
+                                      const pkv_layout* layout, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                                      int32_t part_tokens, void* workspace, size_t ws_bytes, void* stream) {
+    pkv_status st = check_decode(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
+                                 context_lens, num_seqs, n_q_heads, scale, out);
+    if (st != PKV_OK) return st;
+    int32_t P = 0;
+    st = resolve_partition(part_tokens, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P);
+    if (st != PKV_OK) return st;
+    const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
+    st = check_workspace(pl, workspace, ws_bytes);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return ok();
+    if (pl.n_parts_max > 65535) return fail(PKV_ENOTSUP, "%d partitions per sequence exceed 65535", pl.n_parts_max);
+    const pkv::DecodeParams p = make_params(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
+                                            context_lens, num_seqs, n_q_heads, scale, out, pl, workspace);
+    hipError_t e = pkv::launch_decode_partitions(p, layout->dtype, layout->head_dim,
+                                                 n_q_heads / layout->n_kv_heads,
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "partition launch");
+    return ok();
+}
+
+pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads, void* out,
+                                 int32_t part_tokens, const void* workspace, size_t ws_bytes, void* stream) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || max_blocks_per_seq < 1 || n_q_heads < 1 || n_q_heads % layout->n_kv_heads != 0)
+        return fail(PKV_EINVAL, "bad sizes (num_seqs %d, max_blocks_per_seq %d, n_q_heads %d)", num_seqs,
+                    max_blocks_per_seq, n_q_heads);
+    if (num_seqs > 0 && (!context_lens || !out)) return fail(PKV_EINVAL, "a required pointer is NULL");
+    if (layout->block_size != kGpuBlockSize)
+        return fail(PKV_ENOTSUP, "the GPU path serves block_size %d only", kGpuBlockSize);
+    if (!pkv::decode_supported(layout->dtype, layout->head_dim, n_q_heads / layout->n_kv_heads))
+        return fail(PKV_ENOTSUP, "no kernel for dtype %d, head_dim %d", layout->dtype, layout->head_dim);
+    int32_t P = 0;
+    st = resolve_partition(part_tokens, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P);
+    if (st != PKV_OK) return st;
+    const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
+    st = check_workspace(pl, workspace, ws_bytes);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0 || pl.n_parts_max <= 1) return ok();  // every sequence was finished by the partition pass
+    const pkv::DecodeParams p = make_params(nullptr, nullptr, nullptr, layout, nullptr, max_blocks_per_seq,
+                                            context_lens, num_seqs, n_q_heads, 1.f, out, pl,
+                                            const_cast<void*>(workspace));
+    hipError_t e = pkv::launch_decode_merge(p, layout->dtype, layout->head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return ok();
+}
+
+pkv_status paged_attention_decode_ws(const void* q, const void* k_cache, const void* v_cache,
+                                     const pkv_layout* layout, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t n_q_heads, float scale, void* out, int32_t part_tokens,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+    pkv_status st = paged_attention_partitions(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
+                                               context_lens, num_seqs, n_q_heads, scale, out, part_tokens,
+                                               workspace, ws_bytes, stream);
+    if (st != PKV_OK) return st;
+    return paged_attention_merge(layout, max_blocks_per_seq, context_lens, num_seqs, n_q_heads, out,
+                                 part_tokens, workspace, ws_bytes, stream);
+}
+
+pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                  const pkv_layout* layout, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t n_q_heads, float scale, void* out, void* stream) {
+    pkv_status st = check_decode(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
+                                 context_lens, num_seqs, n_q_heads, scale, out);
+    if (st != PKV_OK) return st;
+    int32_t P = 0;
+    st = resolve_partition(0, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P);
+    if (st != PKV_OK) return st;
+    const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
+    void* ws = nullptr;
+    st = library_workspace(pl.ws_bytes, &ws);
+    if (st != PKV_OK) return st;
+    return paged_attention_decode_ws(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
+                                     context_lens, num_seqs, n_q_heads, scale, out, P, ws, pl.ws_bytes,
+                                     stream);
+}
+
+pkv_status pkv_set_partition_tokens(int32_t tokens) {
+    if (tokens < 0 || tokens % kGpuBlockSize != 0)
+        return fail(PKV_EINVAL, "partition length %d is not 0 or a positive multiple of %d", tokens,
+                    kGpuBlockSize);
+    g_part_tokens.store(tokens);
+    return PKV_OK;
+}
+
+int32_t pkv_partition_tokens_for(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks_per_seq,
+                                 const pkv_layout* layout) {
+    if (check_layout(layout) != PKV_OK) return 0;
+    int32_t P = 0;
+    if (resolve_partition(0, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P) != PKV_OK) return 0;
+    return P;
+}
+
+pkv_status pkv_validate(const pkv_layout* layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, const int32_t* positions, int32_t num_seqs) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || max_blocks_per_seq < 1) return fail(PKV_EINVAL, "bad num_seqs or max_blocks_per_seq");
+    if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PKV_EINVAL, "a required pointer is NULL");
+    const int64_t B = layout->block_size;
+    std::vector<int64_t> slots;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+        const int64_t L = context_lens[s];
+        if (L < 0 || L > (int64_t)max_blocks_per_seq * B)
+            return fail(PKV_EOOB, "sequence %d: context length %lld outside [0, %lld]", s, (long long)L,
+                        (long long)max_blocks_per_seq * B);
+        const int64_t nb = (L + B - 1) / B;
+        for (int64_t b = 0; b < nb; ++b)
+            if (row[b] < 0 || row[b] >= layout->num_blocks)
+                return fail(PKV_EOOB, "sequence %d: table entry %lld = %d outside [0, %d)", s, (long long)b,
+                            row[b], layout->num_blocks);
+        if (positions) {
+            const int64_t p = positions[s];
+            if (p < 0 || p / B >= max_blocks_per_seq)
+                return fail(PKV_EOOB, "sequence %d: position %lld outside the table", s, (long long)p);
+            const int32_t blk = row[p / B];
+            if (blk < 0 || blk >= layout->num_blocks)
+                return fail(PKV_EOOB, "sequence %d: position %lld maps to block %d outside [0, %d)", s,
+                            (long long)p, blk, layout->num_blocks);
+            slots.push_back((int64_t)blk * B + p % B);
+        }
+    }
+    if (!slots.empty()) {
+        std::vector<int64_t> sorted = slots;
+        std::sort(sorted.begin(), sorted.end());
+        for (size_t i = 1; i < sorted.size(); ++i)
+            if (sorted[i] == sorted[i - 1])
+                return fail(PKV_EINVAL, "two sequences append to slot %lld", (long long)sorted[i]);
+    }
+    return PKV_OK;
+}
+
+const char* pkv_last_error(void) {
+    return g_last_error.c_str();
+}
+
+const char* pkv_version(void) {
+    return "pagedkv 0.1 gfx950";
+}
+
+pkv_status pkv_probe_read(const void* src, size_t bytes, float* sink, void* stream) {
+    if (!src || !sink || bytes % 16 != 0) return fail(PKV_EINVAL, "probe_read: NULL pointer or size not a multiple of 16");
+    hipError_t e = pkv::launch_probe_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "probe_read launch");
+    return PKV_OK;
+}
+
+pkv_status pkv_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (!src || !dst || bytes % 16 != 0) return fail(PKV_EINVAL, "probe_copy: NULL pointer or size not a multiple of 16");
+    hipError_t e = pkv::launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "probe_copy launch");
+    return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// pkv_launch.h -- parameter blocks and launchers shared between the C-ABI
+// wrapper (pagedkv_abi.hip) and the kernel sources.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendParams {
+    const void* k_new;
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* positions;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t row_bytes;  // n_kv_heads * head_dim * element bytes
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    void* out;
+    float* ws_acc;  // [num_seqs][n_q_heads][n_parts_max][head_dim]
+    float* ws_ml;   // [num_seqs][n_q_heads][n_parts_max][2]: running max (log2 units), sum
+    int32_t num_blocks;
+    int32_t n_kv_heads;
+    int32_t n_q_heads;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t part_tokens;
+    int32_t n_parts_max;
+    float scale_log2;  // scale * log2(e): scores are kept in base-2 units
+};
+
+// Each returns hipSuccess or the launch error.  dtype: 0 f32, 1 f16, 2 bf16.
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int group,
+                                    hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
+bool decode_supported(int dtype, int head_dim, int group);
+
+hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace pkv

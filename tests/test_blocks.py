@@ -116,8 +116,8 @@ def test_random_traffic_never_leaks(ops, B):
         try:
             if op == "new" or not live:
                 s = Sequence("s", alloc)
+                live.append(s)  # tracked before it grows: a failed grow keeps what it got
                 s.append_tokens(n % 20)
-                live.append(s)
             elif op == "grow":
                 live[n % len(live)].append_tokens(n % 7)
             elif op == "fork":
