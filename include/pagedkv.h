@@ -114,12 +114,16 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_cache, 
  *   scale         multiplies every score (usually 1 / sqrt(head_dim))
  *   out           [num_seqs][n_q_heads][head_dim], element type layout->dtype
  *
- * Long contexts are split into partitions of P tokens (a multiple of B; chosen
- * by the library, see pkv_set_partition_tokens) whose partial softmax states
- * are combined by the log-sum-exp rule.  The split-K workspace is owned by the
- * library (one per device, grown on demand with hipMalloc, freed at unload);
- * callers that must not allocate use paged_attention_decode_ws.  Calls that
- * share the library workspace must be ordered (same stream, or synchronised).
+ * Work is split so that every wave of the GPU streams the same number of
+ * 16-token tiles whatever the mix of context lengths (the "flat" schedule):
+ * a sequence may be cut into several pieces whose partial softmax states
+ * (running max, sum of exponentials, unnormalised weighted sum of values) are
+ * combined by the log-sum-exp rule.  A fixed partition length can be asked
+ * for instead (pkv_set_partition_tokens, or paged_attention_decode_ws).  The
+ * split-K workspace is owned by the library (one per device, grown on demand
+ * with hipMalloc, freed at unload); callers that must not allocate use
+ * paged_attention_decode_ws.  Calls that share the library workspace must be
+ * ordered (same stream, or synchronised).
  */
 pkv_status paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
                                   const pkv_layout* layout, const int32_t* block_tables,
@@ -140,8 +144,12 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads,
  * paged_attention_decode_ws -- paged_attention_decode with an explicit
  * partition length and a caller-owned workspace.
  *
- *   part_tokens  partition length in tokens, a positive multiple of
- *                layout->block_size, or 0 for the library's choice
+ *   part_tokens  0 for the library's choice (the flat schedule, unless a
+ *                different default was set with pkv_set_partition_tokens), or
+ *                a fixed partition length: a positive multiple of
+ *                layout->block_size; each P-token partition of a sequence is
+ *                one workgroup's work and the partitions are merged by the
+ *                log-sum-exp rule
  *   workspace    device buffer of at least
  *                paged_attention_workspace_size(..., part_tokens) bytes,
  *                256-byte aligned; may be NULL when that size is 0
@@ -158,12 +166,15 @@ pkv_status paged_attention_decode_ws(const void* q, const void* k_cache, const v
 
 /*
  * The two passes of paged_attention_decode_ws, callable separately (same
- * arguments).  The partition pass writes `out` directly for sequences whose
- * context fits one partition and the per-partition softmax state
- * (running max, sum of exponentials, unnormalised weighted sum of values) to
- * the workspace for the others; the merge pass combines those states,
+ * arguments; the merge must follow the partition pass on the same workspace).
+ * The partition pass writes `out` directly for every (sequence, KV head) that
+ * one wave (flat schedule) or one partition (fixed partitions) covers whole,
+ * and the per-piece softmax state (running max, sum of exponentials,
+ * unnormalised weighted sum of values) to the workspace for the others; the
+ * merge pass combines those states,
  *     M = max_j m_j,   out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
- * and writes their rows of `out`.  The workspace layout is internal.
+ * and writes their rows of `out` (and the zero rows of empty sequences under
+ * the flat schedule).  The workspace layout is internal.
  */
 pkv_status paged_attention_partitions(const void* q, const void* k_cache, const void* v_cache,
                                       const pkv_layout* layout, const int32_t* block_tables,
@@ -180,11 +191,13 @@ pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_pe
 /*
  * Process-wide partition length used when a call passes 0 (and by
  * paged_attention_decode): a positive multiple of the block size, or 0 to
- * restore the library's automatic choice.  Returns PKV_EINVAL otherwise.
+ * restore the library's choice (the flat schedule; batches of more than 8000
+ * sequences, or with more than 2^30 tiles, use 512-token partitions).
+ * Returns PKV_EINVAL otherwise.
  */
 pkv_status pkv_set_partition_tokens(int32_t tokens);
 
-/* Partition length the library would use for these sizes (after the above). */
+/* Partition length the library would use for these sizes (0 = flat schedule). */
 int32_t pkv_partition_tokens_for(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks_per_seq,
                                  const pkv_layout* layout);
 

@@ -1,5 +1,5 @@
-// decode.hip -- paged decode attention on gfx950: split-K partition pass and
-// log-sum-exp merge.
+// decode.hip -- paged decode attention on gfx950: the split-K pass, in two
+// schedules, and the log-sum-exp merge.
 //
 // What is computed: for sequence s, query head h, KV head g = h / G
 // (G = n_q_heads / n_kv_heads) and L = context_lens[s],
@@ -9,29 +9,37 @@
 // formula"; the attention maths is unchanged by paging -- henryhe.ai,
 // "What's deliberately still missing").
 //
-// Partition pass (one workgroup per (partition j, KV head g, sequence s)):
-//   * a partition is P consecutive tokens (P / 16 whole blocks); its blocks
-//     are dealt round-robin to the workgroup's NW waves;
-//   * a wave streams one 16-token block at a time: the K tile and the V tile
-//     of head g (16 rows of head_dim elements, rows n_kv_heads * head_dim
-//     elements apart) with 16-byte loads, R = 8 lanes per row so that one
-//     load instruction reads 8 rows x 128 contiguous bytes; the next block's
-//     tiles are loaded while the current one is computed;
-//   * the G query heads that share head g reuse every K/V register tile, so
+// The unit of work is a tile: one 16-token block of one KV head of one
+// sequence, i.e. 16 K rows and 16 V rows of head_dim elements (rows are
+// n_kv_heads * head_dim elements apart in the cache).  A wave streams tiles:
+//   * loads: 16-byte nontemporal loads, R lanes per row, so one load
+//     instruction reads 64/R rows x 16R contiguous bytes; the tiles of the
+//     next DEPTH blocks are in flight while one is computed;
+//   * the G query heads sharing KV head g reuse every K/V register tile, so
 //     each K/V byte leaves HBM once per step;
 //   * QK: packed 16-bit dot products with fp32 accumulation (v_dot2), summed
-//     over the 8 lanes of a row with DPP; scores are kept in base-2 units
+//     over the R lanes of a row with DPP; scores are kept in base-2 units
 //     (scale * log2 e folded in) so the softmax uses v_exp_f32 directly;
 //   * online softmax per row group of lanes: running max m, sum l and the
 //     unnormalised accumulator acc; acc is rescaled only when some lane's max
 //     grows; rows past L (last block only) are masked by select, values too,
-//     so whatever those slots hold (NaN included) never reaches the output;
-//   * epilogue: the row groups of a wave, then the NW waves (through LDS),
-//     are combined by the log-sum-exp rule; a sequence whose context fits one
-//     partition gets its normalised output written here (rounded to the
-//     cache dtype), otherwise (m, l, acc) go to the workspace.
-// Merge pass (one wave per (s, h), sequences with >= 2 partitions only):
+//     so whatever those slots hold (NaN included) never reaches the output.
+// A run of consecutive tiles of one (sequence, KV head) -- a segment -- ends
+// with the row groups combined by the log-sum-exp rule; the segment's state
+// is then either the whole answer (normalised, rounded to the cache dtype
+// and written to out) or a partial record for the merge pass:
 //     M = max_j m_j,  out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
+//
+// Two schedules:
+//   * flat (the default): a persistent grid of W waves deals the flat stream
+//     of all tiles -- ordered by sequence, KV head, block -- into W equal
+//     contiguous ranges, so every wave does the same number of tiles whatever
+//     the length mix.  Segments are cut where a range ends; segment (pair j,
+//     wave w) keeps its record at index j + w, unique because j + w grows by
+//     at least one from one segment to the next.
+//   * fixed partitions: one workgroup per (P-token partition, KV head,
+//     sequence); its waves share the partition's blocks and combine through
+//     LDS.
 //
 // Everything is bound by HBM bandwidth: each (token, KV head) costs
 // 2 * head_dim * element bytes of reads and 4 * head_dim * G flops.
@@ -42,103 +50,78 @@
 
 namespace pkv {
 
-constexpr int kLanesPerRow = 8;
-constexpr int kWavesPerGroup = 4;
+// Launch shape: NW waves per workgroup, R lanes per K/V row, DEPTH tiles in
+// flight ahead of the one being computed, streaming (nontemporal) loads.
+template <int NW_, int R_, int DEPTH_, bool STREAM_>
+struct Tune {
+    static constexpr int NW = NW_;
+    static constexpr int R = R_;
+    static constexpr int DEPTH = DEPTH_;
+    static constexpr bool STREAM = STREAM_;
+};
 
-template <class E, int D, int G, int NW>
-__global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodeParams p) {
-    constexpr int VEC = E::kPerVec;       // elements per 16-byte vector
-    constexpr int RB = D * E::kBytes;     // bytes per (token, head) row
-    constexpr int CH = RB / 16;           // 16-byte chunks per row
-    constexpr int R = kLanesPerRow;       // lanes sharing one row
-    constexpr int CPL = CH / R;           // chunks per lane per row
-    constexpr int RPS = kWave / R;        // rows covered by one load instruction
-    constexpr int J = kBlock / RPS;       // rows per lane per block
-    constexpr int EPL = CPL * VEC;        // elements per lane per row
-    static_assert(CH % R == 0 && kBlock % RPS == 0, "row / lane mapping");
+// One wave's share of the attention for the G query heads of one KV head.
+template <class E, int D, int G, class TU>
+struct WaveAttn {
+    static constexpr int VEC = E::kPerVec;    // elements per 16-byte vector
+    static constexpr int RB = D * E::kBytes;  // bytes per (token, head) row
+    static constexpr int CH = RB / 16;        // 16-byte chunks per row
+    static constexpr int R = TU::R;           // lanes sharing one row
+    static constexpr int CPL = CH / R;        // chunks per lane per row
+    static constexpr int RPS = kWave / R;     // rows covered by one load instruction
+    static constexpr int J = kBlock / RPS;    // rows per lane per tile
+    static constexpr int EPL = CPL * VEC;     // elements per lane per row
+    static constexpr int NS = TU::DEPTH + 1;  // register tile slots
+    static_assert(CH % R == 0 && kBlock % RPS == 0 && J >= 1, "row / lane mapping");
 
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int s = blockIdx.z;
-    const int Hq = p.n_q_heads;
-    const int h0 = kvh * G;
-    // A length beyond the table is a caller error; clamping keeps every table
-    // read inside the row and every partition inside the workspace.
-    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
-    const int P = p.part_tokens;
-    const int n_parts = (L + P - 1) / P;
-
-    if (part >= n_parts) {
-        if (L == 0 && part == 0) {  // nothing to attend: a zero row
-            for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-                E::store(static_cast<char*>(p.out) +
-                             (((int64_t)s * Hq + h0 + i / D) * D + i % D) * E::kBytes,
-                         0.f);
-        }
-        return;
-    }
-
-    const int lane = threadIdx.x % kWave;
-    const int w = wave_id_uniform();
-    const int rg = lane / R;  // row group
-    const int c = lane % R;   // chunk column
-
-    const int nblk = (L + kBlock - 1) / kBlock;
-    const int PB = P / kBlock;
-    const int b_begin = part * PB;
-    const int b_end = min(b_begin + PB, nblk);
-    const int tail_rows = L - (nblk - 1) * kBlock;  // valid rows of the last block, 1..16
-
-    const uint32_t row_stride = (uint32_t)p.n_kv_heads * RB;  // bytes between token rows
-    const int64_t blk_bytes = (int64_t)row_stride * kBlock;
-    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
-    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
-    const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
-
+    int rg, c;  // row group and chunk column of this lane
     uint32_t lane_off[J][CPL];
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) lane_off[j][k] = (j * RPS + rg) * row_stride + (c + k * R) * 16;
-
-    // Query vectors of the G heads, the same chunks as this lane's K chunks.
     Vec16 qv[G][CPL];
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-        for (int k = 0; k < CPL; ++k)
-            qv[gi][k] = load16(static_cast<const char*>(p.q) +
-                               (((int64_t)s * Hq + h0 + gi) * D) * E::kBytes + (c + k * R) * 16);
-
     float acc[G][EPL];
     float m[G], l[G];
+    Vec16 kb[NS][J][CPL], vb[NS][J][CPL];
+
+    __device__ __forceinline__ void init(int lane, uint32_t row_stride) {
+        rg = lane / R;
+        c = lane % R;
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-        m[gi] = -INFINITY;
-        l[gi] = 0.f;
+        for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[gi][e] = 0.f;
+            for (int k = 0; k < CPL; ++k) lane_off[j][k] = (j * RPS + rg) * row_stride + (c + k * R) * 16;
     }
 
-    Vec16 kb[2][J][CPL], vb[2][J][CPL];
+    // q rows of the G heads (contiguous [G][D]), this lane's chunks only.
+    __device__ __forceinline__ void load_q(const char* q_rows) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) qv[gi][k] = load16(q_rows + gi * RB + (c + k * R) * 16);
+    }
 
-    auto issue = [&](int buf, int bi) {
-        int pb = __builtin_amdgcn_readfirstlane(table[bi]);
-        if (pb < 0 || pb >= p.num_blocks) pb = -1;
-        const int64_t boff = pb < 0 ? 0 : (int64_t)pb * blk_bytes;
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            m[gi] = -INFINITY;
+            l[gi] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[gi][e] = 0.f;
+        }
+    }
+
+    // Loads of one tile: rows of head g at kbase/vbase + boff.
+    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t boff) {
 #pragma unroll
         for (int j = 0; j < J; ++j)
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
-                kb[buf][j][k] = load16(kbase + boff + lane_off[j][k]);
-                vb[buf][j][k] = load16(vbase + boff + lane_off[j][k]);
+                kb[slot][j][k] = load16_policy<TU::STREAM>(kbase + boff + lane_off[j][k]);
+                vb[slot][j][k] = load16_policy<TU::STREAM>(vbase + boff + lane_off[j][k]);
             }
-        return pb;
-    };
+    }
 
-    auto process = [&](int buf, int bi, int pb) {
-        // rows of this block that belong to the sequence
-        const int valid = pb < 0 ? 0 : (bi == nblk - 1 ? tail_rows : kBlock);
+    // Online-softmax update with one tile; `valid` rows (wave-uniform) belong
+    // to the sequence, the rest are masked.
+    __device__ __forceinline__ void process(int slot, int valid, float scale_log2) {
         float sc[G][J];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi)
@@ -146,15 +129,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodePara
             for (int j = 0; j < J; ++j) {
                 float d = 0.f;
 #pragma unroll
-                for (int k = 0; k < CPL; ++k) d = E::dot(qv[gi][k], kb[buf][j][k], d);
-                sc[gi][j] = group_sum<R>(d) * p.scale_log2;
+                for (int k = 0; k < CPL; ++k) d = E::dot(qv[gi][k], kb[slot][j][k], d);
+                sc[gi][j] = group_sum<R>(d) * scale_log2;
             }
         float vf[J][EPL];
 #pragma unroll
         for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int k = 0; k < CPL; ++k) E::expand(vb[buf][j][k], &vf[j][k * VEC]);
-        if (valid < kBlock) {  // wave-uniform: only the last block, or a skipped one
+            for (int k = 0; k < CPL; ++k) E::expand(vb[slot][j][k], &vf[j][k * VEC]);
+        if (valid < kBlock) {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
                 const bool ok = j * RPS + rg < valid;
@@ -186,57 +169,372 @@ __global__ __launch_bounds__(NW * kWave) void decode_partition_kernel(DecodePara
                 for (int e = 0; e < EPL; ++e) acc[gi][e] = __builtin_fmaf(pj, vf[j][e], acc[gi][e]);
             }
         }
-    };
-
-    // Software pipeline: tiles of block i + NW load while block i computes.
-    int bi = b_begin + w;
-    int pb0 = 0, pb1 = 0;
-    if (bi < b_end) pb0 = issue(0, bi);
-    for (; bi < b_end; bi += 2 * NW) {
-        const int b1 = bi + NW;
-        if (b1 < b_end) pb1 = issue(1, b1);
-        process(0, bi, pb0);
-        const int b2 = b1 + NW;
-        if (b2 < b_end) pb0 = issue(0, b2);
-        if (b1 < b_end) process(1, b1, pb1);
     }
 
-    // Combine the row groups of this wave (lanes c, c+8, ..., c+56).
-    float lw[G];
+    // Combine the row groups (lanes c, c+R, c+2R, ...): afterwards every lane
+    // holds the wave's m, l and acc for its chunk column.
+    __device__ __forceinline__ void reduce_rowgroups() {
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-        float M = m[gi];
+        for (int gi = 0; gi < G; ++gi) {
+            float M = m[gi];
 #pragma unroll
-        for (int x = R; x < kWave; x <<= 1) M = fmaxf(M, shfl_xor(M, x));
-        const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[gi] - M);
-        float lsum = l[gi] * f;
+            for (int x = R; x < kWave; x <<= 1) M = fmaxf(M, shfl_xor(M, x));
+            const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[gi] - M);
+            float lsum = l[gi] * f;
 #pragma unroll
-        for (int x = R; x < kWave; x <<= 1) lsum += shfl_xor(lsum, x);
+            for (int x = R; x < kWave; x <<= 1) lsum += shfl_xor(lsum, x);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float a = acc[gi][e] * f;
+            for (int e = 0; e < EPL; ++e) {
+                float a = acc[gi][e] * f;
 #pragma unroll
-            for (int x = R; x < kWave; x <<= 1) a += shfl_xor(a, x);
-            acc[gi][e] = a;
+                for (int x = R; x < kWave; x <<= 1) a += shfl_xor(a, x);
+                acc[gi][e] = a;
+            }
+            m[gi] = M;
+            l[gi] = lsum;
         }
-        m[gi] = M;
-        lw[gi] = lsum;
     }
 
-    // Combine the waves through LDS.
-    __shared__ float sm_acc[NW][G][D];
-    __shared__ float sm_m[NW][G];
-    __shared__ float sm_l[NW][G];
-    if (rg == 0) {
+    // After reduce_rowgroups, row group 0 writes the normalised rows of the G
+    // heads ([G][D] at out_rows) ...
+    __device__ __forceinline__ void store_out(char* out_rows) const {
+        if (rg != 0) return;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const float inv = 1.f / l[gi];
+#pragma unroll
+            for (int k = 0; k < CPL; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    E::store(out_rows + (gi * D + (c + k * R) * VEC + e) * E::kBytes, acc[gi][k * VEC + e] * inv);
+        }
+    }
+
+    // ... or the partial record: acc [G][D] fp32 and (m, l) [G][2] fp32.
+    __device__ __forceinline__ void store_partial(float* rec_acc, float* rec_ml) const {
+        if (rg != 0) return;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) sm_acc[w][gi][(c + k * R) * VEC + e] = acc[gi][k * VEC + e];
+                for (int e = 0; e < VEC; e += 4)
+                    *reinterpret_cast<float4*>(rec_acc + gi * D + (c + k * R) * VEC + e) =
+                        make_float4(acc[gi][k * VEC + e], acc[gi][k * VEC + e + 1], acc[gi][k * VEC + e + 2],
+                                    acc[gi][k * VEC + e + 3]);
             if (c == 0) {
-                sm_m[w][gi] = m[gi];
-                sm_l[w][gi] = lw[gi];
+                rec_ml[gi * 2] = m[gi];
+                rec_ml[gi * 2 + 1] = l[gi];
+            }
+        }
+    }
+};
+
+// ============================================================================
+// Flat schedule: a persistent grid deals equal ranges of the tile stream.
+// ============================================================================
+
+template <class E, int D, int G, class TU>
+__global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParams p) {
+    using A = WaveAttn<E, D, G, TU>;
+    constexpr int NS = A::NS;
+    constexpr int DEPTH = TU::DEPTH;
+    extern __shared__ int32_t sh[];
+    const int S = p.num_seqs;
+    const int Hkv = p.n_kv_heads;
+    const int Hq = p.n_q_heads;
+    int32_t* Ls = sh;         // clamped context length per sequence
+    int32_t* pre = sh + S;    // pre[s] = tiles of sequences < s; pre[S] = all tiles
+
+    // Tile counts and their prefix sums (every workgroup computes them).
+    const int max_len = p.max_blocks * kBlock;
+    for (int i = threadIdx.x; i < S; i += blockDim.x) Ls[i] = min(max(p.context_lens[i], 0), max_len);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        int carry = 0;
+        for (int base = 0; base < S; base += kWave) {
+            const int i = base + lane;
+            int v = i < S ? ((Ls[i] + kBlock - 1) / kBlock) * Hkv : 0;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int y = __shfl_up(v, off, kWave);
+                if (lane >= off) v += y;
+            }
+            if (i < S) pre[i + 1] = carry + v;
+            carry += __shfl(v, kWave - 1, kWave);
+        }
+        if (lane == 0) pre[0] = 0;
+    }
+    __syncthreads();
+    const int T = pre[S];
+    const int Wt = gridDim.x * TU::NW;
+    const int per = max((T + Wt - 1) / Wt, p.min_tiles_per_worker);
+    if (blockIdx.x == 0) {  // the schedule, for the merge pass
+        if (threadIdx.x == 0) {
+            p.ws_hdr[0] = per;
+            p.ws_hdr[1] = T;
+        }
+        for (int i = threadIdx.x; i <= S; i += blockDim.x) p.ws_hdr[2 + i] = pre[i];
+    }
+
+    const int w = blockIdx.x * TU::NW + wave_id_uniform();
+    const int t0 = w * per;
+    const int t1 = min(t0 + per, T);
+    if (t0 >= T) return;
+
+    const int lane = threadIdx.x % kWave;
+    const uint32_t row_stride = (uint32_t)Hkv * A::RB;
+    const int64_t blk_bytes = (int64_t)row_stride * kBlock;
+    const char* kcache = static_cast<const char*>(p.k_cache);
+    const char* vcache = static_cast<const char*>(p.v_cache);
+
+    // Cursor over the tile stream: sequence, KV head, block, blocks of the sequence.
+    struct Cur {
+        int s, kvh, b, nb;
+    };
+    auto locate = [&](int t) {
+        int lo = 0, hi = S;  // largest s with pre[s] <= t (then t < pre[s + 1])
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pre[mid] <= t) lo = mid;
+            else hi = mid;
+        }
+        Cur q;
+        q.s = lo;
+        q.nb = (Ls[lo] + kBlock - 1) / kBlock;
+        const int r = t - pre[lo];
+        q.kvh = r / q.nb;
+        q.b = r - q.kvh * q.nb;
+        return q;
+    };
+    auto advance = [&](Cur& q) {
+        if (++q.b == q.nb) {
+            q.b = 0;
+            if (++q.kvh == Hkv) {
+                q.kvh = 0;
+                do {
+                    ++q.s;
+                } while (q.s < S && Ls[q.s] == 0);
+                q.nb = q.s < S ? (Ls[q.s] + kBlock - 1) / kBlock : 1;
+            }
+        }
+        q.s = __builtin_amdgcn_readfirstlane(q.s);
+        q.kvh = __builtin_amdgcn_readfirstlane(q.kvh);
+        q.b = __builtin_amdgcn_readfirstlane(q.b);
+        q.nb = __builtin_amdgcn_readfirstlane(q.nb);
+    };
+
+    A a;
+    a.init(lane, row_stride);
+    int pbs[NS];
+    auto issue = [&](int slot, const Cur& q) {
+        int pb = __builtin_amdgcn_readfirstlane(p.block_tables[(int64_t)q.s * p.max_blocks + q.b]);
+        if (pb < 0 || pb >= p.num_blocks) pb = -1;
+        const int64_t boff = pb < 0 ? 0 : (int64_t)pb * blk_bytes;
+        a.issue(slot, kcache + (int64_t)q.kvh * A::RB, vcache + (int64_t)q.kvh * A::RB, boff);
+        pbs[slot] = pb;
+    };
+
+    Cur cur = locate(t0);
+    cur.s = __builtin_amdgcn_readfirstlane(cur.s);
+    cur.kvh = __builtin_amdgcn_readfirstlane(cur.kvh);
+    cur.b = __builtin_amdgcn_readfirstlane(cur.b);
+    cur.nb = __builtin_amdgcn_readfirstlane(cur.nb);
+    Cur iss = cur;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (t0 + d < t1) {
+            issue(d, iss);
+            advance(iss);
+        }
+
+    int as = cur.s, akvh = cur.kvh;  // the segment being accumulated
+    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * G) * A::RB);
+    a.reset();
+
+    auto flush = [&]() {
+        a.reduce_rowgroups();
+        const int nb = (Ls[as] + kBlock - 1) / kBlock;
+        const int p0 = pre[as] + akvh * nb;  // the pair's tiles are [p0, p0 + nb)
+        if (p0 / per == (p0 + nb - 1) / per) {
+            a.store_out(static_cast<char*>(p.out) + ((int64_t)as * Hq + akvh * G) * D * E::kBytes);
+        } else {
+            const int64_t rec = (int64_t)as * Hkv + akvh + w;
+            a.store_partial(p.ws_acc + rec * G * D, p.ws_ml + rec * G * 2);
+        }
+    };
+
+    for (int t = t0; t < t1; t += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int tt = t + u;
+            if (tt + DEPTH < t1) {
+                issue((u + DEPTH) % NS, iss);
+                advance(iss);
+            }
+            if (tt < t1) {
+                if (cur.s != as || cur.kvh != akvh) {
+                    flush();
+                    as = cur.s;
+                    akvh = cur.kvh;
+                    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * G) * A::RB);
+                    a.reset();
+                }
+                const int pb = pbs[u];
+                const int valid = pb < 0 ? 0 : (cur.b == cur.nb - 1 ? Ls[cur.s] - cur.b * kBlock : kBlock);
+                a.process(u, valid, p.scale_log2);
+                advance(cur);
+            }
+        }
+    }
+    flush();
+}
+
+// One wave per (sequence, query head): combine the records of pairs that were
+// split between waves, and write zeros for empty sequences.
+template <class E, int D>
+__global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) {
+    constexpr int PER = (D + kWave - 1) / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int pair = blockIdx.x * (blockDim.x / kWave) + wave_id_uniform();
+    if (pair >= p.num_seqs * p.n_q_heads) return;
+    const int s = pair / p.n_q_heads;
+    const int h = pair % p.n_q_heads;
+    const int G = p.n_q_heads / p.n_kv_heads;
+    const int kvh = h / G;
+    const int gi = h % G;
+    char* out_row = static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes;
+    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
+    if (L == 0) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            if (lane + k * kWave < D) E::store(out_row + (lane + k * kWave) * E::kBytes, 0.f);
+        return;
+    }
+    const int per = p.ws_hdr[0];
+    const int nb = (L + kBlock - 1) / kBlock;
+    const int p0 = p.ws_hdr[2 + s] + kvh * nb;
+    const int w0 = p0 / per;
+    const int w1 = (p0 + nb - 1) / per;
+    if (w0 == w1) return;  // one wave held the whole pair and wrote it
+    const int64_t base = (int64_t)s * p.n_kv_heads + kvh;  // record of wave w is base + w
+
+    float M = -INFINITY;
+    for (int x = w0 + lane; x <= w1; x += kWave) M = fmaxf(M, p.ws_ml[((base + x) * G + gi) * 2]);
+    M = wave_max(M);
+    float num[PER], den = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) num[k] = 0.f;
+    for (int x = w0; x <= w1; ++x) {
+        const int64_t rec = (base + x) * G + gi;
+        const float f = __builtin_amdgcn_exp2f(p.ws_ml[rec * 2] - M);
+        den = __builtin_fmaf(f, p.ws_ml[rec * 2 + 1], den);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int d = lane + k * kWave;
+            if (d < D) num[k] = __builtin_fmaf(f, p.ws_acc[rec * D + d], num[k]);
+        }
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int d = lane + k * kWave;
+        if (d < D) E::store(out_row + d * E::kBytes, num[k] * inv);
+    }
+}
+
+// ============================================================================
+// Fixed partitions: one workgroup per (P-token partition, KV head, sequence).
+// ============================================================================
+
+template <class E, int D, int G, class TU>
+__global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(DecodeParams p) {
+    using A = WaveAttn<E, D, G, TU>;
+    constexpr int NW = TU::NW;
+    constexpr int NS = A::NS;
+    constexpr int DEPTH = TU::DEPTH;
+
+    const int part = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int s = blockIdx.z;
+    const int Hq = p.n_q_heads;
+    const int h0 = kvh * G;
+    // A length beyond the table is a caller error; clamping keeps every table
+    // read inside the row and every partition inside the workspace.
+    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
+    const int P = p.part_tokens;
+    const int n_parts = (L + P - 1) / P;
+
+    if (part >= n_parts) {
+        if (L == 0 && part == 0) {  // nothing to attend: a zero row
+            for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+                E::store(static_cast<char*>(p.out) + (((int64_t)s * Hq + h0 + i / D) * D + i % D) * E::kBytes,
+                         0.f);
+        }
+        return;
+    }
+
+    const int lane = threadIdx.x % kWave;
+    const int w = wave_id_uniform();
+    const int nblk = (L + kBlock - 1) / kBlock;
+    const int PB = P / kBlock;
+    const int b_begin = part * PB;
+    const int b_end = min(b_begin + PB, nblk);
+    const int tail_rows = L - (nblk - 1) * kBlock;  // valid rows of the last block, 1..16
+
+    const uint32_t row_stride = (uint32_t)p.n_kv_heads * A::RB;
+    const int64_t blk_bytes = (int64_t)row_stride * kBlock;
+    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * A::RB;
+    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * A::RB;
+    const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
+
+    A a;
+    a.init(lane, row_stride);
+    a.load_q(static_cast<const char*>(p.q) + ((int64_t)s * Hq + h0) * A::RB);
+    a.reset();
+    int pbs[NS];
+    auto issue = [&](int slot, int bi) {
+        int pb = __builtin_amdgcn_readfirstlane(table[bi]);
+        if (pb < 0 || pb >= p.num_blocks) pb = -1;
+        a.issue(slot, kbase, vbase, pb < 0 ? 0 : (int64_t)pb * blk_bytes);
+        pbs[slot] = pb;
+    };
+
+    // This wave's blocks are b_begin + w, + NW, ...
+    const int first = b_begin + w;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (first + d * NW < b_end) issue(d, first + d * NW);
+    for (int bi = first; bi < b_end; bi += NS * NW) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int b = bi + u * NW;
+            const int bn = b + DEPTH * NW;
+            if (bn < b_end) issue((u + DEPTH) % NS, bn);
+            if (b < b_end) {
+                const int valid = pbs[u] < 0 ? 0 : (b == nblk - 1 ? tail_rows : kBlock);
+                a.process(u, valid, p.scale_log2);
+            }
+        }
+    }
+    a.reduce_rowgroups();
+
+    // Combine the waves through LDS.
+    __shared__ float sm_acc[NW][G][D];
+    __shared__ float sm_m[NW][G];
+    __shared__ float sm_l[NW][G];
+    if (a.rg == 0) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+            for (int k = 0; k < A::CPL; ++k)
+#pragma unroll
+                for (int e = 0; e < A::VEC; ++e)
+                    sm_acc[w][gi][(a.c + k * A::R) * A::VEC + e] = a.acc[gi][k * A::VEC + e];
+            if (a.c == 0) {
+                sm_m[w][gi] = a.m[gi];
+                sm_l[w][gi] = a.l[gi];
             }
         }
     }
@@ -305,37 +603,77 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int d = lane + k * kWave;
-        if (d < D)
-            E::store(static_cast<char*>(p.out) + ((int64_t)pair * D + d) * E::kBytes, num[k] * inv);
+        if (d < D) E::store(static_cast<char*>(p.out) + ((int64_t)pair * D + d) * E::kBytes, num[k] * inv);
     }
 }
 
-// ---- dispatch ------------------------------------------------------------------
+// ============================================================================
+// Dispatch
+// ============================================================================
 
+// Launch shape per element type, head_dim and group size.
 template <class E, int D, int G>
-static hipError_t launch_parts_t(const DecodeParams& p, hipStream_t stream) {
+struct DefaultTune {
+    using type = Tune<4, 8, 1, true>;
+};
+
+template <class E, int D, int G, class TU>
+hipError_t launch_parts_tuned(const DecodeParams& p, hipStream_t stream) {
     const dim3 grid(p.n_parts_max, p.n_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, kWavesPerGroup>), grid,
-                       dim3(kWavesPerGroup * kWave), 0, stream, p);
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU>), grid, dim3(TU::NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
+// Workgroups of the flat kernel resident on the whole device, capped so the
+// grid's waves never exceed kMaxFlatWorkers.
+template <class E, int D, int G, class TU>
+hipError_t launch_flat_tuned(const DecodeParams& p, hipStream_t stream) {
+    auto kern = decode_flat_kernel<E, D, G, TU>;
+    const size_t lds = (size_t)(2 * p.num_seqs + 1) * sizeof(int32_t);
+    static thread_local int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
+    static thread_local size_t cached_lds = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev != cached_dev || lds != cached_lds) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, TU::NW * kWave, lds);
+        if (e != hipSuccess) return e;
+        cached_dev = dev;
+        cached_lds = lds;
+        cached_cus = cus;
+        cached_per_cu = per_cu < 1 ? 1 : per_cu;
+    }
+    int wgs = cached_cus * cached_per_cu;
+    if (wgs * TU::NW > kMaxFlatWorkers) wgs = kMaxFlatWorkers / TU::NW;
+    hipLaunchKernelGGL(kern, dim3(wgs), dim3(TU::NW * kWave), lds, stream, p);
+    return hipGetLastError();
+}
+
+template <class E, int D, int G>
+static hipError_t launch_g(const DecodeParams& p, bool flat, hipStream_t stream) {
+    using TU = typename DefaultTune<E, D, G>::type;
+    return flat ? launch_flat_tuned<E, D, G, TU>(p, stream) : launch_parts_tuned<E, D, G, TU>(p, stream);
+}
+
 template <class E, int D>
-static hipError_t launch_parts_g(const DecodeParams& p, int group, hipStream_t stream) {
+static hipError_t launch_d(const DecodeParams& p, int group, bool flat, hipStream_t stream) {
     switch (group) {
-        case 1: return launch_parts_t<E, D, 1>(p, stream);
-        case 2: return launch_parts_t<E, D, 2>(p, stream);
-        case 4: return launch_parts_t<E, D, 4>(p, stream);
-        case 8: return launch_parts_t<E, D, 8>(p, stream);
+        case 1: return launch_g<E, D, 1>(p, flat, stream);
+        case 2: return launch_g<E, D, 2>(p, flat, stream);
+        case 4: return launch_g<E, D, 4>(p, flat, stream);
+        case 8: return launch_g<E, D, 8>(p, flat, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <class E>
-static hipError_t launch_parts_d(const DecodeParams& p, int head_dim, int group, hipStream_t stream) {
+static hipError_t launch_e(const DecodeParams& p, int head_dim, int group, bool flat, hipStream_t stream) {
     switch (head_dim) {
-        case 64: return launch_parts_g<E, 64>(p, group, stream);
-        case 128: return launch_parts_g<E, 128>(p, group, stream);
+        case 64: return launch_d<E, 64>(p, group, flat, stream);
+        case 128: return launch_d<E, 128>(p, group, flat, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -347,21 +685,29 @@ bool decode_supported(int dtype, int head_dim, int group) {
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int group,
                                     hipStream_t stream) {
+    const bool flat = p.part_tokens == 0;
     switch (dtype) {
-        case 0: return launch_parts_d<F32>(p, head_dim, group, stream);
-        case 1: return launch_parts_d<F16>(p, head_dim, group, stream);
-        case 2: return launch_parts_d<BF16>(p, head_dim, group, stream);
+        case 0: return launch_e<F32>(p, head_dim, group, flat, stream);
+        case 1: return launch_e<F16>(p, head_dim, group, flat, stream);
+        case 2: return launch_e<BF16>(p, head_dim, group, flat, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <class E>
-static hipError_t launch_merge_d(const DecodeParams& p, int head_dim, hipStream_t stream) {
+static hipError_t launch_merge_e(const DecodeParams& p, int head_dim, hipStream_t stream) {
     const int pairs = p.num_seqs * p.n_q_heads;
     const dim3 grid((pairs + 3) / 4);
+    const bool flat = p.part_tokens == 0;
     switch (head_dim) {
-        case 64: hipLaunchKernelGGL((decode_merge_kernel<E, 64>), grid, dim3(256), 0, stream, p); break;
-        case 128: hipLaunchKernelGGL((decode_merge_kernel<E, 128>), grid, dim3(256), 0, stream, p); break;
+        case 64:
+            if (flat) hipLaunchKernelGGL((decode_flat_merge_kernel<E, 64>), grid, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((decode_merge_kernel<E, 64>), grid, dim3(256), 0, stream, p);
+            break;
+        case 128:
+            if (flat) hipLaunchKernelGGL((decode_flat_merge_kernel<E, 128>), grid, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((decode_merge_kernel<E, 128>), grid, dim3(256), 0, stream, p);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -369,9 +715,9 @@ static hipError_t launch_merge_d(const DecodeParams& p, int head_dim, hipStream_
 
 hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream) {
     switch (dtype) {
-        case 0: return launch_merge_d<F32>(p, head_dim, stream);
-        case 1: return launch_merge_d<F16>(p, head_dim, stream);
-        case 2: return launch_merge_d<BF16>(p, head_dim, stream);
+        case 0: return launch_merge_e<F32>(p, head_dim, stream);
+        case 1: return launch_merge_e<F16>(p, head_dim, stream);
+        case 2: return launch_merge_e<BF16>(p, head_dim, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -24,6 +24,7 @@ std::atomic<int32_t> g_part_tokens{0};
 
 constexpr int kGpuBlockSize = 16;
 constexpr int32_t kDefaultPartTokens = 512;
+constexpr int32_t kMinTilesPerWorker = 4;
 constexpr size_t kWsAlign = 256;
 
 pkv_status fail(pkv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -61,42 +62,57 @@ pkv_status hip_fail(hipError_t e, const char* what) {
     return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int32_t auto_partition_tokens(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks,
-                              const pkv_layout* L) {
-    (void)num_seqs;
-    (void)n_q_heads;
-    (void)max_blocks;
-    (void)L;
-    return kDefaultPartTokens;
+// The flat schedule serves a batch when its per-workgroup LDS holds the batch
+// and its tile count fits comfortably in int32.
+bool flat_fits(int32_t num_seqs, int32_t max_blocks, const pkv_layout* L) {
+    return num_seqs <= pkv::kMaxFlatSeqs &&
+           (int64_t)num_seqs * L->n_kv_heads * max_blocks <= ((int64_t)1 << 30);
 }
 
-pkv_status resolve_partition(int32_t requested, int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks,
-                             const pkv_layout* L, int32_t* out) {
+// 0 (the library's choice) selects the flat schedule: equal tile ranges per
+// wave, whatever the length mix.  Batches it cannot serve use 512-token
+// partitions.
+pkv_status resolve_partition(int32_t requested, int32_t num_seqs, int32_t max_blocks, const pkv_layout* L,
+                             int32_t* out) {
     int32_t P = requested;
     if (P == 0) P = g_part_tokens.load();
-    if (P == 0) P = auto_partition_tokens(num_seqs, n_q_heads, max_blocks, L);
     if (P < 0 || P % L->block_size != 0)
         return fail(PKV_EINVAL, "partition length %d is not a positive multiple of block_size %d", P,
                     L->block_size);
+    if (P == 0 && !flat_fits(num_seqs, max_blocks, L)) P = kDefaultPartTokens;
     *out = P;
     return PKV_OK;
 }
 
 struct Plan {
-    int32_t part_tokens;
-    int32_t n_parts_max;
-    size_t acc_bytes;  // ws_acc, rounded up to kWsAlign
-    size_t ws_bytes;   // total; 0 when no sequence can need a second partition
+    int32_t part_tokens;  // 0: flat schedule
+    int32_t n_parts_max;  // fixed partitions only
+    size_t hdr_bytes;     // flat only: the schedule header
+    size_t acc_bytes;
+    size_t ws_bytes;      // total; 0 when nothing is needed
 };
+
+size_t round_up(size_t x) {
+    return (x + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
 
 Plan make_plan(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks, const pkv_layout* L, int32_t P) {
     Plan pl{};
     pl.part_tokens = P;
+    if (P == 0) {
+        const size_t G = (size_t)n_q_heads / L->n_kv_heads;
+        const size_t recs = (size_t)num_seqs * L->n_kv_heads + pkv::kMaxFlatWorkers;
+        pl.n_parts_max = 1;
+        pl.hdr_bytes = round_up((size_t)(num_seqs + 3) * sizeof(int32_t));
+        pl.acc_bytes = round_up(recs * G * L->head_dim * sizeof(float));
+        pl.ws_bytes = pl.hdr_bytes + pl.acc_bytes + recs * G * 2 * sizeof(float);
+        return pl;
+    }
     const int64_t max_tokens = (int64_t)max_blocks * L->block_size;
     pl.n_parts_max = (int32_t)std::max<int64_t>(1, (max_tokens + P - 1) / P);
     if (pl.n_parts_max <= 1) return pl;
     const size_t slots = (size_t)num_seqs * n_q_heads * pl.n_parts_max;
-    pl.acc_bytes = (slots * L->head_dim * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
+    pl.acc_bytes = round_up(slots * L->head_dim * sizeof(float));
     pl.ws_bytes = pl.acc_bytes + slots * 2 * sizeof(float);
     return pl;
 }
@@ -141,8 +157,11 @@ pkv::DecodeParams make_params(const void* q, const void* k_cache, const void* v_
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.out = out;
-    p.ws_acc = static_cast<float*>(workspace);
-    p.ws_ml = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.acc_bytes) : nullptr;
+    char* ws = static_cast<char*>(workspace);
+    p.ws_hdr = ws ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    p.ws_acc = ws ? reinterpret_cast<float*>(ws + pl.hdr_bytes) : nullptr;
+    p.ws_ml = ws ? reinterpret_cast<float*>(ws + pl.hdr_bytes + pl.acc_bytes) : nullptr;
+    p.min_tiles_per_worker = kMinTilesPerWorker;
     p.num_blocks = L->num_blocks;
     p.n_kv_heads = L->n_kv_heads;
     p.n_q_heads = n_q_heads;
@@ -245,7 +264,7 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32
                                       const pkv_layout* layout, int32_t part_tokens) {
     if (check_layout(layout) != PKV_OK || num_seqs < 0 || n_q_heads < 1 || max_blocks_per_seq < 1) return 0;
     int32_t P = 0;
-    if (resolve_partition(part_tokens, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P) != PKV_OK)
+    if (resolve_partition(part_tokens, num_seqs, max_blocks_per_seq, layout, &P) != PKV_OK)
         return 0;
     return make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P).ws_bytes;
 }
@@ -259,7 +278,7 @@ pkv_status paged_attention_partitions(const void* q, const void* k_cache, const 
                                  context_lens, num_seqs, n_q_heads, scale, out);
     if (st != PKV_OK) return st;
     int32_t P = 0;
-    st = resolve_partition(part_tokens, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P);
+    st = resolve_partition(part_tokens, num_seqs, max_blocks_per_seq, layout, &P);
     if (st != PKV_OK) return st;
     const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
     st = check_workspace(pl, workspace, ws_bytes);
@@ -289,12 +308,14 @@ pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_pe
     if (!pkv::decode_supported(layout->dtype, layout->head_dim, n_q_heads / layout->n_kv_heads))
         return fail(PKV_ENOTSUP, "no kernel for dtype %d, head_dim %d", layout->dtype, layout->head_dim);
     int32_t P = 0;
-    st = resolve_partition(part_tokens, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P);
+    st = resolve_partition(part_tokens, num_seqs, max_blocks_per_seq, layout, &P);
     if (st != PKV_OK) return st;
     const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
     st = check_workspace(pl, workspace, ws_bytes);
     if (st != PKV_OK) return st;
-    if (num_seqs == 0 || pl.n_parts_max <= 1) return ok();  // every sequence was finished by the partition pass
+    // Fixed partitions: nothing to merge when no sequence can span two.  The flat
+    // schedule always runs its merge pass (split pairs, and zeros for L = 0).
+    if (num_seqs == 0 || (pl.part_tokens > 0 && pl.n_parts_max <= 1)) return ok();
     const pkv::DecodeParams p = make_params(nullptr, nullptr, nullptr, layout, nullptr, max_blocks_per_seq,
                                             context_lens, num_seqs, n_q_heads, 1.f, out, pl,
                                             const_cast<void*>(workspace));
@@ -324,7 +345,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
                                  context_lens, num_seqs, n_q_heads, scale, out);
     if (st != PKV_OK) return st;
     int32_t P = 0;
-    st = resolve_partition(0, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P);
+    st = resolve_partition(0, num_seqs, max_blocks_per_seq, layout, &P);
     if (st != PKV_OK) return st;
     const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
     void* ws = nullptr;
@@ -347,7 +368,7 @@ int32_t pkv_partition_tokens_for(int32_t num_seqs, int32_t n_q_heads, int32_t ma
                                  const pkv_layout* layout) {
     if (check_layout(layout) != PKV_OK) return 0;
     int32_t P = 0;
-    if (resolve_partition(0, num_seqs, n_q_heads, max_blocks_per_seq, layout, &P) != PKV_OK) return 0;
+    if (resolve_partition(0, num_seqs, max_blocks_per_seq, layout, &P) != PKV_OK) return 0;
     return P;
 }
 

@@ -31,6 +31,28 @@ __device__ __forceinline__ Vec16 load16(const void* p) {
     return v;
 }
 
+typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
+
+// Streaming load: the nontemporal hint marks the lines for early eviction, the
+// right policy for K/V tiles that each step reads exactly once.
+__device__ __forceinline__ Vec16 load16_stream(const void* p) {
+    const v4u32_t u = __builtin_nontemporal_load(reinterpret_cast<const v4u32_t*>(p));
+    Vec16 v;
+    v.w[0] = u.x;
+    v.w[1] = u.y;
+    v.w[2] = u.z;
+    v.w[3] = u.w;
+    return v;
+}
+
+template <bool Stream>
+__device__ __forceinline__ Vec16 load16_policy(const void* p) {
+    if constexpr (Stream)
+        return load16_stream(p);
+    else
+        return load16(p);
+}
+
 __device__ __forceinline__ void store16(void* p, const Vec16& v) {
     *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
 }

@@ -21,6 +21,13 @@ struct AppendParams {
     int32_t row_bytes;  // n_kv_heads * head_dim * element bytes
 };
 
+// The flat schedule's grid never has more waves than this; its workspace is
+// sized for it.
+constexpr int kMaxFlatWorkers = 8192;
+// Largest batch the flat schedule serves (its per-workgroup LDS holds two
+// int32 per sequence); larger batches use fixed partitions.
+constexpr int kMaxFlatSeqs = 8000;
+
 struct DecodeParams {
     const void* q;
     const void* k_cache;
@@ -28,15 +35,21 @@ struct DecodeParams {
     const int32_t* block_tables;
     const int32_t* context_lens;
     void* out;
-    float* ws_acc;  // [num_seqs][n_q_heads][n_parts_max][head_dim]
-    float* ws_ml;   // [num_seqs][n_q_heads][n_parts_max][2]: running max (log2 units), sum
+    // Split-K workspace.  Fixed partitions: ws_acc [num_seqs][n_q_heads][n_parts_max][head_dim],
+    // ws_ml [..][2] (running max in log2 units, sum).  Flat schedule: records
+    // [num_seqs * n_kv_heads + kMaxFlatWorkers][G][head_dim] and [..][G][2], and
+    // ws_hdr = {tiles per wave, total tiles, tile prefix per sequence [num_seqs + 1]}.
+    float* ws_acc;
+    float* ws_ml;
+    int32_t* ws_hdr;
     int32_t num_blocks;
     int32_t n_kv_heads;
     int32_t n_q_heads;
     int32_t max_blocks;
     int32_t num_seqs;
-    int32_t part_tokens;
+    int32_t part_tokens;  // 0 selects the flat schedule
     int32_t n_parts_max;
+    int32_t min_tiles_per_worker;
     float scale_log2;  // scale * log2(e): scores are kept in base-2 units
 };
 

@@ -149,3 +149,34 @@ def test_prefix_shared_equals_copied():
 def test_long_context_sampled():
     w = W.long_context()
     _sampled_check(w, 1, part_tokens=w.part_tokens)
+
+
+# ---- the flat schedule's edge cases ---------------------------------------------------------
+
+def test_flat_many_short_sequences():
+    rng = np.random.default_rng(82)
+    lens = rng.integers(1, 40, size=3000)
+    w = W.small(len(lens), lens, 4, 2, 64, "bf16", seed=82)
+    _full_check(w)
+
+
+def test_flat_empty_sequences_between():
+    lens = [0, 17, 0, 0, 300, 1, 0, 64, 0]
+    w = W.small(len(lens), [max(L, 1) for L in lens], 8, 4, 128, "f16", seed=83)
+    w.context_lens[:] = lens
+    w2 = poisoned(w)
+    T, out = gpu_step(w2)
+    _, _, ref_out = oracle_step(w2)
+    o = out.float().cpu().numpy()
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(o[s], np.zeros_like(o[s]))
+    assert max_err(out, ref_out) <= TOL["f16"]
+
+
+def test_flat_equals_partitions_within_tolerance():
+    lens = [5000, 33, 2048, 700]
+    w = W.small(len(lens), lens, 32, 8, 128, "bf16", seed=84)
+    a = _full_check(w)                  # flat schedule
+    b = _full_check(w, part_tokens=512)  # fixed partitions
+    assert float((a.float() - b.float()).abs().max()) <= 2e-2
