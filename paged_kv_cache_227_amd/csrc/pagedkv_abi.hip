@@ -344,6 +344,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
     pkv_status st = check_decode(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
                                  context_lens, num_seqs, n_q_heads, scale, out);
     if (st != PKV_OK) return st;
+    if (num_seqs == 0) return ok();
     int32_t P = 0;
     st = resolve_partition(0, num_seqs, max_blocks_per_seq, layout, &P);
     if (st != PKV_OK) return st;
