@@ -68,7 +68,7 @@ def make_workload(name):
     return W.CONFIGS[name]()
 
 
-def run_gpu(w, steps, warmup, extras):
+def run_gpu(w, steps, warmup, extras, graph=False):
     import torch
     import paged_kv_cache_227_amd as P
     from paged_kv_cache_227_amd import workloads as W
@@ -97,18 +97,45 @@ def run_gpu(w, steps, warmup, extras):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    res_graph = {}
+    if graph:
+        # the whole step as one HIP graph, replayed
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            step()
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        res_graph["graph_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
+    # The timed region: exactly `steps` steps between two synchronisations,
+    # nothing else on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    # Right after it, the same steps with HIP events around every kernel (on
+    # torch's current stream, where the library launches): per-kernel durations.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / steps
     t_app = [e[0].elapsed_time(e[1]) for e in events]
     t_part = [e[1].elapsed_time(e[2]) for e in events]
     t_merge = [e[2].elapsed_time(e[3]) for e in events]
-    res = dict(ms_per_step=ms_step, part_tokens=part,
+    res = dict(ms_per_step=ms_step, part_tokens=part, **res_graph,
+               kernel="decode_flat_kernel" if part == 0 else "decode_partition_kernel",
                partition_ms_mean=statistics.fmean(t_part), partition_ms_median=statistics.median(t_part),
                partition_ms_p10=sorted(t_part)[len(t_part) // 10],
                partition_ms_p90=sorted(t_part)[(len(t_part) * 9) // 10],
@@ -204,6 +231,41 @@ def summarize_pmc(d):
     return out
 
 
+def write_traffic(fetch_dir, write_dir, config, kv_bytes, copy_bytes, out_path):
+    """HBM traffic per launch of the decode kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain copy kernel of known size in the same run."""
+    f, w = summarize_pmc(fetch_dir), summarize_pmc(write_dir)
+
+    def pick(d, key):
+        names = [n for n in d if key in n]
+        if len(names) != 1:
+            raise SystemExit("expected one kernel matching %r, found %r" % (key, names))
+        return d[names[0]], names[0]
+
+    copy_f, _ = pick(f, "probe_copy_kernel")
+    copy_w, _ = pick(w, "probe_copy_kernel")
+    dec_f, name = pick(f, "decode_flat_kernel")
+    dec_w, _ = pick(w, "decode_flat_kernel")
+    copy_kib = copy_bytes / 1024.0
+    f_scale = copy_kib / copy_f["FETCH_SIZE"]["mean"]
+    w_scale = copy_kib / copy_w["WRITE_SIZE"]["mean"]
+    read_b = dec_f["FETCH_SIZE"]["mean"] * f_scale * 1024
+    write_b = dec_w["WRITE_SIZE"]["mean"] * w_scale * 1024
+    t = {"config": config, "kernel": name, "kernel_hash": kernel_hash(),
+         "fetch_size_kib_raw": dec_f["FETCH_SIZE"]["mean"], "write_size_kib_raw": dec_w["WRITE_SIZE"]["mean"],
+         "dispatches": dec_f["FETCH_SIZE"]["dispatches"],
+         "copy_probe_bytes": copy_bytes, "copy_fetch_kib_raw": copy_f["FETCH_SIZE"]["mean"],
+         "copy_write_kib_raw": copy_w["WRITE_SIZE"]["mean"], "fetch_scale": f_scale, "write_scale": w_scale,
+         "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+         "hbm_bytes_per_launch": read_b + write_b, "algorithmic_kv_bytes": kv_bytes,
+         "read_over_algorithmic": read_b / kv_bytes}
+    with open(out_path, "w") as fh:
+        json.dump(t, fh, indent=1)
+        fh.write("\n")
+    return t
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,10 +276,25 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<config>.json from two rocprofv3 --pmc runs of this bench "
+                         "made with --copy-probe-bytes (pass the same size)")
+    ap.add_argument("--graph", action="store_true", help="also time the step as a replayed HIP graph")
+    ap.add_argument("--copy-probe-bytes", type=int, default=0,
+                    help="after the steps, run the plain copy kernel once over this many bytes "
+                         "(a launch of known traffic for calibrating hardware counters)")
     a = ap.parse_args()
 
     if a.summarize_pmc:
         print(json.dumps(summarize_pmc(a.summarize_pmc), indent=1))
+        return 0
+    if a.write_traffic:
+        w = make_workload(a.config)
+        if not a.copy_probe_bytes:
+            raise SystemExit("--write-traffic needs --copy-probe-bytes (the size the counter runs used)")
+        t = write_traffic(a.write_traffic[0], a.write_traffic[1], a.config, w.kv_read_bytes(),
+                          a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=a.config))
+        print(json.dumps(t, indent=1))
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
@@ -233,7 +310,7 @@ def main():
     log("workload %s: %d sequences, %d tokens, KV bytes %.3f GB (generated in %.1f s)"
         % (w.name, w.num_seqs, int(w.context_lens.sum()), w.kv_read_bytes() / 1e9, time.perf_counter() - t))
     kv = w.kv_read_bytes()
-    g = run_gpu(w, a.steps, a.warmup, not a.no_extras)
+    g = run_gpu(w, a.steps, a.warmup, not a.no_extras, graph=a.graph)
     log("gpu: %.4f ms/step, partition %.4f ms, merge %.4f ms, append %.4f ms"
         % (g["ms_per_step"], g["partition_ms_mean"], g["merge_ms_mean"], g["append_ms_mean"]))
 
@@ -241,8 +318,9 @@ def main():
     traffic = load_traffic(w.name, kv)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
-                "kernel": "decode_partition_kernel", "algorithmic_bytes_per_launch": kv,
+                "traffic": None if traffic is None else round(traffic["hbm_bytes_per_launch"]),
+                "kernel": g["kernel"], "algorithmic_bytes_per_launch": kv,
+                "timing": "HIP events around each launch, %d steps right after the timed region" % a.steps,
                 "mean_launch_ms": round(g["partition_ms_mean"], 5)}
     value = kv / (g["ms_per_step"] * 1e-3) / 1e9
     res = {
@@ -260,6 +338,7 @@ def main():
         "kernel_ms": {k: round(g[k], 5) for k in ("partition_ms_mean", "partition_ms_median",
                                                   "partition_ms_p10", "partition_ms_p90",
                                                   "merge_ms_mean", "append_ms_mean")},
+        "step_ms_variants": {k: round(g[k], 5) for k in ("graph_ms_per_step",) if k in g},
     }
     if not a.no_extras:
         from paged_kv_cache_227_amd import workloads as W
@@ -272,6 +351,17 @@ def main():
             t_seq = time_partitions_only(seq)
             res["shuffled_vs_in_order_throughput"] = round(t_seq / g["partition_ms_mean"], 4)
             del seq
+    if a.copy_probe_bytes:
+        import torch
+        import paged_kv_cache_227_amd as P
+        n = a.copy_probe_bytes // 16 * 16
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        P.probe_copy(src, dst)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = n
+        del src, dst
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -45,6 +45,8 @@
 // 2 * head_dim * element bytes of reads and 4 * head_dim * G flops.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
@@ -52,12 +54,13 @@ namespace pkv {
 
 // Launch shape: NW waves per workgroup, R lanes per K/V row, DEPTH tiles in
 // flight ahead of the one being computed, streaming (nontemporal) loads.
-template <int NW_, int R_, int DEPTH_, bool STREAM_>
+template <int NW_, int R_, int DEPTH_, bool STREAM_, bool MFMA_ = false>
 struct Tune {
     static constexpr int NW = NW_;
     static constexpr int R = R_;
     static constexpr int DEPTH = DEPTH_;
     static constexpr bool STREAM = STREAM_;
+    static constexpr bool MFMA = MFMA_;  // matrix-core engine (16-bit caches, G >= 4)
 };
 
 // One wave's share of the attention for the G query heads of one KV head.
@@ -72,6 +75,7 @@ struct WaveAttn {
     static constexpr int J = kBlock / RPS;    // rows per lane per tile
     static constexpr int EPL = CPL * VEC;     // elements per lane per row
     static constexpr int NS = TU::DEPTH + 1;  // register tile slots
+    static constexpr int kLdsBytes = 0;       // per wave
     static_assert(CH % R == 0 && kBlock % RPS == 0 && J >= 1, "row / lane mapping");
 
     int rg, c;  // row group and chunk column of this lane
@@ -81,7 +85,7 @@ struct WaveAttn {
     float m[G], l[G];
     Vec16 kb[NS][J][CPL], vb[NS][J][CPL];
 
-    __device__ __forceinline__ void init(int lane, uint32_t row_stride) {
+    __device__ __forceinline__ void init(int lane, uint32_t row_stride, char*) {
         rg = lane / R;
         c = lane % R;
 #pragma unroll
@@ -173,7 +177,7 @@ struct WaveAttn {
 
     // Combine the row groups (lanes c, c+R, c+2R, ...): afterwards every lane
     // holds the wave's m, l and acc for its chunk column.
-    __device__ __forceinline__ void reduce_rowgroups() {
+    __device__ __forceinline__ void reduce() {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             float M = m[gi];
@@ -195,7 +199,7 @@ struct WaveAttn {
         }
     }
 
-    // After reduce_rowgroups, row group 0 writes the normalised rows of the G
+    // After reduce, row group 0 writes the normalised rows of the G
     // heads ([G][D] at out_rows) ...
     __device__ __forceinline__ void store_out(char* out_rows) const {
         if (rg != 0) return;
@@ -230,21 +234,239 @@ struct WaveAttn {
     }
 };
 
+// ----------------------------------------------------------------------------
+// Matrix-core engine for 16-bit caches and G >= 4: per tile,
+//   S^T[16 tok][16 heads]  = K[16][D] . Q^T[D][16]          (D/32 MFMA 16x16x32)
+//   O^T[D][16 heads]      += V^T[D][16 tok] . P^T[16][16]     (D/16 x 2 MFMA 16x16x16)
+// with the G query heads in columns 0..G-1 (the others are zero padding).
+// Lane l = 16 g + j holds S^T rows 4g..4g+3 of column j, which is exactly the
+// B operand P^T of the second product, so the softmax state of head j lives in
+// lane column j and never moves between lanes.  K is loaded straight into the
+// A-operand layout (lane: row j, 16-byte chunk 4kk + g); V goes through LDS
+// (rows written with 16-byte stores, 32-byte chunks swizzled by row) and comes
+// back transposed with ds_read_b64_tr_b16.  P is rounded to the 16-bit type as
+// a sum hi + lo of two 16-bit values, so the product keeps ~16 bits of P.
+// ----------------------------------------------------------------------------
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+template <class E>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<BF16> {
+    typedef __bf16 v8_t __attribute__((ext_vector_type(8)));
+    typedef __bf16 tr_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+    typedef s16x4_t op4_t;
+    __device__ static __forceinline__ f32x4_t qk(const Vec16& a, const Vec16& b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8_t, a), __builtin_bit_cast(v8_t, b), c, 0,
+                                                       0, 0);
+    }
+    __device__ static __forceinline__ op4_t read_tr(const char* p) {
+        auto q = (__attribute__((address_space(3))) tr_t*)((__attribute__((address_space(3))) char*)(p));
+        return __builtin_bit_cast(op4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q));
+    }
+    __device__ static __forceinline__ f32x4_t pv(op4_t a, op4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ void split(float x, short& hi, short& lo) {
+        const __bf16 h = (__bf16)x;
+        hi = __builtin_bit_cast(short, h);
+        lo = __builtin_bit_cast(short, (__bf16)(x - (float)h));
+    }
+};
+
+template <>
+struct MfmaOps<F16> {
+    typedef _Float16 v8_t __attribute__((ext_vector_type(8)));
+    typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
+    typedef __fp16 tr_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+    typedef v4h_t op4_t;
+    __device__ static __forceinline__ f32x4_t qk(const Vec16& a, const Vec16& b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8_t, a), __builtin_bit_cast(v8_t, b), c, 0, 0,
+                                                      0);
+    }
+    __device__ static __forceinline__ op4_t read_tr(const char* p) {
+        auto q = (__attribute__((address_space(3))) tr_t*)((__attribute__((address_space(3))) char*)(p));
+        return __builtin_bit_cast(op4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16(q));
+    }
+    __device__ static __forceinline__ f32x4_t pv(op4_t a, op4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ void split(float x, short& hi, short& lo) {
+        const _Float16 h = (_Float16)x;
+        hi = __builtin_bit_cast(short, h);
+        lo = __builtin_bit_cast(short, (_Float16)(x - (float)h));
+    }
+};
+
+template <class E, int D, int G, class TU>
+struct MfmaAttn {
+    static_assert(E::kBytes == 2 && G <= 16 && D % 32 == 0, "16-bit caches, up to 16 heads per KV head");
+    using OPS = MfmaOps<E>;
+    using op4_t = typename OPS::op4_t;
+    static constexpr int RB = D * 2;             // bytes per row
+    static constexpr int CH = RB / 16;           // 16-byte chunks per row
+    static constexpr int KK = D / 32;            // QK products
+    static constexpr int TT = D / 16;            // PV output tiles
+    static constexpr int RPI = kWave / CH;       // V rows per load instruction
+    static constexpr int VI = kBlock / RPI;      // V load instructions per tile
+    static constexpr int NT32 = RB / 32;         // 32-byte chunks per row (swizzle modulus)
+    static constexpr int NS = TU::DEPTH + 1;     // register tile slots
+    static constexpr int kBufBytes = kBlock * RB;
+    static constexpr int kLdsBytes = 2 * kBufBytes;  // per wave: two V staging buffers
+
+    int g, j;
+    char* lds;
+    uint32_t k_off[KK], v_off[VI], v_lds[VI], tr_lds[TT];
+    Vec16 qb[KK];
+    f32x4_t acc[TT];
+    float m, l;
+    Vec16 kt[NS][KK], vt[NS][VI];
+
+    __device__ __forceinline__ static uint32_t swz(int row, int chunk32) {
+        return (uint32_t)(row * RB + ((chunk32 ^ (row % NT32)) * 32));
+    }
+
+    __device__ __forceinline__ void init(int lane, uint32_t row_stride, char* lds_wave) {
+        g = lane / 16;
+        j = lane % 16;
+        lds = lds_wave;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) k_off[kk] = j * row_stride + (4 * kk + g) * 16;
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            const int row = i * RPI + lane / CH;
+            const int c16 = lane % CH;
+            v_off[i] = row * row_stride + c16 * 16;
+            v_lds[i] = swz(row, c16 / 2) + (c16 % 2) * 16;
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t) tr_lds[t] = swz(4 * g + j / 4, t) + 8 * (j % 4);
+    }
+
+    __device__ __forceinline__ void load_q(const char* q_rows) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            Vec16 z = {{0u, 0u, 0u, 0u}};
+            qb[kk] = j < G ? load16(q_rows + j * RB + (4 * kk + g) * 16) : z;
+        }
+    }
+
+    __device__ __forceinline__ void reset() {
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t boff) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kt[slot][kk] = load16_policy<TU::STREAM>(kbase + boff + k_off[kk]);
+#pragma unroll
+        for (int i = 0; i < VI; ++i) vt[slot][i] = load16_policy<TU::STREAM>(vbase + boff + v_off[i]);
+    }
+
+    __device__ __forceinline__ void process(int slot, int valid, float scale_log2) {
+        char* buf = lds + (slot & 1) * kBufBytes;
+        const int lane = g * 16 + j;
+        // V rows into LDS; rows past `valid` are written as zeros.
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            Vec16 v = vt[slot][i];
+            if (valid < kBlock && i * RPI + lane / CH >= valid) v = Vec16{{0u, 0u, 0u, 0u}};
+            store16(buf + v_lds[i], v);
+        }
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sacc = OPS::qk(kt[slot][kk], qb[kk], sacc);
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sc[r] = sacc[r] * scale_log2;
+            if (valid < kBlock && 4 * g + r >= valid) sc[r] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        if (__builtin_amdgcn_ballot_w64(mn > m)) {
+            const float alpha = __builtin_amdgcn_exp2f(m - ms);
+            l *= alpha;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[t] *= alpha;
+            m = mn;
+        }
+        op4_t phi, plo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(sc[r] - ms);
+            l += pr;
+            short h, lo;
+            OPS::split(pr, h, lo);
+            phi[r] = __builtin_bit_cast(typename std::remove_reference<decltype(phi[0])>::type, h);
+            plo[r] = __builtin_bit_cast(typename std::remove_reference<decltype(plo[0])>::type, lo);
+        }
+        // the V rows this wave just stored are read back by other lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const op4_t a = OPS::read_tr(buf + tr_lds[t]);
+            acc[t] = OPS::pv(a, phi, acc[t]);
+            acc[t] = OPS::pv(a, plo, acc[t]);
+        }
+    }
+
+    __device__ __forceinline__ void reduce() {
+        l += shfl_xor(l, 16);
+        l += shfl_xor(l, 32);
+    }
+
+    __device__ __forceinline__ void store_out(char* out_rows) const {
+        if (j >= G) return;
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) E::store(out_rows + (j * D + 16 * t + 4 * g + r) * 2, acc[t][r] * inv);
+    }
+
+    __device__ __forceinline__ void store_partial(float* rec_acc, float* rec_ml) const {
+        if (j >= G) return;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            *reinterpret_cast<float4*>(rec_acc + j * D + 16 * t + 4 * g) =
+                make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+        if (g == 0) {
+            rec_ml[j * 2] = m;
+            rec_ml[j * 2 + 1] = l;
+        }
+    }
+};
+
+template <class E, int D, int G, class TU>
+using Engine = typename std::conditional<TU::MFMA, MfmaAttn<E, D, G, TU>, WaveAttn<E, D, G, TU>>::type;
+
 // ============================================================================
 // Flat schedule: a persistent grid deals equal ranges of the tile stream.
 // ============================================================================
 
 template <class E, int D, int G, class TU>
 __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParams p) {
-    using A = WaveAttn<E, D, G, TU>;
+    using A = Engine<E, D, G, TU>;
     constexpr int NS = A::NS;
     constexpr int DEPTH = TU::DEPTH;
-    extern __shared__ int32_t sh[];
+    extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
     const int S = p.num_seqs;
     const int Hkv = p.n_kv_heads;
     const int Hq = p.n_q_heads;
-    int32_t* Ls = sh;         // clamped context length per sequence
-    int32_t* pre = sh + S;    // pre[s] = tiles of sequences < s; pre[S] = all tiles
+    // [NW engine areas][Ls: clamped context length per sequence][pre: tile prefix]
+    int32_t* Ls = reinterpret_cast<int32_t*>(dyn_lds + TU::NW * A::kLdsBytes);
+    int32_t* pre = Ls + S;  // pre[s] = tiles of sequences < s; pre[S] = all tiles
 
     // Tile counts and their prefix sums (every workgroup computes them).
     const int max_len = p.max_blocks * kBlock;
@@ -326,7 +548,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     };
 
     A a;
-    a.init(lane, row_stride);
+    a.init(lane, row_stride, dyn_lds + wave_id_uniform() * A::kLdsBytes);
     int pbs[NS];
     auto issue = [&](int slot, const Cur& q) {
         int pb = __builtin_amdgcn_readfirstlane(p.block_tables[(int64_t)q.s * p.max_blocks + q.b]);
@@ -354,7 +576,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     a.reset();
 
     auto flush = [&]() {
-        a.reduce_rowgroups();
+        a.reduce();
         const int nb = (Ls[as] + kBlock - 1) / kBlock;
         const int p0 = pre[as] + akvh * nb;  // the pair's tiles are [p0, p0 + nb)
         if (p0 / per == (p0 + nb - 1) / per) {
@@ -391,6 +613,61 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     flush();
 }
 
+// Log-sum-exp combination, by one wave, of n partial records: record x has its
+// (m, l) at ml[(first + x * stride) * 2] and its acc row at acc[(first + x * stride) * D].
+// The records' (m, l) are read by all lanes at once; the weighted sum over the
+// acc rows keeps several rows' loads in flight.
+template <class E, int D>
+__device__ __forceinline__ void merge_records(const float* ml, const float* acc, int64_t first, int stride, int n,
+                                              char* out_row) {
+    constexpr int PER = (D + kWave - 1) / kWave;
+    constexpr int UNROLL = 4;
+    const int lane = threadIdx.x % kWave;
+    float M = -INFINITY;
+    for (int x = lane; x < n; x += kWave) M = fmaxf(M, ml[(first + (int64_t)x * stride) * 2]);
+    M = wave_max(M);
+    float den = 0.f;
+    for (int x = lane; x < n; x += kWave) {
+        const int64_t r = first + (int64_t)x * stride;
+        den += __builtin_amdgcn_exp2f(ml[r * 2] - M) * ml[r * 2 + 1];
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) den += shfl_xor(den, m);
+    float num[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) num[k] = 0.f;
+    for (int x0 = 0; x0 < n; x0 += kWave) {
+        // weights of records x0 .. x0+63, one per lane, then broadcast
+        const int xl = x0 + lane;
+        const float fl = xl < n ? __builtin_amdgcn_exp2f(ml[(first + (int64_t)xl * stride) * 2] - M) : 0.f;
+        const int cnt = min(kWave, n - x0);
+        for (int i = 0; i < cnt; i += UNROLL) {
+            float a[UNROLL][PER], f[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const bool ok = i + u < cnt;
+                f[u] = __shfl(fl, i + u, kWave);
+                const int64_t r = first + (int64_t)(x0 + (ok ? i + u : 0)) * stride;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) {
+                    const int d = lane + k * kWave;
+                    a[u][k] = (ok && d < D) ? acc[r * D + d] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int k = 0; k < PER; ++k) num[k] = __builtin_fmaf(f[u], a[u][k], num[k]);
+        }
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int d = lane + k * kWave;
+        if (d < D) E::store(out_row + d * E::kBytes, num[k] * inv);
+    }
+}
+
 // One wave per (sequence, query head): combine the records of pairs that were
 // split between waves, and write zeros for empty sequences.
 template <class E, int D>
@@ -419,29 +696,7 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
     const int w1 = (p0 + nb - 1) / per;
     if (w0 == w1) return;  // one wave held the whole pair and wrote it
     const int64_t base = (int64_t)s * p.n_kv_heads + kvh;  // record of wave w is base + w
-
-    float M = -INFINITY;
-    for (int x = w0 + lane; x <= w1; x += kWave) M = fmaxf(M, p.ws_ml[((base + x) * G + gi) * 2]);
-    M = wave_max(M);
-    float num[PER], den = 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) num[k] = 0.f;
-    for (int x = w0; x <= w1; ++x) {
-        const int64_t rec = (base + x) * G + gi;
-        const float f = __builtin_amdgcn_exp2f(p.ws_ml[rec * 2] - M);
-        den = __builtin_fmaf(f, p.ws_ml[rec * 2 + 1], den);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int d = lane + k * kWave;
-            if (d < D) num[k] = __builtin_fmaf(f, p.ws_acc[rec * D + d], num[k]);
-        }
-    }
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int d = lane + k * kWave;
-        if (d < D) E::store(out_row + d * E::kBytes, num[k] * inv);
-    }
+    merge_records<E, D>(p.ws_ml, p.ws_acc, (base + w0) * G + gi, G, w1 - w0 + 1, out_row);
 }
 
 // ============================================================================
@@ -450,10 +705,11 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
 
 template <class E, int D, int G, class TU>
 __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(DecodeParams p) {
-    using A = WaveAttn<E, D, G, TU>;
+    using A = Engine<E, D, G, TU>;
     constexpr int NW = TU::NW;
     constexpr int NS = A::NS;
     constexpr int DEPTH = TU::DEPTH;
+    __shared__ __attribute__((aligned(16))) char sm_eng[NW * (A::kLdsBytes > 0 ? A::kLdsBytes : 16)];
 
     const int part = blockIdx.x;
     const int kvh = blockIdx.y;
@@ -490,7 +746,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
 
     A a;
-    a.init(lane, row_stride);
+    a.init(lane, row_stride, sm_eng + w * A::kLdsBytes);
     a.load_q(static_cast<const char*>(p.q) + ((int64_t)s * Hq + h0) * A::RB);
     a.reset();
     int pbs[NS];
@@ -518,26 +774,14 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
             }
         }
     }
-    a.reduce_rowgroups();
+    a.reduce();
 
     // Combine the waves through LDS.
-    __shared__ float sm_acc[NW][G][D];
-    __shared__ float sm_m[NW][G];
-    __shared__ float sm_l[NW][G];
-    if (a.rg == 0) {
-#pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-#pragma unroll
-            for (int k = 0; k < A::CPL; ++k)
-#pragma unroll
-                for (int e = 0; e < A::VEC; ++e)
-                    sm_acc[w][gi][(a.c + k * A::R) * A::VEC + e] = a.acc[gi][k * A::VEC + e];
-            if (a.c == 0) {
-                sm_m[w][gi] = a.m[gi];
-                sm_l[w][gi] = a.l[gi];
-            }
-        }
-    }
+    __shared__ __attribute__((aligned(16))) float sm_acc[NW][G][D];
+    __shared__ float sm_ml[NW][G][2];
+    for (int i = threadIdx.x % kWave; i < G * 2; i += kWave) sm_ml[w][i / 2][i % 2] = i % 2 ? 0.f : -INFINITY;
+    __builtin_amdgcn_wave_barrier();
+    a.store_partial(&sm_acc[w][0][0], &sm_ml[w][0][0]);
     __syncthreads();
 
     const bool single = n_parts == 1;
@@ -546,13 +790,14 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
         const int d = i % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int x = 0; x < NW; ++x) M = fmaxf(M, sm_m[x][gi]);
+        for (int x = 0; x < NW; ++x) M = fmaxf(M, sm_ml[x][gi][0]);
         float num = 0.f, den = 0.f;
 #pragma unroll
         for (int x = 0; x < NW; ++x) {
-            const float f = sm_m[x][gi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_m[x][gi] - M);
-            num = __builtin_fmaf(f, sm_acc[x][gi][d], num);
-            den = __builtin_fmaf(f, sm_l[x][gi], den);
+            // a wave that held no rows keeps m = -inf (and no acc): weight 0
+            const float f = sm_ml[x][gi][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_ml[x][gi][0] - M);
+            num = f == 0.f ? num : __builtin_fmaf(f, sm_acc[x][gi][d], num);
+            den = __builtin_fmaf(f, sm_ml[x][gi][1], den);
         }
         const int64_t row = (int64_t)s * Hq + h0 + gi;
         if (single) {
@@ -579,32 +824,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
     const int n = (L + p.part_tokens - 1) / p.part_tokens;
     if (n < 2) return;
-    const int64_t base = (int64_t)pair * p.n_parts_max;
-    const float* ml = p.ws_ml + base * 2;
-    const float* acc = p.ws_acc + base * D;
-
-    float M = -INFINITY;
-    for (int j = lane; j < n; j += kWave) M = fmaxf(M, ml[2 * j]);
-    M = wave_max(M);
-
-    float num[PER], den = 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) num[k] = 0.f;
-    for (int j = 0; j < n; ++j) {
-        const float f = __builtin_amdgcn_exp2f(ml[2 * j] - M);
-        den = __builtin_fmaf(f, ml[2 * j + 1], den);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int d = lane + k * kWave;
-            if (d < D) num[k] = __builtin_fmaf(f, acc[(int64_t)j * D + d], num[k]);
-        }
-    }
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int d = lane + k * kWave;
-        if (d < D) E::store(static_cast<char*>(p.out) + ((int64_t)pair * D + d) * E::kBytes, num[k] * inv);
-    }
+    merge_records<E, D>(p.ws_ml, p.ws_acc, (int64_t)pair * p.n_parts_max, 1, n,
+                        static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes);
 }
 
 // ============================================================================
@@ -614,7 +835,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 // Launch shape per element type, head_dim and group size.
 template <class E, int D, int G>
 struct DefaultTune {
-    using type = Tune<4, 8, 1, true>;
+    static constexpr bool kMfma = E::kBytes == 2 && G >= 4;
+    using type = Tune<4, 8, 1, true, kMfma>;
 };
 
 template <class E, int D, int G, class TU>
@@ -629,7 +851,7 @@ hipError_t launch_parts_tuned(const DecodeParams& p, hipStream_t stream) {
 template <class E, int D, int G, class TU>
 hipError_t launch_flat_tuned(const DecodeParams& p, hipStream_t stream) {
     auto kern = decode_flat_kernel<E, D, G, TU>;
-    const size_t lds = (size_t)(2 * p.num_seqs + 1) * sizeof(int32_t);
+    const size_t lds = (size_t)TU::NW * Engine<E, D, G, TU>::kLdsBytes + (size_t)(2 * p.num_seqs + 1) * sizeof(int32_t);
     static thread_local int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
     static thread_local size_t cached_lds = 0;
     int dev = 0;
