@@ -54,31 +54,39 @@ namespace pkv {
 
 // Launch shape: NW waves per workgroup, R lanes per K/V row, DEPTH tiles in
 // flight ahead of the one being computed, streaming (nontemporal) loads.
-template <int NW_, int R_, int DEPTH_, bool STREAM_, bool MFMA_ = false>
+template <int NW_, int R_, int DEPTH_, bool STREAM_, bool MFMA_ = false, int NH_ = 1>
 struct Tune {
     static constexpr int NW = NW_;
     static constexpr int R = R_;
     static constexpr int DEPTH = DEPTH_;
     static constexpr bool STREAM = STREAM_;
     static constexpr bool MFMA = MFMA_;  // matrix-core engine (16-bit caches, G >= 4)
+    static constexpr int NH = NH_;       // adjacent KV heads per wave (VALU engine)
 };
 
-// One wave's share of the attention for the G query heads of one KV head.
+// One wave's share of the attention for NH adjacent KV heads (a head group)
+// and the G query heads of each.  The NH head rows of one token are adjacent
+// in the cache, so one load instruction reads RPS tokens x NH * RB contiguous
+// bytes; lane l serves head hd = (l mod NH*R) / R only, so the per-lane state
+// does not grow with NH.
 template <class E, int D, int G, class TU>
 struct WaveAttn {
+    static constexpr int NH = TU::NH;         // KV heads per wave
+    static constexpr int HG = NH * G;         // query heads per wave
     static constexpr int VEC = E::kPerVec;    // elements per 16-byte vector
     static constexpr int RB = D * E::kBytes;  // bytes per (token, head) row
     static constexpr int CH = RB / 16;        // 16-byte chunks per row
-    static constexpr int R = TU::R;           // lanes sharing one row
+    static constexpr int R = TU::R;           // lanes sharing one head row
+    static constexpr int HR = NH * R;         // lanes sharing one token's head-group row
     static constexpr int CPL = CH / R;        // chunks per lane per row
-    static constexpr int RPS = kWave / R;     // rows covered by one load instruction
+    static constexpr int RPS = kWave / HR;    // tokens covered by one load instruction
     static constexpr int J = kBlock / RPS;    // rows per lane per tile
     static constexpr int EPL = CPL * VEC;     // elements per lane per row
     static constexpr int NS = TU::DEPTH + 1;  // register tile slots
     static constexpr int kLdsBytes = 0;       // per wave
-    static_assert(CH % R == 0 && kBlock % RPS == 0 && J >= 1, "row / lane mapping");
+    static_assert(CH % R == 0 && kWave % HR == 0 && kBlock % RPS == 0 && J >= 1 && R <= 16, "lane mapping");
 
-    int rg, c;  // row group and chunk column of this lane
+    int rg, c, hd;  // row group, chunk column and head (within the group) of this lane
     uint32_t lane_off[J][CPL];
     Vec16 qv[G][CPL];
     float acc[G][EPL];
@@ -86,20 +94,23 @@ struct WaveAttn {
     Vec16 kb[NS][J][CPL], vb[NS][J][CPL];
 
     __device__ __forceinline__ void init(int lane, uint32_t row_stride, char*) {
-        rg = lane / R;
+        rg = lane / HR;
+        hd = (lane % HR) / R;
         c = lane % R;
 #pragma unroll
         for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int k = 0; k < CPL; ++k) lane_off[j][k] = (j * RPS + rg) * row_stride + (c + k * R) * 16;
+            for (int k = 0; k < CPL; ++k)
+                lane_off[j][k] = (j * RPS + rg) * row_stride + hd * RB + (c + k * R) * 16;
     }
 
-    // q rows of the G heads (contiguous [G][D]), this lane's chunks only.
+    // q rows of the group's HG query heads (contiguous [HG][D]); this lane
+    // loads its own head's G rows, its chunks only.
     __device__ __forceinline__ void load_q(const char* q_rows) {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-            for (int k = 0; k < CPL; ++k) qv[gi][k] = load16(q_rows + gi * RB + (c + k * R) * 16);
+            for (int k = 0; k < CPL; ++k) qv[gi][k] = load16(q_rows + (hd * G + gi) * RB + (c + k * R) * 16);
     }
 
     __device__ __forceinline__ void reset() {
@@ -136,21 +147,14 @@ struct WaveAttn {
                 for (int k = 0; k < CPL; ++k) d = E::dot(qv[gi][k], kb[slot][j][k], d);
                 sc[gi][j] = group_sum<R>(d) * scale_log2;
             }
-        float vf[J][EPL];
+        const bool masked = valid < kBlock;  // wave-uniform: the last tile, or a skipped one
+        if (masked) {
 #pragma unroll
-        for (int j = 0; j < J; ++j)
+            for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int k = 0; k < CPL; ++k) E::expand(vb[slot][j][k], &vf[j][k * VEC]);
-        if (valid < kBlock) {
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const bool ok = j * RPS + rg < valid;
-#pragma unroll
-                for (int gi = 0; gi < G; ++gi) sc[gi][j] = ok ? sc[gi][j] : -INFINITY;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) vf[j][e] = ok ? vf[j][e] : 0.f;
-            }
+                for (int gi = 0; gi < G; ++gi) sc[gi][j] = j * RPS + rg < valid ? sc[gi][j] : -INFINITY;
         }
+        float pj[G][J];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             float mx = sc[gi][0];
@@ -167,31 +171,47 @@ struct WaveAttn {
             }
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const float pj = __builtin_amdgcn_exp2f(sc[gi][j] - ms);
-                l[gi] += pj;
+                pj[gi][j] = __builtin_amdgcn_exp2f(sc[gi][j] - ms);
+                l[gi] += pj[gi][j];
+            }
+        }
+        // P.V, one row at a time: a row past `valid` contributes nothing, even
+        // when its slot holds NaN (select, not multiply).
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[gi][e] = __builtin_fmaf(pj, vf[j][e], acc[gi][e]);
+        for (int j = 0; j < J; ++j) {
+            const bool ok = !masked || j * RPS + rg < valid;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                float vf[VEC];
+                E::expand(vb[slot][j][k], vf);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float v = ok ? vf[e] : 0.f;
+#pragma unroll
+                    for (int gi = 0; gi < G; ++gi)
+                        acc[gi][k * VEC + e] = __builtin_fmaf(pj[gi][j], v, acc[gi][k * VEC + e]);
+                }
             }
         }
     }
 
-    // Combine the row groups (lanes c, c+R, c+2R, ...): afterwards every lane
-    // holds the wave's m, l and acc for its chunk column.
+    // Combine the row groups (lanes l, l+HR, l+2HR, ...): afterwards every
+    // lane holds the wave's m, l and acc for its head and chunk column.
     __device__ __forceinline__ void reduce() {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             float M = m[gi];
 #pragma unroll
-            for (int x = R; x < kWave; x <<= 1) M = fmaxf(M, shfl_xor(M, x));
+            for (int x = HR; x < kWave; x <<= 1) M = fmaxf(M, shfl_xor(M, x));
             const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[gi] - M);
             float lsum = l[gi] * f;
 #pragma unroll
-            for (int x = R; x < kWave; x <<= 1) lsum += shfl_xor(lsum, x);
+            for (int x = HR; x < kWave; x <<= 1) lsum += shfl_xor(lsum, x);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 float a = acc[gi][e] * f;
 #pragma unroll
-                for (int x = R; x < kWave; x <<= 1) a += shfl_xor(a, x);
+                for (int x = HR; x < kWave; x <<= 1) a += shfl_xor(a, x);
                 acc[gi][e] = a;
             }
             m[gi] = M;
@@ -199,36 +219,38 @@ struct WaveAttn {
         }
     }
 
-    // After reduce, row group 0 writes the normalised rows of the G
-    // heads ([G][D] at out_rows) ...
+    // After reduce, row group 0 writes the normalised rows of the HG query
+    // heads ([HG][D] at out_rows) ...
     __device__ __forceinline__ void store_out(char* out_rows) const {
         if (rg != 0) return;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             const float inv = 1.f / l[gi];
+            const int row = hd * G + gi;
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    E::store(out_rows + (gi * D + (c + k * R) * VEC + e) * E::kBytes, acc[gi][k * VEC + e] * inv);
+                    E::store(out_rows + (row * D + (c + k * R) * VEC + e) * E::kBytes, acc[gi][k * VEC + e] * inv);
         }
     }
 
-    // ... or the partial record: acc [G][D] fp32 and (m, l) [G][2] fp32.
+    // ... or the partial record: acc [HG][D] fp32 and (m, l) [HG][2] fp32.
     __device__ __forceinline__ void store_partial(float* rec_acc, float* rec_ml) const {
         if (rg != 0) return;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
+            const int row = hd * G + gi;
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4)
-                    *reinterpret_cast<float4*>(rec_acc + gi * D + (c + k * R) * VEC + e) =
+                    *reinterpret_cast<float4*>(rec_acc + row * D + (c + k * R) * VEC + e) =
                         make_float4(acc[gi][k * VEC + e], acc[gi][k * VEC + e + 1], acc[gi][k * VEC + e + 2],
                                     acc[gi][k * VEC + e + 3]);
             if (c == 0) {
-                rec_ml[gi * 2] = m[gi];
-                rec_ml[gi * 2 + 1] = l[gi];
+                rec_ml[row * 2] = m[gi];
+                rec_ml[row * 2 + 1] = l[gi];
             }
         }
     }
@@ -306,6 +328,8 @@ struct MfmaAttn {
     static_assert(E::kBytes == 2 && G <= 16 && D % 32 == 0, "16-bit caches, up to 16 heads per KV head");
     using OPS = MfmaOps<E>;
     using op4_t = typename OPS::op4_t;
+    static constexpr int NH = 1;                 // one KV head per wave
+    static constexpr int HG = G;
     static constexpr int RB = D * 2;             // bytes per row
     static constexpr int CH = RB / 16;           // 16-byte chunks per row
     static constexpr int KK = D / 32;            // QK products
@@ -463,6 +487,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
     const int S = p.num_seqs;
     const int Hkv = p.n_kv_heads;
+    const int NG = Hkv / A::NH;  // head groups: the tile stream's middle index
     const int Hq = p.n_q_heads;
     // [NW engine areas][Ls: clamped context length per sequence][pre: tile prefix]
     int32_t* Ls = reinterpret_cast<int32_t*>(dyn_lds + TU::NW * A::kLdsBytes);
@@ -477,7 +502,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         int carry = 0;
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;
-            int v = i < S ? ((Ls[i] + kBlock - 1) / kBlock) * Hkv : 0;
+            int v = i < S ? ((Ls[i] + kBlock - 1) / kBlock) * NG : 0;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 const int y = __shfl_up(v, off, kWave);
@@ -511,9 +536,9 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     const char* kcache = static_cast<const char*>(p.k_cache);
     const char* vcache = static_cast<const char*>(p.v_cache);
 
-    // Cursor over the tile stream: sequence, KV head, block, blocks of the sequence.
+    // Cursor over the tile stream: sequence, head group, block, blocks of the sequence.
     struct Cur {
-        int s, kvh, b, nb;
+        int s, kvh, b, nb;  // kvh: the head group
     };
     auto locate = [&](int t) {
         int lo = 0, hi = S;  // largest s with pre[s] <= t (then t < pre[s + 1])
@@ -533,7 +558,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     auto advance = [&](Cur& q) {
         if (++q.b == q.nb) {
             q.b = 0;
-            if (++q.kvh == Hkv) {
+            if (++q.kvh == NG) {
                 q.kvh = 0;
                 do {
                     ++q.s;
@@ -554,7 +579,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         int pb = __builtin_amdgcn_readfirstlane(p.block_tables[(int64_t)q.s * p.max_blocks + q.b]);
         if (pb < 0 || pb >= p.num_blocks) pb = -1;
         const int64_t boff = pb < 0 ? 0 : (int64_t)pb * blk_bytes;
-        a.issue(slot, kcache + (int64_t)q.kvh * A::RB, vcache + (int64_t)q.kvh * A::RB, boff);
+        a.issue(slot, kcache + (int64_t)q.kvh * A::NH * A::RB, vcache + (int64_t)q.kvh * A::NH * A::RB, boff);
         pbs[slot] = pb;
     };
 
@@ -572,7 +597,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         }
 
     int as = cur.s, akvh = cur.kvh;  // the segment being accumulated
-    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * G) * A::RB);
+    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
     a.reset();
 
     auto flush = [&]() {
@@ -580,10 +605,10 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         const int nb = (Ls[as] + kBlock - 1) / kBlock;
         const int p0 = pre[as] + akvh * nb;  // the pair's tiles are [p0, p0 + nb)
         if (p0 / per == (p0 + nb - 1) / per) {
-            a.store_out(static_cast<char*>(p.out) + ((int64_t)as * Hq + akvh * G) * D * E::kBytes);
+            a.store_out(static_cast<char*>(p.out) + ((int64_t)as * Hq + akvh * A::HG) * D * E::kBytes);
         } else {
-            const int64_t rec = (int64_t)as * Hkv + akvh + w;
-            a.store_partial(p.ws_acc + rec * G * D, p.ws_ml + rec * G * 2);
+            const int64_t rec = (int64_t)as * NG + akvh + w;
+            a.store_partial(p.ws_acc + rec * A::HG * D, p.ws_ml + rec * A::HG * 2);
         }
     };
 
@@ -600,7 +625,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
                     flush();
                     as = cur.s;
                     akvh = cur.kvh;
-                    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * G) * A::RB);
+                    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
                     a.reset();
                 }
                 const int pb = pbs[u];
@@ -678,9 +703,10 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
     if (pair >= p.num_seqs * p.n_q_heads) return;
     const int s = pair / p.n_q_heads;
     const int h = pair % p.n_q_heads;
-    const int G = p.n_q_heads / p.n_kv_heads;
-    const int kvh = h / G;
-    const int gi = h % G;
+    const int HG = p.n_q_heads / p.n_kv_heads * p.heads_per_wave;  // query heads per record
+    const int NG = p.n_kv_heads / p.heads_per_wave;
+    const int hg = h / HG;
+    const int gi = h % HG;
     char* out_row = static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes;
     const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
     if (L == 0) {
@@ -691,12 +717,12 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
     }
     const int per = p.ws_hdr[0];
     const int nb = (L + kBlock - 1) / kBlock;
-    const int p0 = p.ws_hdr[2 + s] + kvh * nb;
+    const int p0 = p.ws_hdr[2 + s] + hg * nb;
     const int w0 = p0 / per;
     const int w1 = (p0 + nb - 1) / per;
     if (w0 == w1) return;  // one wave held the whole pair and wrote it
-    const int64_t base = (int64_t)s * p.n_kv_heads + kvh;  // record of wave w is base + w
-    merge_records<E, D>(p.ws_ml, p.ws_acc, (base + w0) * G + gi, G, w1 - w0 + 1, out_row);
+    const int64_t base = (int64_t)s * NG + hg;  // record of wave w is base + w
+    merge_records<E, D>(p.ws_ml, p.ws_acc, (base + w0) * HG + gi, HG, w1 - w0 + 1, out_row);
 }
 
 // ============================================================================
@@ -711,11 +737,12 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     constexpr int DEPTH = TU::DEPTH;
     __shared__ __attribute__((aligned(16))) char sm_eng[NW * (A::kLdsBytes > 0 ? A::kLdsBytes : 16)];
 
+    constexpr int HG = A::HG;
     const int part = blockIdx.x;
-    const int kvh = blockIdx.y;
+    const int kvh = blockIdx.y * A::NH;  // first KV head of the group
     const int s = blockIdx.z;
     const int Hq = p.n_q_heads;
-    const int h0 = kvh * G;
+    const int h0 = blockIdx.y * HG;
     // A length beyond the table is a caller error; clamping keeps every table
     // read inside the row and every partition inside the workspace.
     const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
@@ -724,7 +751,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
 
     if (part >= n_parts) {
         if (L == 0 && part == 0) {  // nothing to attend: a zero row
-            for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+            for (int i = threadIdx.x; i < HG * D; i += blockDim.x)
                 E::store(static_cast<char*>(p.out) + (((int64_t)s * Hq + h0 + i / D) * D + i % D) * E::kBytes,
                          0.f);
         }
@@ -777,15 +804,15 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     a.reduce();
 
     // Combine the waves through LDS.
-    __shared__ __attribute__((aligned(16))) float sm_acc[NW][G][D];
-    __shared__ float sm_ml[NW][G][2];
-    for (int i = threadIdx.x % kWave; i < G * 2; i += kWave) sm_ml[w][i / 2][i % 2] = i % 2 ? 0.f : -INFINITY;
+    __shared__ __attribute__((aligned(16))) float sm_acc[NW][HG][D];
+    __shared__ float sm_ml[NW][HG][2];
+    for (int i = threadIdx.x % kWave; i < HG * 2; i += kWave) sm_ml[w][i / 2][i % 2] = i % 2 ? 0.f : -INFINITY;
     __builtin_amdgcn_wave_barrier();
     a.store_partial(&sm_acc[w][0][0], &sm_ml[w][0][0]);
     __syncthreads();
 
     const bool single = n_parts == 1;
-    for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+    for (int i = threadIdx.x; i < HG * D; i += NW * kWave) {
         const int gi = i / D;
         const int d = i % D;
         float M = -INFINITY;
@@ -832,24 +859,42 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 // Dispatch
 // ============================================================================
 
-// Launch shape per element type, head_dim and group size.
+// Launch shape per element type, head_dim and group size: the matrix-core
+// engine for 16-bit caches with G >= 4; otherwise the vector engine streaming
+// two adjacent KV heads per wave (16 lanes per head row, so one load
+// instruction reads two tokens x 512 contiguous bytes at D = 128, 16-bit).
+// NH1 is the one-head shape used when the KV head count is odd.
 template <class E, int D, int G>
 struct DefaultTune {
     static constexpr bool kMfma = E::kBytes == 2 && G >= 4;
-    using type = Tune<4, 8, 1, true, kMfma>;
+    static constexpr int kCH = D * E::kBytes / 16;
+    static constexpr int kR = kCH < 16 ? kCH : 16;
+    static constexpr int kNH = (E::kBytes == 2 && !kMfma) ? 2 : 1;
+    using type = Tune<4, kNH == 2 ? kR : 8, 1, true, kMfma, kNH>;
+    using NH1 = Tune<4, 8, 1, true, kMfma, 1>;
 };
+
+template <class E, int D, int G>
+static int heads_per_wave_t(int n_kv_heads) {
+    constexpr int nh = DefaultTune<E, D, G>::type::NH;
+    return n_kv_heads % nh == 0 ? nh : 1;
+}
 
 template <class E, int D, int G, class TU>
 hipError_t launch_parts_tuned(const DecodeParams& p, hipStream_t stream) {
-    const dim3 grid(p.n_parts_max, p.n_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU>), grid, dim3(TU::NW * kWave), 0, stream, p);
+    DecodeParams q = p;
+    q.heads_per_wave = TU::NH;
+    const dim3 grid(q.n_parts_max, q.n_kv_heads / TU::NH, q.num_seqs);
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU>), grid, dim3(TU::NW * kWave), 0, stream, q);
     return hipGetLastError();
 }
 
 // Workgroups of the flat kernel resident on the whole device, capped so the
 // grid's waves never exceed kMaxFlatWorkers.
 template <class E, int D, int G, class TU>
-hipError_t launch_flat_tuned(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_flat_tuned(const DecodeParams& pin, hipStream_t stream) {
+    DecodeParams p = pin;
+    p.heads_per_wave = TU::NH;
     auto kern = decode_flat_kernel<E, D, G, TU>;
     const size_t lds = (size_t)TU::NW * Engine<E, D, G, TU>::kLdsBytes + (size_t)(2 * p.num_seqs + 1) * sizeof(int32_t);
     static thread_local int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
@@ -877,7 +922,10 @@ hipError_t launch_flat_tuned(const DecodeParams& p, hipStream_t stream) {
 template <class E, int D, int G>
 static hipError_t launch_g(const DecodeParams& p, bool flat, hipStream_t stream) {
     using TU = typename DefaultTune<E, D, G>::type;
-    return flat ? launch_flat_tuned<E, D, G, TU>(p, stream) : launch_parts_tuned<E, D, G, TU>(p, stream);
+    using TU1 = typename DefaultTune<E, D, G>::NH1;
+    if (heads_per_wave_t<E, D, G>(p.n_kv_heads) == TU::NH)
+        return flat ? launch_flat_tuned<E, D, G, TU>(p, stream) : launch_parts_tuned<E, D, G, TU>(p, stream);
+    return flat ? launch_flat_tuned<E, D, G, TU1>(p, stream) : launch_parts_tuned<E, D, G, TU1>(p, stream);
 }
 
 template <class E, int D>
@@ -900,6 +948,32 @@ static hipError_t launch_e(const DecodeParams& p, int head_dim, int group, bool 
     }
 }
 
+template <class E, int D>
+static int heads_per_wave_d(int group, int n_kv_heads) {
+    switch (group) {
+        case 1: return heads_per_wave_t<E, D, 1>(n_kv_heads);
+        case 2: return heads_per_wave_t<E, D, 2>(n_kv_heads);
+        case 4: return heads_per_wave_t<E, D, 4>(n_kv_heads);
+        case 8: return heads_per_wave_t<E, D, 8>(n_kv_heads);
+        default: return 1;
+    }
+}
+
+template <class E>
+static int heads_per_wave_e(int head_dim, int group, int n_kv_heads) {
+    return head_dim == 64 ? heads_per_wave_d<E, 64>(group, n_kv_heads)
+                          : heads_per_wave_d<E, 128>(group, n_kv_heads);
+}
+
+int decode_heads_per_wave(int dtype, int head_dim, int group, int n_kv_heads) {
+    switch (dtype) {
+        case 0: return heads_per_wave_e<F32>(head_dim, group, n_kv_heads);
+        case 1: return heads_per_wave_e<F16>(head_dim, group, n_kv_heads);
+        case 2: return heads_per_wave_e<BF16>(head_dim, group, n_kv_heads);
+        default: return 1;
+    }
+}
+
 bool decode_supported(int dtype, int head_dim, int group) {
     return dtype >= 0 && dtype <= 2 && (head_dim == 64 || head_dim == 128) &&
            (group == 1 || group == 2 || group == 4 || group == 8);
@@ -917,7 +991,9 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_d
 }
 
 template <class E>
-static hipError_t launch_merge_e(const DecodeParams& p, int head_dim, hipStream_t stream) {
+static hipError_t launch_merge_e(const DecodeParams& pin, int head_dim, int group, hipStream_t stream) {
+    DecodeParams p = pin;
+    p.heads_per_wave = heads_per_wave_e<E>(head_dim, group, p.n_kv_heads);
     const int pairs = p.num_seqs * p.n_q_heads;
     const dim3 grid((pairs + 3) / 4);
     const bool flat = p.part_tokens == 0;
@@ -935,11 +1011,11 @@ static hipError_t launch_merge_e(const DecodeParams& p, int head_dim, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream) {
+hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, int group, hipStream_t stream) {
     switch (dtype) {
-        case 0: return launch_merge_e<F32>(p, head_dim, stream);
-        case 1: return launch_merge_e<F16>(p, head_dim, stream);
-        case 2: return launch_merge_e<BF16>(p, head_dim, stream);
+        case 0: return launch_merge_e<F32>(p, head_dim, group, stream);
+        case 1: return launch_merge_e<F16>(p, head_dim, group, stream);
+        case 2: return launch_merge_e<BF16>(p, head_dim, group, stream);
         default: return hipErrorInvalidValue;
     }
 }

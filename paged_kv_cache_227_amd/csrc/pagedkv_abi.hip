@@ -100,8 +100,10 @@ Plan make_plan(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks, const pk
     Plan pl{};
     pl.part_tokens = P;
     if (P == 0) {
+        // records of NH * G query heads, (num_seqs * Hkv / NH + waves) of them: at
+        // most (num_seqs * Hkv + waves * kMaxHeadsPerWave) * G head rows
         const size_t G = (size_t)n_q_heads / L->n_kv_heads;
-        const size_t recs = (size_t)num_seqs * L->n_kv_heads + pkv::kMaxFlatWorkers;
+        const size_t recs = (size_t)num_seqs * L->n_kv_heads + (size_t)pkv::kMaxFlatWorkers * pkv::kMaxHeadsPerWave;
         pl.n_parts_max = 1;
         pl.hdr_bytes = round_up((size_t)(num_seqs + 3) * sizeof(int32_t));
         pl.acc_bytes = round_up(recs * G * L->head_dim * sizeof(float));
@@ -319,7 +321,8 @@ pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_pe
     const pkv::DecodeParams p = make_params(nullptr, nullptr, nullptr, layout, nullptr, max_blocks_per_seq,
                                             context_lens, num_seqs, n_q_heads, 1.f, out, pl,
                                             const_cast<void*>(workspace));
-    hipError_t e = pkv::launch_decode_merge(p, layout->dtype, layout->head_dim, static_cast<hipStream_t>(stream));
+    hipError_t e = pkv::launch_decode_merge(p, layout->dtype, layout->head_dim, n_q_heads / layout->n_kv_heads,
+                                            static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return ok();
 }

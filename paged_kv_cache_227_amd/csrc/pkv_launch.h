@@ -27,6 +27,8 @@ constexpr int kMaxFlatWorkers = 8192;
 // Largest batch the flat schedule serves (its per-workgroup LDS holds two
 // int32 per sequence); larger batches use fixed partitions.
 constexpr int kMaxFlatSeqs = 8000;
+// Most adjacent KV heads one wave streams together; the workspace is sized for it.
+constexpr int kMaxHeadsPerWave = 2;
 
 struct DecodeParams {
     const void* q;
@@ -50,6 +52,7 @@ struct DecodeParams {
     int32_t part_tokens;  // 0 selects the flat schedule
     int32_t n_parts_max;
     int32_t min_tiles_per_worker;
+    int32_t heads_per_wave;  // adjacent KV heads one wave streams together (see decode_heads_per_wave)
     float scale_log2;  // scale * log2(e): scores are kept in base-2 units
 };
 
@@ -57,8 +60,10 @@ struct DecodeParams {
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int group,
                                     hipStream_t stream);
-hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, int group, hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int group);
+// KV heads per wave the decode kernels use for this shape (1 or 2).
+int decode_heads_per_wave(int dtype, int head_dim, int group, int n_kv_heads);
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);

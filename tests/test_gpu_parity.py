@@ -180,3 +180,12 @@ def test_flat_equals_partitions_within_tolerance():
     a = _full_check(w)                  # flat schedule
     b = _full_check(w, part_tokens=512)  # fixed partitions
     assert float((a.float() - b.float()).abs().max()) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,group", [("f16", 1), ("bf16", 2), ("bf16", 4)])
+def test_odd_kv_head_count(dtype, group):
+    # three KV heads: the two-heads-per-wave shape does not divide them
+    lens = [1, 40, 777, 16]
+    w = W.small(len(lens), lens, 3 * group, 3, 128, dtype, seed=85)
+    _full_check(w)
+    _full_check(w, part_tokens=256)
