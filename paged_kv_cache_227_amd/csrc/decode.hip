@@ -257,17 +257,21 @@ struct WaveAttn {
 };
 
 // ----------------------------------------------------------------------------
-// Matrix-core engine for 16-bit caches and G >= 4: per tile,
-//   S^T[16 tok][16 heads]  = K[16][D] . Q^T[D][16]          (D/32 MFMA 16x16x32)
-//   O^T[D][16 heads]      += V^T[D][16 tok] . P^T[16][16]     (D/16 x 2 MFMA 16x16x16)
-// with the G query heads in columns 0..G-1 (the others are zero padding).
-// Lane l = 16 g + j holds S^T rows 4g..4g+3 of column j, which is exactly the
-// B operand P^T of the second product, so the softmax state of head j lives in
-// lane column j and never moves between lanes.  K is loaded straight into the
-// A-operand layout (lane: row j, 16-byte chunk 4kk + g); V goes through LDS
-// (rows written with 16-byte stores, 32-byte chunks swizzled by row) and comes
-// back transposed with ds_read_b64_tr_b16.  P is rounded to the 16-bit type as
-// a sum hi + lo of two 16-bit values, so the product keeps ~16 bits of P.
+// Matrix-core engine for 16-bit caches and G >= 4.  Per tile of NH adjacent KV
+// heads (16 tokens), with the wave's HG = NH * G query heads in columns
+// 0..HG-1 of 16 (the rest zero padding):
+//   S^T[16 tok][16]  = sum_h K_h[16][D] . Q_h^T[D][16]      (NH * D/32 MFMA 16x16x32)
+//   O^T[D][16]      += sum_h V_h^T[D][16 tok] . P_h^T[16][16] (NH * D/16 x 2 MFMA 16x16x16)
+// Q_h^T holds only head h's columns, so both heads accumulate into one S^T
+// and P_h^T keeps only head h's columns of P^T.  Lane l = 16 g + j holds S^T
+// rows 4g..4g+3 of column j, which is exactly the B operand P^T, so the
+// softmax state of query head j lives in lane column j and never moves.
+// K and V are loaded with the wide coalesced pattern (each token's NH head
+// rows, NH * D * 2 contiguous bytes, by NH * D / 8 lanes), written once to a
+// per-wave LDS tile with the 16-byte chunks XOR-swizzled by row, and read back
+// as MFMA operands: K with 16-byte reads (lane: row j, chunk 4kk + g), V
+// transposed with ds_read_b64_tr_b16.  P is rounded to the 16-bit type as a
+// sum hi + lo of two 16-bit values, so the product keeps ~16 bits of P.
 // ----------------------------------------------------------------------------
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -325,57 +329,70 @@ struct MfmaOps<F16> {
 
 template <class E, int D, int G, class TU>
 struct MfmaAttn {
-    static_assert(E::kBytes == 2 && G <= 16 && D % 32 == 0, "16-bit caches, up to 16 heads per KV head");
+    static constexpr int NH = TU::NH;            // adjacent KV heads per wave
+    static constexpr int HG = NH * G;            // query heads per wave (S^T columns used)
+    static_assert(E::kBytes == 2 && HG <= 16 && D % 32 == 0, "16-bit caches, up to 16 query heads per wave");
     using OPS = MfmaOps<E>;
     using op4_t = typename OPS::op4_t;
-    static constexpr int NH = 1;                 // one KV head per wave
-    static constexpr int HG = G;
-    static constexpr int RB = D * 2;             // bytes per row
-    static constexpr int CH = RB / 16;           // 16-byte chunks per row
-    static constexpr int KK = D / 32;            // QK products
+    static constexpr int RB = D * 2;             // bytes per head row
+    static constexpr int CH = RB / 16;           // 16-byte chunks per head row
+    static constexpr int ROW = NH * RB;          // bytes of one token's NH head rows
+    static constexpr int LPR = NH * CH;          // lanes per token row in a load
+    static constexpr int RPI = kWave / LPR;      // token rows per load instruction
+    static constexpr int NI = kBlock / RPI;      // load instructions per tile (each of K, V)
+    static constexpr int KK = D / 32;            // QK products per head
     static constexpr int TT = D / 16;            // PV output tiles
-    static constexpr int RPI = kWave / CH;       // V rows per load instruction
-    static constexpr int VI = kBlock / RPI;      // V load instructions per tile
-    static constexpr int NT32 = RB / 32;         // 32-byte chunks per row (swizzle modulus)
     static constexpr int NS = TU::DEPTH + 1;     // register tile slots
-    static constexpr int kBufBytes = kBlock * RB;
-    static constexpr int kLdsBytes = 2 * kBufBytes;  // per wave: two V staging buffers
+    static constexpr int kTileBytes = kBlock * ROW;
+    static constexpr int kLdsBytes = 2 * kTileBytes;  // per wave: the K and V of one tile
+    static_assert(kWave % LPR == 0 && kBlock % RPI == 0 && CH == 4 * KK, "lane mapping");
 
-    int g, j;
+    int g, j;          // MFMA lane coordinates
+    int lrow, lhead, lchunk;  // this lane's token row (in a load), head and chunk
     char* lds;
-    uint32_t k_off[KK], v_off[VI], v_lds[VI], tr_lds[TT];
-    Vec16 qb[KK];
+    uint32_t ld_base;  // this lane's byte offset in a tile (first load instruction)
+    Vec16 qb[NH][KK];
     f32x4_t acc[TT];
     float m, l;
-    Vec16 kt[NS][KK], vt[NS][VI];
+    Vec16 kt[NS][NI], vt[NS][NI];
 
-    __device__ __forceinline__ static uint32_t swz(int row, int chunk32) {
-        return (uint32_t)(row * RB + ((chunk32 ^ (row % NT32)) * 32));
+    __device__ __forceinline__ static uint32_t lds_pos(int row, int head, int chunk) {
+        return (uint32_t)(row * ROW + head * RB + ((chunk ^ (row % CH)) * 16));
+    }
+    __device__ __forceinline__ static void lds_store16(char* base, uint32_t off, const Vec16& v) {
+        typedef __attribute__((address_space(3))) v4u32_t lds_v4;
+        typedef __attribute__((address_space(3))) char lds_c;
+        *(lds_v4*)((lds_c*)base + off) = v4u32_t{v.w[0], v.w[1], v.w[2], v.w[3]};
+    }
+    __device__ __forceinline__ static Vec16 lds_load16(const char* base, uint32_t off) {
+        typedef const __attribute__((address_space(3))) v4u32_t lds_v4;
+        typedef const __attribute__((address_space(3))) char lds_c;
+        const v4u32_t u = *(lds_v4*)((lds_c*)base + off);
+        return Vec16{{u.x, u.y, u.z, u.w}};
     }
 
     __device__ __forceinline__ void init(int lane, uint32_t row_stride, char* lds_wave) {
         g = lane / 16;
         j = lane % 16;
+        lrow = lane / LPR;
+        lhead = (lane % LPR) / CH;
+        lchunk = lane % CH;
         lds = lds_wave;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) k_off[kk] = j * row_stride + (4 * kk + g) * 16;
-#pragma unroll
-        for (int i = 0; i < VI; ++i) {
-            const int row = i * RPI + lane / CH;
-            const int c16 = lane % CH;
-            v_off[i] = row * row_stride + c16 * 16;
-            v_lds[i] = swz(row, c16 / 2) + (c16 % 2) * 16;
-        }
-#pragma unroll
-        for (int t = 0; t < TT; ++t) tr_lds[t] = swz(4 * g + j / 4, t) + 8 * (j % 4);
+        ld_base = lrow * row_stride + lhead * RB + lchunk * 16;
+        row_stride_ = row_stride;
     }
+    uint32_t row_stride_;
 
+    // q rows of the wave's HG query heads (contiguous [HG][D]): column j takes
+    // row j, in the B operand of head j / G only.
     __device__ __forceinline__ void load_q(const char* q_rows) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            Vec16 z = {{0u, 0u, 0u, 0u}};
-            qb[kk] = j < G ? load16(q_rows + j * RB + (4 * kk + g) * 16) : z;
-        }
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const Vec16 z = {{0u, 0u, 0u, 0u}};
+                qb[h][kk] = (j >= h * G && j < (h + 1) * G) ? load16(q_rows + j * RB + (4 * kk + g) * 16) : z;
+            }
     }
 
     __device__ __forceinline__ void reset() {
@@ -387,24 +404,37 @@ struct MfmaAttn {
 
     __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t boff) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kt[slot][kk] = load16_policy<TU::STREAM>(kbase + boff + k_off[kk]);
-#pragma unroll
-        for (int i = 0; i < VI; ++i) vt[slot][i] = load16_policy<TU::STREAM>(vbase + boff + v_off[i]);
+        for (int i = 0; i < NI; ++i) {
+            const int64_t off = boff + ld_base + (int64_t)i * RPI * row_stride_;
+            kt[slot][i] = load16_policy<TU::STREAM>(kbase + off);
+            vt[slot][i] = load16_policy<TU::STREAM>(vbase + off);
+        }
     }
 
     __device__ __forceinline__ void process(int slot, int valid, float scale_log2) {
-        char* buf = lds + (slot & 1) * kBufBytes;
-        const int lane = g * 16 + j;
-        // V rows into LDS; rows past `valid` are written as zeros.
+        char* kl = lds;
+        char* vl = lds + kTileBytes;
+        // K and V rows into LDS; V rows past `valid` are written as zeros.
 #pragma unroll
-        for (int i = 0; i < VI; ++i) {
+        for (int i = 0; i < NI; ++i) {
+            const int row = i * RPI + lrow;
+            const uint32_t pos = lds_pos(row, lhead, lchunk);
+            lds_store16(kl, pos, kt[slot][i]);
             Vec16 v = vt[slot][i];
-            if (valid < kBlock && i * RPI + lane / CH >= valid) v = Vec16{{0u, 0u, 0u, 0u}};
-            store16(buf + v_lds[i], v);
+            if (valid < kBlock && row >= valid) v = Vec16{{0u, 0u, 0u, 0u}};
+            lds_store16(vl, pos, v);
         }
+        // the rows this wave just stored are read back by other lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sacc = OPS::qk(kt[slot][kk], qb[kk], sacc);
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                sacc = OPS::qk(lds_load16(kl, lds_pos(j, h, 4 * kk + g)), qb[h][kk], sacc);
         float sc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -424,24 +454,30 @@ struct MfmaAttn {
             m = mn;
         }
         op4_t phi, plo;
+        using el_t = typename std::remove_reference<decltype(phi[0])>::type;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float pr = __builtin_amdgcn_exp2f(sc[r] - ms);
             l += pr;
             short h, lo;
             OPS::split(pr, h, lo);
-            phi[r] = __builtin_bit_cast(typename std::remove_reference<decltype(phi[0])>::type, h);
-            plo[r] = __builtin_bit_cast(typename std::remove_reference<decltype(plo[0])>::type, lo);
+            phi[r] = __builtin_bit_cast(el_t, h);
+            plo[r] = __builtin_bit_cast(el_t, lo);
         }
-        // the V rows this wave just stored are read back by other lanes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const op4_t zero = {};
+        // V^T read transposed: lane (g, j) takes row 4g + j/4, bytes 32t + 8(j%4) of its head row.
+        const int trow = 4 * g + j / 4;
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            const op4_t a = OPS::read_tr(buf + tr_lds[t]);
-            acc[t] = OPS::pv(a, phi, acc[t]);
-            acc[t] = OPS::pv(a, plo, acc[t]);
+        for (int h = 0; h < NH; ++h) {
+            const bool mine = j >= h * G && j < (h + 1) * G;
+            const op4_t bh = mine ? phi : zero;
+            const op4_t bl = mine ? plo : zero;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const op4_t a = OPS::read_tr(vl + lds_pos(trow, h, 2 * t + (j % 4) / 2) + 8 * (j % 2));
+                acc[t] = OPS::pv(a, bh, acc[t]);
+                acc[t] = OPS::pv(a, bl, acc[t]);
+            }
         }
     }
 
@@ -451,7 +487,7 @@ struct MfmaAttn {
     }
 
     __device__ __forceinline__ void store_out(char* out_rows) const {
-        if (j >= G) return;
+        if (j >= HG) return;
         const float inv = 1.f / l;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
@@ -460,7 +496,7 @@ struct MfmaAttn {
     }
 
     __device__ __forceinline__ void store_partial(float* rec_acc, float* rec_ml) const {
-        if (j >= G) return;
+        if (j >= HG) return;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
             *reinterpret_cast<float4*>(rec_acc + j * D + 16 * t + 4 * g) =
@@ -479,9 +515,8 @@ using Engine = typename std::conditional<TU::MFMA, MfmaAttn<E, D, G, TU>, WaveAt
 // Flat schedule: a persistent grid deals equal ranges of the tile stream.
 // ============================================================================
 
-template <class E, int D, int G, class TU>
+template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
 __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParams p) {
-    using A = Engine<E, D, G, TU>;
     constexpr int NS = A::NS;
     constexpr int DEPTH = TU::DEPTH;
     extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
@@ -726,23 +761,28 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
 }
 
 // ============================================================================
-// Fixed partitions: one workgroup per (P-token partition, KV head, sequence).
+// Fixed partitions: one wave per (P-token partition, head group, sequence).
+// A workgroup holds NW consecutive partitions of one sequence and head group;
+// its waves share nothing.  Grid: x = sequence * chunks + chunk, y = head group.
 // ============================================================================
 
-template <class E, int D, int G, class TU>
+template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
 __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(DecodeParams p) {
-    using A = Engine<E, D, G, TU>;
     constexpr int NW = TU::NW;
     constexpr int NS = A::NS;
     constexpr int DEPTH = TU::DEPTH;
+    constexpr int HG = A::HG;
     __shared__ __attribute__((aligned(16))) char sm_eng[NW * (A::kLdsBytes > 0 ? A::kLdsBytes : 16)];
 
-    constexpr int HG = A::HG;
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y * A::NH;  // first KV head of the group
-    const int s = blockIdx.z;
+    const int chunks = (p.n_parts_max + NW - 1) / NW;
+    const int s = blockIdx.x / chunks;
+    const int w = wave_id_uniform();
+    const int part = (blockIdx.x - s * chunks) * NW + w;
+    const int hg = blockIdx.y;  // head group: KV heads hg*NH .. +NH-1
+    const int NG = gridDim.y;
     const int Hq = p.n_q_heads;
-    const int h0 = blockIdx.y * HG;
+    const int lane = threadIdx.x % kWave;
+    char* out_rows = static_cast<char*>(p.out) + ((int64_t)s * Hq + hg * HG) * D * E::kBytes;
     // A length beyond the table is a caller error; clamping keeps every table
     // read inside the row and every partition inside the workspace.
     const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
@@ -750,16 +790,11 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     const int n_parts = (L + P - 1) / P;
 
     if (part >= n_parts) {
-        if (L == 0 && part == 0) {  // nothing to attend: a zero row
-            for (int i = threadIdx.x; i < HG * D; i += blockDim.x)
-                E::store(static_cast<char*>(p.out) + (((int64_t)s * Hq + h0 + i / D) * D + i % D) * E::kBytes,
-                         0.f);
-        }
+        if (L == 0 && part == 0)  // nothing to attend: zero rows
+            for (int i = lane; i < HG * D; i += kWave) E::store(out_rows + i * E::kBytes, 0.f);
         return;
     }
 
-    const int lane = threadIdx.x % kWave;
-    const int w = wave_id_uniform();
     const int nblk = (L + kBlock - 1) / kBlock;
     const int PB = P / kBlock;
     const int b_begin = part * PB;
@@ -768,13 +803,13 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
 
     const uint32_t row_stride = (uint32_t)p.n_kv_heads * A::RB;
     const int64_t blk_bytes = (int64_t)row_stride * kBlock;
-    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * A::RB;
-    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * A::RB;
+    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)hg * A::NH * A::RB;
+    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)hg * A::NH * A::RB;
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
 
     A a;
     a.init(lane, row_stride, sm_eng + w * A::kLdsBytes);
-    a.load_q(static_cast<const char*>(p.q) + ((int64_t)s * Hq + h0) * A::RB);
+    a.load_q(static_cast<const char*>(p.q) + ((int64_t)s * Hq + hg * HG) * A::RB);
     a.reset();
     int pbs[NS];
     auto issue = [&](int slot, int bi) {
@@ -784,17 +819,15 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
         pbs[slot] = pb;
     };
 
-    // This wave's blocks are b_begin + w, + NW, ...
-    const int first = b_begin + w;
+    // Block b_begin + k goes through register slot k % NS, DEPTH blocks ahead.
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
-        if (first + d * NW < b_end) issue(d, first + d * NW);
-    for (int bi = first; bi < b_end; bi += NS * NW) {
+        if (b_begin + d < b_end) issue(d, b_begin + d);
+    for (int bi = b_begin; bi < b_end; bi += NS) {
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
-            const int b = bi + u * NW;
-            const int bn = b + DEPTH * NW;
-            if (bn < b_end) issue((u + DEPTH) % NS, bn);
+            const int b = bi + u;
+            if (b + DEPTH < b_end) issue((u + DEPTH) % NS, b + DEPTH);
             if (b < b_end) {
                 const int valid = pbs[u] < 0 ? 0 : (b == nblk - 1 ? tail_rows : kBlock);
                 a.process(u, valid, p.scale_log2);
@@ -802,75 +835,56 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
         }
     }
     a.reduce();
-
-    // Combine the waves through LDS.
-    __shared__ __attribute__((aligned(16))) float sm_acc[NW][HG][D];
-    __shared__ float sm_ml[NW][HG][2];
-    for (int i = threadIdx.x % kWave; i < HG * 2; i += kWave) sm_ml[w][i / 2][i % 2] = i % 2 ? 0.f : -INFINITY;
-    __builtin_amdgcn_wave_barrier();
-    a.store_partial(&sm_acc[w][0][0], &sm_ml[w][0][0]);
-    __syncthreads();
-
-    const bool single = n_parts == 1;
-    for (int i = threadIdx.x; i < HG * D; i += NW * kWave) {
-        const int gi = i / D;
-        const int d = i % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int x = 0; x < NW; ++x) M = fmaxf(M, sm_ml[x][gi][0]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int x = 0; x < NW; ++x) {
-            // a wave that held no rows keeps m = -inf (and no acc): weight 0
-            const float f = sm_ml[x][gi][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_ml[x][gi][0] - M);
-            num = f == 0.f ? num : __builtin_fmaf(f, sm_acc[x][gi][d], num);
-            den = __builtin_fmaf(f, sm_ml[x][gi][1], den);
-        }
-        const int64_t row = (int64_t)s * Hq + h0 + gi;
-        if (single) {
-            E::store(static_cast<char*>(p.out) + (row * D + d) * E::kBytes, num / den);
-        } else {
-            const int64_t slot = row * p.n_parts_max + part;
-            p.ws_acc[slot * D + d] = num;
-            if (d == 0) {
-                p.ws_ml[slot * 2] = M;
-                p.ws_ml[slot * 2 + 1] = den;
-            }
-        }
+    if (n_parts == 1) {
+        a.store_out(out_rows);
+    } else {  // record [sequence][head group][partition] of [HG][D] acc and [HG][2] (m, l)
+        const int64_t rec = ((int64_t)s * NG + hg) * p.n_parts_max + part;
+        a.store_partial(p.ws_acc + rec * HG * D, p.ws_ml + rec * HG * 2);
     }
 }
 
 // One wave per (sequence, query head); only sequences split into >= 2 partitions.
 template <class E, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-    constexpr int PER = (D + kWave - 1) / kWave;
-    const int lane = threadIdx.x % kWave;
     const int pair = blockIdx.x * (blockDim.x / kWave) + wave_id_uniform();
     if (pair >= p.num_seqs * p.n_q_heads) return;
     const int s = pair / p.n_q_heads;
+    const int h = pair % p.n_q_heads;
     const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
     const int n = (L + p.part_tokens - 1) / p.part_tokens;
     if (n < 2) return;
-    merge_records<E, D>(p.ws_ml, p.ws_acc, (int64_t)pair * p.n_parts_max, 1, n,
-                        static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes);
+    const int HG = p.n_q_heads / p.n_kv_heads * p.heads_per_wave;  // query heads per record
+    const int NG = p.n_kv_heads / p.heads_per_wave;
+    const int hg = h / HG;
+    const int64_t first = ((int64_t)s * NG + hg) * p.n_parts_max * HG + h % HG;
+    merge_records<E, D>(p.ws_ml, p.ws_acc, first, HG, n, static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes);
 }
 
 // ============================================================================
 // Dispatch
 // ============================================================================
 
-// Launch shape per element type, head_dim and group size: the matrix-core
-// engine for 16-bit caches with G >= 4; otherwise the vector engine streaming
-// two adjacent KV heads per wave (16 lanes per head row, so one load
-// instruction reads two tokens x 512 contiguous bytes at D = 128, 16-bit).
-// NH1 is the one-head shape used when the KV head count is odd.
+// Launch shape per element type, head_dim and group size (chosen by measured
+// sweeps on MI355X).  16-bit caches with G >= 4 use the matrix-core engine:
+// under the flat schedule 8 waves per workgroup with two tiles in flight at
+// G = 4, one wave with one tile in flight at G = 8 (its larger score tile
+// leaves fewer registers for prefetch); under fixed partitions one wave per
+// workgroup with two tiles in flight, so that a wave streams its partition
+// alone and no workgroup waits on its slowest wave.  Other 16-bit caches use
+// the vector engine streaming two adjacent KV heads per wave (16 lanes per head
+// row, so one load instruction reads two tokens x 512 contiguous bytes at
+// D = 128); fp32 caches one head per wave.  NH1 is the one-head shape used
+// when the KV head count is odd (it must match `type` in everything but NH).
 template <class E, int D, int G>
 struct DefaultTune {
     static constexpr bool kMfma = E::kBytes == 2 && G >= 4;
     static constexpr int kCH = D * E::kBytes / 16;
     static constexpr int kR = kCH < 16 ? kCH : 16;
-    static constexpr int kNH = (E::kBytes == 2 && !kMfma) ? 2 : 1;
-    using type = Tune<4, kNH == 2 ? kR : 8, 1, true, kMfma, kNH>;
+    static constexpr int kNH = E::kBytes == 2 && !kMfma ? 2 : 1;
+    using mfma_flat = typename std::conditional<(G >= 8), Tune<1, 8, 1, true, true, 1>, Tune<8, 8, 2, true, true, 1>>::type;
+    using valu = typename std::conditional<kNH == 2, Tune<8, kR, 1, true, false, 2>, Tune<4, 8, 1, true, false, 1>>::type;
+    using type = typename std::conditional<kMfma, mfma_flat, valu>::type;
+    using parts = typename std::conditional<kMfma, Tune<1, 8, 2, true, true, 1>, valu>::type;
     using NH1 = Tune<4, 8, 1, true, kMfma, 1>;
 };
 
@@ -880,23 +894,25 @@ static int heads_per_wave_t(int n_kv_heads) {
     return n_kv_heads % nh == 0 ? nh : 1;
 }
 
-template <class E, int D, int G, class TU>
-hipError_t launch_parts_tuned(const DecodeParams& p, hipStream_t stream) {
-    DecodeParams q = p;
-    q.heads_per_wave = TU::NH;
-    const dim3 grid(q.n_parts_max, q.n_kv_heads / TU::NH, q.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU>), grid, dim3(TU::NW * kWave), 0, stream, q);
+template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
+hipError_t launch_parts_tuned(const DecodeParams& pin, hipStream_t stream) {
+    DecodeParams p = pin;
+    p.heads_per_wave = A::NH;
+    const int64_t chunks = (p.n_parts_max + TU::NW - 1) / TU::NW;
+    if (chunks * p.num_seqs > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(chunks * p.num_seqs), p.n_kv_heads / A::NH);
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU, A>), grid, dim3(TU::NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
 // Workgroups of the flat kernel resident on the whole device, capped so the
 // grid's waves never exceed kMaxFlatWorkers.
-template <class E, int D, int G, class TU>
+template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
 hipError_t launch_flat_tuned(const DecodeParams& pin, hipStream_t stream) {
     DecodeParams p = pin;
-    p.heads_per_wave = TU::NH;
-    auto kern = decode_flat_kernel<E, D, G, TU>;
-    const size_t lds = (size_t)TU::NW * Engine<E, D, G, TU>::kLdsBytes + (size_t)(2 * p.num_seqs + 1) * sizeof(int32_t);
+    p.heads_per_wave = A::NH;
+    auto kern = decode_flat_kernel<E, D, G, TU, A>;
+    const size_t lds = (size_t)TU::NW * A::kLdsBytes + (size_t)(2 * p.num_seqs + 1) * sizeof(int32_t);
     static thread_local int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
     static thread_local size_t cached_lds = 0;
     int dev = 0;
@@ -922,9 +938,11 @@ hipError_t launch_flat_tuned(const DecodeParams& pin, hipStream_t stream) {
 template <class E, int D, int G>
 static hipError_t launch_g(const DecodeParams& p, bool flat, hipStream_t stream) {
     using TU = typename DefaultTune<E, D, G>::type;
+    using TP = typename DefaultTune<E, D, G>::parts;
     using TU1 = typename DefaultTune<E, D, G>::NH1;
+    static_assert(TU::NH == TP::NH, "both schedules must group KV heads alike (the merge pass assumes it)");
     if (heads_per_wave_t<E, D, G>(p.n_kv_heads) == TU::NH)
-        return flat ? launch_flat_tuned<E, D, G, TU>(p, stream) : launch_parts_tuned<E, D, G, TU>(p, stream);
+        return flat ? launch_flat_tuned<E, D, G, TU>(p, stream) : launch_parts_tuned<E, D, G, TP>(p, stream);
     return flat ? launch_flat_tuned<E, D, G, TU1>(p, stream) : launch_parts_tuned<E, D, G, TU1>(p, stream);
 }
 

@@ -286,7 +286,9 @@ pkv_status paged_attention_partitions(const void* q, const void* k_cache, const 
     st = check_workspace(pl, workspace, ws_bytes);
     if (st != PKV_OK) return st;
     if (num_seqs == 0) return ok();
-    if (pl.n_parts_max > 65535) return fail(PKV_ENOTSUP, "%d partitions per sequence exceed 65535", pl.n_parts_max);
+    if ((int64_t)pl.n_parts_max * num_seqs > 0x7fffffff)
+        return fail(PKV_ENOTSUP, "%d partitions per sequence x %d sequences exceed the launch grid", pl.n_parts_max,
+                    num_seqs);
     const pkv::DecodeParams p = make_params(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
                                             context_lens, num_seqs, n_q_heads, scale, out, pl, workspace);
     hipError_t e = pkv::launch_decode_partitions(p, layout->dtype, layout->head_dim,
