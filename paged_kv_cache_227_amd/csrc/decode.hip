@@ -843,21 +843,100 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     }
 }
 
-// One wave per (sequence, query head); only sequences split into >= 2 partitions.
+// Fixed partitions: one 256-thread workgroup per (sequence, query head) whose
+// sequence has >= 2 partitions.  A long sequence has hundreds of records, so
+// the workgroup reads RS records side by side (thread t owns float4 column
+// t % VPR of record slot t / VPR), UNROLL deep, and the slots' partial sums
+// meet in LDS.
+constexpr int kMergeThreads = 256;
+
 template <class E, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-    const int pair = blockIdx.x * (blockDim.x / kWave) + wave_id_uniform();
-    if (pair >= p.num_seqs * p.n_q_heads) return;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
+    constexpr int NT = kMergeThreads;
+    constexpr int NWV = NT / kWave;
+    constexpr int VPR = D / 4;    // float4 columns of a record row
+    constexpr int RS = NT / VPR;  // record slots
+    constexpr int UNROLL = 4;
+    __shared__ float sm_max[NWV], sm_den[NWV];
+    __shared__ __attribute__((aligned(16))) float4 sm_num[RS][VPR];
+
+    const int pair = blockIdx.x;
     const int s = pair / p.n_q_heads;
     const int h = pair % p.n_q_heads;
     const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
     const int n = (L + p.part_tokens - 1) / p.part_tokens;
-    if (n < 2) return;
+    if (n < 2) return;  // uniform over the workgroup
     const int HG = p.n_q_heads / p.n_kv_heads * p.heads_per_wave;  // query heads per record
     const int NG = p.n_kv_heads / p.heads_per_wave;
     const int hg = h / HG;
+    // record x of this head: row (first + x * HG) of acc ([.][D]) and ml ([.][2])
     const int64_t first = ((int64_t)s * NG + hg) * p.n_parts_max * HG + h % HG;
-    merge_records<E, D>(p.ws_ml, p.ws_acc, first, HG, n, static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes);
+    const float* ml = p.ws_ml;
+    const float* acc = p.ws_acc;
+    const int tid = threadIdx.x;
+    const int wv = tid / kWave;
+
+    float M = -INFINITY;
+    for (int x = tid; x < n; x += NT) M = fmaxf(M, ml[(first + (int64_t)x * HG) * 2]);
+    M = wave_max(M);
+    if (tid % kWave == 0) sm_max[wv] = M;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) M = fmaxf(M, sm_max[i]);
+
+    float den = 0.f;
+    for (int x = tid; x < n; x += NT) {
+        const int64_t r = first + (int64_t)x * HG;
+        den += __builtin_amdgcn_exp2f(ml[r * 2] - M) * ml[r * 2 + 1];
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) den += shfl_xor(den, m);
+    if (tid % kWave == 0) sm_den[wv] = den;
+
+    const int c = tid % VPR;
+    const int slot = tid / VPR;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int x0 = slot; x0 < n; x0 += RS * UNROLL) {
+        float f[UNROLL];
+        float4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int x = x0 + u * RS;
+            const bool ok = x < n;
+            const int64_t r = first + (int64_t)(ok ? x : 0) * HG;
+            f[u] = ok ? __builtin_amdgcn_exp2f(ml[r * 2] - M) : 0.f;
+            v[u] = *reinterpret_cast<const float4*>(acc + r * D + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            num.x = __builtin_fmaf(f[u], v[u].x, num.x);
+            num.y = __builtin_fmaf(f[u], v[u].y, num.y);
+            num.z = __builtin_fmaf(f[u], v[u].z, num.z);
+            num.w = __builtin_fmaf(f[u], v[u].w, num.w);
+        }
+    }
+    sm_num[slot][c] = num;
+    __syncthreads();
+    if (tid < VPR) {
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < NWV; ++i) tot += sm_den[i];
+        const float inv = 1.f / tot;
+        float4 o = sm_num[0][tid];
+#pragma unroll
+        for (int r = 1; r < RS; ++r) {
+            const float4 y = sm_num[r][tid];
+            o.x += y.x;
+            o.y += y.y;
+            o.z += y.z;
+            o.w += y.w;
+        }
+        char* out_row = static_cast<char*>(p.out) + ((int64_t)pair * D + 4 * tid) * E::kBytes;
+        E::store(out_row, o.x * inv);
+        E::store(out_row + E::kBytes, o.y * inv);
+        E::store(out_row + 2 * E::kBytes, o.z * inv);
+        E::store(out_row + 3 * E::kBytes, o.w * inv);
+    }
 }
 
 // ============================================================================
@@ -1013,16 +1092,17 @@ static hipError_t launch_merge_e(const DecodeParams& pin, int head_dim, int grou
     DecodeParams p = pin;
     p.heads_per_wave = heads_per_wave_e<E>(head_dim, group, p.n_kv_heads);
     const int pairs = p.num_seqs * p.n_q_heads;
-    const dim3 grid((pairs + 3) / 4);
+    const dim3 grid_flat((pairs + 3) / 4);  // one wave per pair
+    const dim3 grid_parts(pairs);           // one workgroup per pair
     const bool flat = p.part_tokens == 0;
     switch (head_dim) {
         case 64:
-            if (flat) hipLaunchKernelGGL((decode_flat_merge_kernel<E, 64>), grid, dim3(256), 0, stream, p);
-            else hipLaunchKernelGGL((decode_merge_kernel<E, 64>), grid, dim3(256), 0, stream, p);
+            if (flat) hipLaunchKernelGGL((decode_flat_merge_kernel<E, 64>), grid_flat, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((decode_merge_kernel<E, 64>), grid_parts, dim3(kMergeThreads), 0, stream, p);
             break;
         case 128:
-            if (flat) hipLaunchKernelGGL((decode_flat_merge_kernel<E, 128>), grid, dim3(256), 0, stream, p);
-            else hipLaunchKernelGGL((decode_merge_kernel<E, 128>), grid, dim3(256), 0, stream, p);
+            if (flat) hipLaunchKernelGGL((decode_flat_merge_kernel<E, 128>), grid_flat, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((decode_merge_kernel<E, 128>), grid_parts, dim3(kMergeThreads), 0, stream, p);
             break;
         default: return hipErrorInvalidValue;
     }
