@@ -193,6 +193,42 @@ int ref_append(const void* k_new, const void* v_new, void* k_cache, void* v_cach
 }
 
 /* ------------------------------------------------------------------------ */
+/* Copy-on-write, the data half ("How a serving engine actually works",      */
+/* section "Copy-on-write, because you have used fork()"): a sequence about  */
+/* to write into a block that others also hold takes a private block first. */
+/* The tokens the shared block already holds for it (its first n rows) must  */
+/* then exist in the private block too; the pages' counter simulation skips  */
+/* this copy.                                                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For every i < n_copies: rows 0 .. n_rows[i]-1 of physical block src[i] are
+ * copied bit for bit to the same rows of block dst[i], all heads, in both
+ * caches.  Row r of block b is slot b * B + r.  Every argument is checked
+ * before anything is written: a block outside the pool or a row count outside
+ * [0, B] rejects the whole call.
+ */
+int ref_copy_blocks(void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size,
+                    int32_t n_kv_heads, int32_t head_dim, int dtype, const int32_t* src,
+                    const int32_t* dst, const int32_t* n_rows, int32_t n_copies) {
+    const int esz = ref_elt_size(dtype);
+    if (esz == 0 || block_size < 1 || n_kv_heads < 1 || head_dim < 1 || n_copies < 0) return REF_EINVAL;
+    for (int32_t i = 0; i < n_copies; ++i)
+        if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks || n_rows[i] < 0 ||
+            n_rows[i] > block_size)
+            return REF_EINVAL;
+    const int64_t row_bytes = (int64_t)n_kv_heads * head_dim * esz;
+    for (int32_t i = 0; i < n_copies; ++i)
+        for (int32_t r = 0; r < n_rows[i]; ++r) {
+            const int64_t from = (int64_t)src[i] * block_size + r;
+            const int64_t to = (int64_t)dst[i] * block_size + r;
+            memcpy((char*)k_cache + to * row_bytes, (const char*)k_cache + from * row_bytes, row_bytes);
+            memcpy((char*)v_cache + to * row_bytes, (const char*)v_cache + from * row_bytes, row_bytes);
+        }
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Gather (snowch ch08, "The measurement"): one sequence's cache as a        */
 /* contiguous [n_kv_heads][length][head_dim] array, here in double.          */
 /* ------------------------------------------------------------------------ */

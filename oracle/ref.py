@@ -59,6 +59,8 @@ class Oracle:
         L.ref_append.argtypes = [P, P, P, P, i32, i32, i32, i32, ctypes.c_int, P, i32, P, i32]
         L.ref_append.restype = ctypes.c_int
         L.ref_gather.argtypes = [P, i32, i32, i32, ctypes.c_int, P, i32, P]
+        L.ref_copy_blocks.argtypes = [P, P, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32]
+        L.ref_copy_blocks.restype = ctypes.c_int
         L.ref_gather.restype = ctypes.c_int
         L.ref_attention_decode.argtypes = [P, P, P, i32, i32, i32, ctypes.c_int, P, i32, P, i32,
                                            i32, dbl, P, i32, i32, P]
@@ -117,6 +119,21 @@ class Oracle:
                                D, dtype, _ptr(bt), bt.shape[1], _ptr(pos), S)
         if rc:
             raise ValueError("ref_append rejected its arguments (%d)" % rc)
+
+    def copy_blocks(self, k_cache, v_cache, src, dst, n_rows, dtype):
+        """In place: rows [0, n_rows[i]) of block src[i] to block dst[i], both caches."""
+        for a in (k_cache, v_cache):
+            _check_store(a, dtype)
+        nb, B, Hkv, D = k_cache.shape
+        if v_cache.shape != k_cache.shape:
+            raise ValueError("shape mismatch")
+        s, d, n = _i32(src), _i32(dst), _i32(n_rows)
+        if not (s.shape == d.shape == n.shape) or s.ndim != 1:
+            raise ValueError("src, dst and n_rows must be equal-length vectors")
+        rc = self.L.ref_copy_blocks(_ptr(k_cache), _ptr(v_cache), nb, B, Hkv, D, dtype, _ptr(s), _ptr(d),
+                                    _ptr(n), s.shape[0])
+        if rc:
+            raise ValueError("ref_copy_blocks rejected its arguments (%d)" % rc)
 
     def gather(self, cache, table_row, length, dtype):
         """Contiguous [Hkv][length][D] float64 copy of one sequence's cache."""
@@ -203,6 +220,10 @@ def physical_slot(table_row, block_size, i):
 
 def append(*a, **k):
     return default().append(*a, **k)
+
+
+def copy_blocks(*a, **k):
+    return default().copy_blocks(*a, **k)
 
 
 def gather(*a, **k):

@@ -321,4 +321,126 @@ def pin_sampled_sequences(orc):
     assert np.all(np.isnan(part[[0, 2, 4]]))
 
 
+# ---------------------------------------------------------------------------
+# Copy-on-write: the data half
+# ---------------------------------------------------------------------------
+
+def _poisoned_pool(shape, dtype):
+    """A pool of quiet NaNs whose payload names the block (1 + block index), so
+    a row copied from the wrong block, or past the rows asked for, changes bits."""
+    b = (np.arange(shape[0]) + 1).reshape((-1,) + (1,) * (len(shape) - 1))
+    if dtype == F32:
+        return np.ascontiguousarray(np.broadcast_to((0x7FC00000 | b).astype(np.uint32), shape)).view(np.float32)
+    quiet = {F16: 0x7E00, BF16: 0x7FC0}[dtype]
+    mask = {F16: 0x1FF, BF16: 0x3F}[dtype]
+    return np.ascontiguousarray(np.broadcast_to((quiet | (b & mask)).astype(np.uint16), shape))
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+def _fork_example():
+    g = read_golden("fork_cow_b16.txt")
+    B = ints(g["block_size"][0])[0]
+    n_prompt = ints(g["prompt_tokens"][0])[0]
+    prompt_table = ints(g["prompt_table"][0])
+    samples = [ints(r[1:]) for r in sorted(g["sample_table"], key=lambda r: int(r[0]))]
+    return B, n_prompt, prompt_table, samples
+
+
+def _diverge(orc, rng, dtype, Hkv, D):
+    """The printed fork: the prompt's rows in its blocks, then for each sample
+    the copy of the shared last block's filled rows into the sample's private
+    block, then the sample's first generated token appended at position
+    n_prompt.  Unwritten slots hold NaN."""
+    B, n_prompt, prompt_table, samples = _fork_example()
+    nb = 1 + max(max(t) for t in samples + [prompt_table])
+    pk = to_storage(rng.standard_normal((n_prompt, Hkv, D)), dtype)
+    pv = to_storage(rng.standard_normal((n_prompt, Hkv, D)), dtype)
+    nk = to_storage(rng.standard_normal((len(samples), Hkv, D)), dtype)
+    nv = to_storage(rng.standard_normal((len(samples), Hkv, D)), dtype)
+    kc, vc = _poisoned_pool((nb, B, Hkv, D), dtype), _poisoned_pool((nb, B, Hkv, D), dtype)
+    sequential_fill(kc, prompt_table, pk)
+    sequential_fill(vc, prompt_table, pv)
+    before_k, before_v = kc.copy(), vc.copy()
+    # each sample's table differs from the prompt's in its last entry only
+    for t in samples:
+        assert t[:-1] == prompt_table[:-1] and t[-1] != prompt_table[-1]
+    src = [prompt_table[-1]] * len(samples)
+    dst = [t[-1] for t in samples]
+    orc.copy_blocks(kc, vc, src, dst, [n_prompt % B] * len(samples), dtype)
+    orc.append(nk, nv, kc, vc, np.array(samples, np.int32), np.full(len(samples), n_prompt, np.int32), dtype)
+    return dict(B=B, n_prompt=n_prompt, prompt_table=prompt_table, samples=samples, kc=kc, vc=vc,
+                before_k=before_k, before_v=before_v, pk=pk, pv=pv, nk=nk, nv=nv)
+
+
+def pin_fork_diverge_copy(orc):
+    """Worked example of "How a serving engine actually works", section
+    "Copy-on-write, because you have used fork()", with data: every sample's
+    blocks hold exactly the prompt followed by its own token (checked against
+    an independent sequential fill, NaN slots included), and the prompt's
+    blocks are untouched."""
+    rng = np.random.default_rng(41)
+    for dtype in (F32, F16, BF16):
+        r = _diverge(orc, rng, dtype, 2, 8)
+        for i, t in enumerate(r["samples"]):
+            for cache, rows, new in ((r["kc"], r["pk"], r["nk"]), (r["vc"], r["pv"], r["nv"])):
+                want = _poisoned_pool(cache.shape, dtype)
+                sequential_fill(want, t, list(rows) + [new[i]])
+                assert np.array_equal(_bits(cache[t]), _bits(want[t])), "sample %d's blocks (dtype %d)" % (i, dtype)
+        pt = r["prompt_table"]
+        assert np.array_equal(_bits(r["kc"][pt]), _bits(r["before_k"][pt])), "prompt K blocks changed"
+        assert np.array_equal(_bits(r["vc"][pt]), _bits(r["before_v"][pt])), "prompt V blocks changed"
+
+
+def pin_fork_diverge_attention(orc):
+    """After the divergence each sample attends to the prompt plus its own token:
+    the oracle through the shared tables equals torch SDPA (float64) on the
+    dense sequences."""
+    rng = np.random.default_rng(42)
+    Hkv, D, Hq = 2, 16, 4
+    r = _diverge(orc, rng, BF16, Hkv, D)
+    S = len(r["samples"])
+    L = r["n_prompt"] + 1
+    q = to_storage(rng.standard_normal((S, Hq, D)), BF16)
+    got = orc.attention_decode(q, r["kc"], r["vc"], np.array(r["samples"], np.int32),
+                               np.full(S, L, np.int32), 0.25, BF16)
+    for i in range(S):
+        k = np.concatenate([from_storage(r["pk"], BF16), from_storage(r["nk"][i:i + 1], BF16)])
+        v = np.concatenate([from_storage(r["pv"], BF16), from_storage(r["nv"][i:i + 1], BF16)])
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(from_storage(q[i], BF16))[None, :, None, :],
+            torch.from_numpy(k.transpose(1, 0, 2).copy())[None],
+            torch.from_numpy(v.transpose(1, 0, 2).copy())[None], scale=0.25, enable_gqa=True)
+        _close(got[i], o[0, :, 0, :].numpy(), 1e-12, "sample %d after copy-on-write" % i)
+
+
+def pin_copy_blocks_whole_and_empty(orc):
+    """n_rows = B moves a whole block (a full block's sequence reads the same
+    through either block); n_rows = 0 changes nothing; a bad argument rejects
+    the call before anything is written."""
+    rng = np.random.default_rng(43)
+    B, Hkv, D, L = 16, 2, 8, 16
+    rows = to_storage(rng.standard_normal((L, Hkv, D)), F16)
+    kc, vc = _poisoned_pool((6, B, Hkv, D), F16), _poisoned_pool((6, B, Hkv, D), F16)
+    sequential_fill(kc, [2], rows)
+    sequential_fill(vc, [2], rows)
+    snap = kc.copy()
+    orc.copy_blocks(kc, vc, [2], [4], [0], F16)
+    assert np.array_equal(_bits(kc), _bits(snap)), "n_rows = 0 wrote something"
+    orc.copy_blocks(kc, vc, [2], [4], [B], F16)
+    assert np.array_equal(orc.gather(kc, [4], L, F16), orc.gather(kc, [2], L, F16))
+    assert np.array_equal(orc.gather(kc, [4], L, F16), from_storage(rows, F16).transpose(1, 0, 2))
+    snap = kc.copy()
+    for bad in (([2], [6], [1]), ([-1], [4], [1]), ([2], [4], [B + 1]), ([2], [4], [-1])):
+        try:
+            orc.copy_blocks(kc, vc, *bad, F16)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("copy_blocks accepted %r" % (bad,))
+    assert np.array_equal(_bits(kc), _bits(snap)), "a rejected call wrote something"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -58,6 +58,18 @@ MUTANTS = [
      "const int64_t slot = ref_physical_slot(row, block_size, p) + 1;"),
     ("L = 0 not handled", "    if (L <= 0) {\n        for (int32_t d = 0; d < D; ++d) out_row[d] = 0.0;\n        return;\n    }\n    ref_scores",
      "    ref_scores"),
+    ("copy drops the last filled row", "for (int32_t r = 0; r < n_rows[i]; ++r) {",
+     "for (int32_t r = 0; r < n_rows[i] - 1; ++r) {"),
+    ("copy runs backwards (destination into source)",
+     "memcpy((char*)k_cache + to * row_bytes, (const char*)k_cache + from * row_bytes, row_bytes);",
+     "memcpy((char*)k_cache + from * row_bytes, (const char*)k_cache + to * row_bytes, row_bytes);"),
+    ("copy forgets the value cache",
+     "            memcpy((char*)v_cache + to * row_bytes, (const char*)v_cache + from * row_bytes, row_bytes);\n",
+     ""),
+    ("copy target not scaled by B", "const int64_t to = (int64_t)dst[i] * block_size + r;",
+     "const int64_t to = (int64_t)dst[i] + r;"),
+    ("copy moves whole blocks whatever n_rows", "for (int32_t r = 0; r < n_rows[i]; ++r) {",
+     "for (int32_t r = 0; r < (n_rows[i] ? block_size : 0); ++r) {"),
 ]
 
 
