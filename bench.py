@@ -42,23 +42,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+COPY_KERNEL_SOURCES = ["paged_kv_cache_227_amd/csrc/copy_blocks.hip"]
+
+
+def kernel_hash(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(config, n_bytes):
-    """HBM traffic of the partition kernel from committed counter summaries,
+def load_traffic(config, n_bytes, sources=None):
+    """HBM traffic of the measured kernel from committed counter summaries,
     or None when absent or taken on different kernel sources."""
     path = TRAFFIC_FILE.format(config=config)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash(sources):
         return None
     return t
 
@@ -221,6 +224,114 @@ def cpu_baseline(w, budget_s=15.0, min_s=10.0):
             "tokens_per_s": done / elapsed}
 
 
+def run_copy_probe(n_bytes):
+    """One launch of the plain copy kernel over n_bytes: a dispatch of known
+    traffic for calibrating hardware counters in the same profiled run."""
+    import torch
+    import paged_kv_cache_227_amd as P
+    n = n_bytes // 16 * 16
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    P.probe_copy(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def run_copy(cw, steps, warmup):
+    """Time paged_kv_copy_blocks on the copy workload: `steps` calls between two
+    synchronisations, then the same calls with HIP events around each launch."""
+    import torch
+    import paged_kv_cache_227_amd as P
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cw.dtype]
+    shape = (cw.num_blocks, cw.block_size, cw.n_kv_heads, cw.head_dim)
+    kc = torch.zeros(shape, dtype=tdt, device="cuda:0")
+    vc = torch.zeros_like(kc)
+    src, dst, rows = (torch.from_numpy(x).to("cuda:0") for x in (cw.src, cw.dst, cw.rows))
+
+    def step():
+        P.paged_kv_copy_blocks(kc, vc, src, dst, rows)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        step()
+        e[1].record()
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    del kc, vc
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms_step, kernel_ms_mean=statistics.fmean(t), kernel_ms_median=statistics.median(t))
+
+
+def cpu_baseline_copy(cw, min_s=3.0):
+    """The oracle's block copy on host copies of the caches, repeated until
+    min_s has elapsed."""
+    import numpy as np
+    from oracle import ref
+    orc = ref.default()
+    st = np.float32 if cw.dtype == "f32" else np.uint16
+    shape = (cw.num_blocks, cw.block_size, cw.n_kv_heads, cw.head_dim)
+    kc, vc = np.zeros(shape, st), np.zeros(shape, st)
+    code = {"f32": 0, "f16": 1, "bf16": 2}[cw.dtype]
+    n, elapsed = 0, 0.0
+    while elapsed < min_s:
+        t0 = time.perf_counter()
+        orc.copy_blocks(kc, vc, cw.src, cw.dst, cw.rows, code)
+        elapsed += time.perf_counter() - t0
+        n += 1
+    return {"value": 2 * cw.moved_bytes() * n / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d whole calls (%d copies each), %.1f s" % (n, len(cw.src), elapsed)}
+
+
+def main_copy(a):
+    from paged_kv_cache_227_amd import workloads as W
+    if a.config not in W.COPY_CONFIGS:
+        raise SystemExit("copy workloads: %s" % ", ".join(W.COPY_CONFIGS))
+    name = a.config
+    cw = W.COPY_CONFIGS[name]()
+    moved = 2 * cw.moved_bytes()  # read + written
+    log("copy workload %s: %d copies, %d rows, %.1f MB read and written" % (
+        name, len(cw.src), int(cw.rows.sum()), moved / 1e6))
+    g = run_copy(cw, a.steps, a.warmup)
+    log("gpu: %.4f ms/call, kernel %.4f ms" % (g["ms_per_step"], g["kernel_ms_mean"]))
+    achieved = moved / (g["kernel_ms_mean"] * 1e-3) / 1e9
+    value = moved / (g["ms_per_step"] * 1e-3) / 1e9
+    t = load_traffic(name, moved, COPY_KERNEL_SOURCES)
+    traffic = None if t is None else int(round(t["hbm_bytes_per_launch"]))
+    res = {
+        "metric": "paged KV block copy (copy-on-write): bytes read + written per second", "value": round(value, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(g["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cw.dtype, "data": "synthetic",
+        "config": {"workload": name, "n_copies": int(len(cw.src)), "rows_copied": int(cw.rows.sum()),
+                   "num_blocks": cw.num_blocks, "n_kv_heads": cw.n_kv_heads, "head_dim": cw.head_dim,
+                   "block_size": cw.block_size, "bytes_read_and_written": moved, "seed": cw.seed,
+                   "notes": cw.notes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "copy_blocks_kernel",
+                     "algorithmic_bytes_per_launch": moved,
+                     "timing": "HIP events around each launch, %d calls right after the timed region" % a.steps,
+                     "mean_launch_ms": round(g["kernel_ms_mean"], 5)},
+        "us_per_call": round(g["ms_per_step"] * 1e3, 2),
+    }
+    if a.copy_probe_bytes:
+        run_copy_probe(a.copy_probe_bytes)
+        res["copy_probe_bytes"] = a.copy_probe_bytes // 16 * 16
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_copy(cw)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def summarize_pmc(d):
     """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
     --pmc CSV output under directory d."""
@@ -238,7 +349,8 @@ def summarize_pmc(d):
     return out
 
 
-def write_traffic(fetch_dir, write_dir, config, kv_bytes, copy_bytes, out_path, kernel_key="decode_flat_kernel"):
+def write_traffic(fetch_dir, write_dir, config, kv_bytes, copy_bytes, out_path, kernel_key="decode_flat_kernel",
+                  sources=None):
     """HBM traffic per launch of the decode kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the same
     counter reads for the plain copy kernel of known size in the same run."""
@@ -259,7 +371,7 @@ def write_traffic(fetch_dir, write_dir, config, kv_bytes, copy_bytes, out_path, 
     w_scale = copy_kib / copy_w["WRITE_SIZE"]["mean"]
     read_b = dec_f["FETCH_SIZE"]["mean"] * f_scale * 1024
     write_b = dec_w["WRITE_SIZE"]["mean"] * w_scale * 1024
-    t = {"config": config, "kernel": name, "kernel_hash": kernel_hash(),
+    t = {"config": config, "kernel": name, "kernel_hash": kernel_hash(sources),
          "fetch_size_kib_raw": dec_f["FETCH_SIZE"]["mean"], "write_size_kib_raw": dec_w["WRITE_SIZE"]["mean"],
          "dispatches": dec_f["FETCH_SIZE"]["dispatches"],
          "copy_probe_bytes": copy_bytes, "copy_fetch_kib_raw": copy_f["FETCH_SIZE"]["mean"],
@@ -278,7 +390,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama2_7b")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks"],
+                    help="decode: the append + decode step (default); copy_blocks: the copy-on-write block copy")
+    ap.add_argument("--config", default=None,
+                    help="workload (default llama2_7b for decode, copy_whole_llama2_7b for copy_blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -291,17 +406,27 @@ def main():
                     help="after the steps, run the plain copy kernel once over this many bytes "
                          "(a launch of known traffic for calibrating hardware counters)")
     a = ap.parse_args()
+    if a.config is None:
+        a.config = "llama2_7b" if a.op == "decode" else "copy_whole_llama2_7b"
 
     if a.summarize_pmc:
         print(json.dumps(summarize_pmc(a.summarize_pmc), indent=1))
         return 0
     if a.write_traffic:
-        w = make_workload(a.config)
         if not a.copy_probe_bytes:
             raise SystemExit("--write-traffic needs --copy-probe-bytes (the size the counter runs used)")
-        t = write_traffic(a.write_traffic[0], a.write_traffic[1], a.config, w.kv_read_bytes(),
-                          a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=a.config),
-                          "decode_partition_kernel" if w.part_tokens else "decode_flat_kernel")
+        if a.op == "copy_blocks":
+            from paged_kv_cache_227_amd import workloads as W
+            cw = W.COPY_CONFIGS[a.config]()
+            # algorithmic reads: the bytes copied (the writes are as many)
+            t = write_traffic(a.write_traffic[0], a.write_traffic[1], a.config, cw.moved_bytes(),
+                              a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=a.config),
+                              "copy_blocks_kernel", COPY_KERNEL_SOURCES)
+        else:
+            w = make_workload(a.config)
+            t = write_traffic(a.write_traffic[0], a.write_traffic[1], a.config, w.kv_read_bytes(),
+                              a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=a.config),
+                              "decode_partition_kernel" if w.part_tokens else "decode_flat_kernel")
         print(json.dumps(t, indent=1))
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -312,6 +437,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if a.op == "copy_blocks":
+        return main_copy(a)
 
     t = time.perf_counter()
     w = make_workload(a.config)
@@ -360,16 +487,8 @@ def main():
             res["shuffled_vs_in_order_throughput"] = round(t_seq / g["partition_ms_mean"], 4)
             del seq
     if a.copy_probe_bytes:
-        import torch
-        import paged_kv_cache_227_amd as P
-        n = a.copy_probe_bytes // 16 * 16
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        P.probe_copy(src, dst)
-        torch.cuda.synchronize()
-        res["copy_probe_bytes"] = n
-        del src, dst
+        run_copy_probe(a.copy_probe_bytes)
+        res["copy_probe_bytes"] = a.copy_probe_bytes // 16 * 16
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
     print(json.dumps(res), flush=True)

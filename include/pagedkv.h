@@ -6,9 +6,12 @@
  *   append  -- write each sequence's new key/value row into the slot its
  *              block table gives for the token's logical position;
  *   decode  -- attention of each sequence's query over its cached keys and
- *              values, read in place through the block table.
+ *              values, read in place through the block table;
  *
- * Both use the address translation of "How a serving engine actually works"
+ * and the block copy that copy-on-write needs before an append into a block
+ * that another sequence also holds.
+ *
+ * Append and decode use the address translation of "How a serving engine actually works"
  * (paperfordummies.in), section "The one formula":
  *
  *     slot(seq, i) = block_table[seq][i / B] * B + (i mod B)
@@ -103,6 +106,34 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_cache, 
                            const pkv_layout* layout, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* positions, int32_t num_seqs,
                            void* stream);
+
+/*
+ * paged_kv_copy_blocks -- the data half of copy-on-write.
+ *
+ * A sequence about to write into a block that other sequences also hold takes
+ * a private block first, and the tokens the shared block already holds for it
+ * (its first n rows) must be in the private block before the write ("How a
+ * serving engine actually works", paperfordummies.in, section "Copy-on-write,
+ * because you have used fork()"; there the simulation counts the copy but moves
+ * no data).  For every i < n_copies:
+ *     rows [0, n_rows[i]) of block dst_blocks[i] = the same rows of block src_blocks[i]
+ * in both caches, all heads, a bit-exact copy.  Rows >= n_rows[i] of the target
+ * and every other block are left as they were.  n_rows[i] = block_size copies a
+ * whole block (a beam or a swapped-in sequence); 0 copies nothing.
+ *
+ *   k_cache, v_cache  the layer's caches (see top of file), changed in place
+ *   layout            host pointer; any block_size (the copy does not depend on it)
+ *   src_blocks, dst_blocks, n_rows  [n_copies] int32 device arrays
+ *
+ * Preconditions: the targets of copies with n_rows > 0 are pairwise distinct
+ * and none of them is also a source in the same call (a target is a freshly
+ * allocated private block); otherwise the result is unspecified.  A copy with a
+ * block outside [0, num_blocks) or n_rows outside [0, block_size] is skipped.
+ * pkv_validate_copies() checks all of this on host copies of the arrays.
+ */
+pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_layout* layout,
+                                const int32_t* src_blocks, const int32_t* dst_blocks, const int32_t* n_rows,
+                                int32_t n_copies, void* stream);
 
 /*
  * paged_attention_decode -- one decode step of attention through block tables.
@@ -213,6 +244,15 @@ int32_t pkv_partition_tokens_for(int32_t num_seqs, int32_t n_q_heads, int32_t ma
 pkv_status pkv_validate(const pkv_layout* layout, const int32_t* block_tables,
                         int32_t max_blocks_per_seq, const int32_t* context_lens,
                         const int32_t* positions, int32_t num_seqs);
+
+/*
+ * pkv_validate_copies -- host-side check of a paged_kv_copy_blocks batch (HOST
+ * pointers, no GPU work): blocks inside the pool and row counts inside
+ * [0, block_size] (else PKV_EOOB), and the targets of non-empty copies pairwise
+ * distinct and disjoint from the sources (else PKV_EINVAL), with a message.
+ */
+pkv_status pkv_validate_copies(const pkv_layout* layout, const int32_t* src_blocks, const int32_t* dst_blocks,
+                               const int32_t* n_rows, int32_t n_copies);
 
 /* Message of this thread's last non-OK call ("" if none).  Owned by the library. */
 const char* pkv_last_error(void);

@@ -45,6 +45,8 @@ SIGNATURES = {
     "pkv_set_partition_tokens": (ctypes.c_int, [_I32]),
     "pkv_partition_tokens_for": (_I32, [_I32, _I32, _I32, _LP]),
     "pkv_validate": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _I32]),
+    "paged_kv_copy_blocks": (ctypes.c_int, [_P, _P, _LP, _P, _P, _P, _I32, _P]),
+    "pkv_validate_copies": (ctypes.c_int, [_LP, _P, _P, _P, _I32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_probe_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
@@ -164,6 +166,21 @@ def paged_kv_append(k_new, v_new, k_cache, v_cache, block_tables, positions, str
                                  _stream(stream, k_cache.device)), "paged_kv_append")
 
 
+def paged_kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, n_rows, stream=None) -> None:
+    """Rows [0, n_rows[i]) of block src_blocks[i] -> block dst_blocks[i], both
+    caches (the data half of copy-on-write); int32 device vectors."""
+    _check_caches(k_cache, v_cache)
+    L = layout_of(k_cache)
+    n = src_blocks.shape[0]
+    for t, name in ((src_blocks, "src_blocks"), (dst_blocks, "dst_blocks"), (n_rows, "n_rows")):
+        if t.dim() != 1 or t.shape[0] != n:
+            raise ValueError("src_blocks, dst_blocks and n_rows must be equal-length vectors (%s)" % name)
+    _check(lib().paged_kv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L),
+                                      _i32(src_blocks, "src_blocks"), _i32(dst_blocks, "dst_blocks"),
+                                      _i32(n_rows, "n_rows"), n, _stream(stream, k_cache.device)),
+           "paged_kv_copy_blocks")
+
+
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
     _check_caches(k_cache, v_cache)
     L = layout_of(k_cache)
@@ -255,6 +272,15 @@ def validate(layout: Layout, block_tables: np.ndarray, context_lens: np.ndarray,
            "pkv_validate")
 
 
+def validate_copies(layout: Layout, src_blocks, dst_blocks, n_rows) -> None:
+    """Host-side check of a copy_blocks batch (numpy int32 vectors)."""
+    a = [np.ascontiguousarray(x, dtype=np.int32) for x in (src_blocks, dst_blocks, n_rows)]
+    if any(x.ndim != 1 or x.shape != a[0].shape for x in a):
+        raise ValueError("src_blocks, dst_blocks and n_rows must be equal-length vectors")
+    _check(lib().pkv_validate_copies(ctypes.byref(layout), *[ctypes.c_void_p(x.ctypes.data) for x in a],
+                                     a[0].shape[0]), "pkv_validate_copies")
+
+
 def probe_read(buf, sink, stream=None) -> None:
     _check(lib().pkv_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
                                 _stream(stream, buf.device)), "pkv_probe_read")
@@ -279,6 +305,9 @@ class PagedKVCache:
 
     def append(self, k_new, v_new, block_tables, positions, stream=None) -> None:
         paged_kv_append(k_new, v_new, self.k_cache, self.v_cache, block_tables, positions, stream)
+
+    def copy_blocks(self, src_blocks, dst_blocks, n_rows, stream=None) -> None:
+        paged_kv_copy_blocks(self.k_cache, self.v_cache, src_blocks, dst_blocks, n_rows, stream)
 
     def decode(self, q, block_tables, context_lens, scale, out, **kw) -> None:
         paged_attention_decode(q, self.k_cache, self.v_cache, block_tables, context_lens, scale, out, **kw)

@@ -17,13 +17,16 @@ Semantics follow the two allocators on the pages:
 
 Unlike the pages' counter simulation, ``copy_on_write`` here reports the block
 whose rows the caller must copy (the simulation allocates without copying any
-data); copying the rows is the caller's job.
+data); copying the rows is the caller's job.  ``Sequence`` queues each such copy
+as (source block, private block, rows already written); ``take_copies`` hands
+the queue to the caller, who runs them (``paged_kv_copy_blocks``) before the
+append that triggered them.
 
 This module does bookkeeping only; it never touches device memory.
 """
 from __future__ import annotations
 
-from typing import Iterable, List, Optional
+from typing import Iterable, List, Optional, Tuple
 
 
 class OutOfBlocks(RuntimeError):
@@ -128,6 +131,7 @@ class Sequence:
         self.table: List[int] = []
         self.n_tokens = 0
         self.last_cow: Optional[tuple] = None  # (src, dst) of the latest private copy
+        self.pending_copies: List[Tuple[int, int, int]] = []  # (src, dst, rows) not yet run
 
     def append_tokens(self, n: int) -> None:
         """Grow by ``n`` tokens: a new block when the current one is full, a
@@ -142,8 +146,15 @@ class Sequence:
                 new = self.alloc.copy_on_write(old)
                 if new != old:
                     self.last_cow = (old, new)
+                    # rows 0 .. offset-1 hold this sequence's tokens already
+                    self.pending_copies.append((old, new, offset))
                 self.table[last] = new
             self.n_tokens += 1
+
+    def take_copies(self) -> List[Tuple[int, int, int]]:
+        """The queued (src, dst, rows) block copies, oldest first; clears the queue."""
+        out, self.pending_copies = self.pending_copies, []
+        return out
 
     def fork(self, name: str) -> "Sequence":
         """Same tokens, shared blocks (parallel sampling, shared prompts)."""

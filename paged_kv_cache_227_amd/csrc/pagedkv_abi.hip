@@ -1,8 +1,8 @@
 // pagedkv_abi.hip -- the C ABI declared in include/pagedkv.h: argument
 // checks, dtype / head_dim / group dispatch, split-K planning, the library's
 // workspace, status codes and the per-thread error message.  Host code only;
-// every step of the decode path runs in the kernels of append.hip and
-// decode.hip.
+// every step of the decode path runs in the kernels of append.hip,
+// copy_blocks.hip and decode.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -262,6 +262,31 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_cache, 
     return ok();
 }
 
+pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_layout* layout,
+                                const int32_t* src_blocks, const int32_t* dst_blocks, const int32_t* n_rows,
+                                int32_t n_copies, void* stream) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (n_copies < 0) return fail(PKV_EINVAL, "n_copies %d < 0", n_copies);
+    if (n_copies == 0) return ok();
+    if (!k_cache || !v_cache || !src_blocks || !dst_blocks || !n_rows)
+        return fail(PKV_EINVAL, "a required pointer is NULL");
+    pkv::CopyParams p{};
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.src_blocks = src_blocks;
+    p.dst_blocks = dst_blocks;
+    p.n_rows = n_rows;
+    p.num_blocks = layout->num_blocks;
+    p.block_size = layout->block_size;
+    p.n_copies = n_copies;
+    p.row_bytes = (int64_t)layout->n_kv_heads * layout->head_dim * elt_bytes(layout->dtype);
+    hipError_t e = pkv::launch_copy_blocks(p, static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidConfiguration) return fail(PKV_EINVAL, "%d copies exceed the launch grid", n_copies);
+    if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+    return ok();
+}
+
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks_per_seq,
                                       const pkv_layout* layout, int32_t part_tokens) {
     if (check_layout(layout) != PKV_OK || num_seqs < 0 || n_q_heads < 1 || max_blocks_per_seq < 1) return 0;
@@ -415,6 +440,34 @@ pkv_status pkv_validate(const pkv_layout* layout, const int32_t* block_tables, i
             if (sorted[i] == sorted[i - 1])
                 return fail(PKV_EINVAL, "two sequences append to slot %lld", (long long)sorted[i]);
     }
+    return PKV_OK;
+}
+
+pkv_status pkv_validate_copies(const pkv_layout* layout, const int32_t* src_blocks, const int32_t* dst_blocks,
+                               const int32_t* n_rows, int32_t n_copies) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (n_copies < 0) return fail(PKV_EINVAL, "n_copies %d < 0", n_copies);
+    if (n_copies > 0 && (!src_blocks || !dst_blocks || !n_rows)) return fail(PKV_EINVAL, "a required pointer is NULL");
+    std::vector<int32_t> dsts, srcs;
+    for (int32_t i = 0; i < n_copies; ++i) {
+        if (src_blocks[i] < 0 || src_blocks[i] >= layout->num_blocks || dst_blocks[i] < 0 ||
+            dst_blocks[i] >= layout->num_blocks)
+            return fail(PKV_EOOB, "copy %d: block %d -> %d outside [0, %d)", i, src_blocks[i], dst_blocks[i],
+                        layout->num_blocks);
+        if (n_rows[i] < 0 || n_rows[i] > layout->block_size)
+            return fail(PKV_EOOB, "copy %d: %d rows outside [0, %d]", i, n_rows[i], layout->block_size);
+        if (n_rows[i] == 0) continue;  // moves nothing, so overlaps nothing
+        dsts.push_back(dst_blocks[i]);
+        srcs.push_back(src_blocks[i]);
+    }
+    std::sort(dsts.begin(), dsts.end());
+    std::sort(srcs.begin(), srcs.end());
+    for (size_t i = 1; i < dsts.size(); ++i)
+        if (dsts[i] == dsts[i - 1]) return fail(PKV_EINVAL, "two copies write block %d", dsts[i]);
+    for (int32_t d : dsts)
+        if (std::binary_search(srcs.begin(), srcs.end(), d))
+            return fail(PKV_EINVAL, "block %d is both a copy's source and a copy's target", d);
     return PKV_OK;
 }
 

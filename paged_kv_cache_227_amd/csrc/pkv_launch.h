@@ -21,6 +21,19 @@ struct AppendParams {
     int32_t row_bytes;  // n_kv_heads * head_dim * element bytes
 };
 
+struct CopyParams {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* src_blocks;
+    const int32_t* dst_blocks;
+    const int32_t* n_rows;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t n_copies;
+    int32_t chunks;     // workgroups per copy (set by the launcher)
+    int64_t row_bytes;  // n_kv_heads * head_dim * element bytes
+};
+
 // The flat schedule's grid never has more waves than this; its workspace is
 // sized for it.
 constexpr int kMaxFlatWorkers = 8192;
@@ -58,6 +71,7 @@ struct DecodeParams {
 
 // Each returns hipSuccess or the launch error.  dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int group,
                                     hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, int group, hipStream_t stream);

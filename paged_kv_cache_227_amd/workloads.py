@@ -272,14 +272,23 @@ def llama2_7b(seed: int = SEED_BASE + 2) -> Workload:
 
     Reading: if the draw does not fit the pool, redraw with the next seed
     (the seed actually used is recorded)."""
+    lens, s = _llama_lengths_and_seed(seed)
+    return build("llama2_7b", lens, 32, 32, 128, "f16", s, num_blocks=5120,
+                 data_mult=1.0 / math.sqrt(128.0))
+
+
+def _llama_lengths_and_seed(seed: int):
     s = seed
     while True:
         lens = _lens_rng(s).integers(128, 2048, size=64, endpoint=True)
         if sum(-(-int(L) // BLOCK_SIZE) for L in lens) <= 5120:
-            break
+            return lens, s
         s += 1000
-    return build("llama2_7b", lens, 32, 32, 128, "f16", s, num_blocks=5120,
-                 data_mult=1.0 / math.sqrt(128.0))
+
+
+def llama2_7b_lengths(seed: int = SEED_BASE + 2) -> np.ndarray:
+    """The Llama-2-7B configuration's 64 context lengths (without drawing data)."""
+    return _llama_lengths_and_seed(seed)[0]
 
 
 def gqa_8b(seed: int = SEED_BASE + 3) -> Workload:
@@ -322,6 +331,76 @@ CONFIGS = {
     "prefix_shared": lambda: prefix_sharing("shared"),
     "prefix_copied": lambda: prefix_sharing("copied"),
     "long_context": long_context,
+}
+
+
+# --------------------------------------------------------------------------
+# Block copies (copy-on-write, whole-block moves)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class CopyWorkload:
+    """A batch of block copies on one layer's caches: rows [0, rows[i]) of block
+    src[i] to block dst[i], both caches.  Cache contents do not matter for
+    timing; tests draw their own."""
+    name: str
+    dtype: str
+    n_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    src: np.ndarray   # int32 [n]
+    dst: np.ndarray   # int32 [n]
+    rows: np.ndarray  # int32 [n]
+    seed: int
+    notes: str = ""
+
+    @property
+    def row_bytes(self) -> int:
+        return self.n_kv_heads * self.head_dim * ELT_BYTES[self.dtype]
+
+    def moved_bytes(self) -> int:
+        """Bytes read (= bytes written) by one call: both caches."""
+        return 2 * int(np.sum(self.rows, dtype=np.int64)) * self.row_bytes
+
+
+def cow_llama2_7b(samples: int = 4, seed: int = SEED_BASE + 2) -> CopyWorkload:
+    """One fork wave of parallel sampling on the Llama-2-7B layer: each of the
+    64 sequences (lengths as in the Llama-2-7B configuration) is forked into
+    `samples` samples, and each sample's first generated token copies the
+    shared last block's filled rows (L mod 16 of them) into a private block.
+    The host block manager decides every block; the pool is 5,120 blocks plus
+    one per sample, in seeded shuffled order."""
+    base = llama2_7b_lengths(seed)
+    n_pool = 5120 + samples * len(base)
+    order = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7]))).permutation(n_pool)
+    alloc = BlockAllocator(n_pool, BLOCK_SIZE, free_order=order)
+    copies = []
+    for L in base:
+        prompt = Sequence("p", alloc)
+        prompt.append_tokens(int(L))
+        for i in range(samples):
+            child = prompt.fork("s%d" % i)
+            child.append_tokens(1)
+            copies += child.take_copies()
+    src, dst, rows = (np.array(x, np.int32) for x in zip(*copies))
+    return CopyWorkload("cow_llama2_7b", "f16", 32, 128, BLOCK_SIZE, n_pool, src, dst, rows, seed,
+                        notes="%d sequences x %d samples; sequences with L mod 16 = 0 need no copy"
+                              % (len(base), samples))
+
+
+def copy_whole_llama2_7b(n: int = 2048, seed: int = SEED_BASE + 6) -> CopyWorkload:
+    """`n` whole-block copies (16 rows x 8 KiB per cache) in the Llama-2-7B
+    layer's 5,120-block pool: distinct sources and targets in seeded order."""
+    perm = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 8]))).permutation(5120)
+    return CopyWorkload("copy_whole_llama2_7b", "f16", 32, 128, BLOCK_SIZE, 5120,
+                        perm[:n].astype(np.int32), perm[n:2 * n].astype(np.int32),
+                        np.full(n, BLOCK_SIZE, np.int32), seed)
+
+
+COPY_CONFIGS = {
+    "cow_llama2_7b": cow_llama2_7b,
+    "copy_whole_llama2_7b": copy_whole_llama2_7b,
 }
 
 

@@ -84,3 +84,12 @@ def max_err(gpu_out, ref_out, seq_ids=None):
         g, ref_out = g[seq_ids], ref_out[seq_ids]
     assert np.all(np.isfinite(g)), "GPU output holds NaN/inf"
     return float(np.max(np.abs(g - ref_out)))
+
+
+def dev_storage(a, dtype, device="cuda"):
+    """A storage array (float32, or uint16 bits of f16 / bf16) as a device tensor of that dtype."""
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype != "f32":
+        x = x.view(torch.int16).view({"f16": torch.float16, "bf16": torch.bfloat16}[dtype])
+    return x.to(device)

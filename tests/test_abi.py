@@ -128,3 +128,35 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         P.paged_kv_append(torch.zeros(1, 2, 64), torch.zeros(1, 2, 64), kc, kc.clone(),
                           torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+
+
+def test_copy_blocks_rejects(L):
+    lay = _layout()
+    args = [FAKE, FAKE, ctypes.byref(lay), FAKE, FAKE, FAKE, 3, None]
+    assert L.paged_kv_copy_blocks(*args[:2], None, *args[3:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_copy_blocks(None, *args[1:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_copy_blocks(*args[:5], None, *args[6:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_copy_blocks(*args[:6], -1, None) == _lib.PKV_EINVAL
+    bad = _layout(dtype=9)
+    assert L.paged_kv_copy_blocks(*args[:2], ctypes.byref(bad), *args[3:]) == _lib.PKV_EINVAL
+    # nothing to copy: OK without touching the GPU
+    assert L.paged_kv_copy_blocks(*args[:6], 0, None) == _lib.PKV_OK
+
+
+def test_validate_copies(L):
+    lay = _layout(num_blocks=10, block_size=16)
+    _lib.validate_copies(lay, [5, 5, 5, 5], [6, 7, 8, 9], [10, 10, 10, 10])   # the pages' fork
+    _lib.validate_copies(lay, [], [], [])
+    _lib.validate_copies(lay, [1, 2], [3, 3], [4, 0])          # an empty copy overlaps nothing
+    with pytest.raises(ValueError, match="outside"):
+        _lib.validate_copies(lay, [5], [10], [1])
+    with pytest.raises(ValueError, match="rows"):
+        _lib.validate_copies(lay, [5], [6], [17])
+    with pytest.raises(ValueError, match="rows"):
+        _lib.validate_copies(lay, [5], [6], [-1])
+    with pytest.raises(ValueError, match="two copies"):
+        _lib.validate_copies(lay, [1, 2], [3, 3], [4, 4])
+    with pytest.raises(ValueError, match="source"):
+        _lib.validate_copies(lay, [1, 3], [3, 4], [4, 4])
+    with pytest.raises(ValueError, match="equal-length"):
+        _lib.validate_copies(lay, [1, 2], [3], [4])

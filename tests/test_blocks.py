@@ -40,10 +40,15 @@ def test_fork_copy_on_write_and_refcount_guard():
     assert saved * B * 512 / 1024 == float(g["saved_mib"][0][0])  # 512 KiB per token
     for i, s in enumerate(samples):
         s.append_tokens(1)
+    n_prompt = ints(g["prompt_tokens"][0])[0]
     for row in g["sample_table"]:
         r = ints(row)
         assert samples[r[0]].table == r[1:]
         assert samples[r[0]].last_cow is not None  # copy-on-write triggered
+        # the data half the caller must run: the shared last block's filled rows
+        assert samples[r[0]].take_copies() == [(parent.table[-1], r[-1], n_prompt % B)]
+        assert samples[r[0]].take_copies() == []
+    assert parent.take_copies() == []
     assert alloc.n_blocks - alloc.n_free == ints(g["blocks_used_after_diverge"][0])[0]
     samples[0].release()
     assert alloc.refcount(0) == ints(g["refcount_block0_after_release_sample0"][0])[0]
