@@ -410,6 +410,127 @@ int ref_attention_decode(const void* q, const void* k_cache, const void* v_cache
     return REF_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Chunked prefill ("How a serving engine actually works", section "Prefill  */
+/* and decode are two different jobs": a long prompt is processed a slice at */
+/* a time; "Paged Attention and the Block Manager", section "The build":     */
+/* the table grows by as many blocks as n new tokens need).  A sequence whose */
+/* cache holds L tokens after this step received its last n of them in the   */
+/* step: they are written at positions L-n .. L-1, and the query of token j  */
+/* of the chunk (position L-n+j) attends to positions 0 .. L-n+j -- the whole */
+/* earlier context and the chunk up to itself.  n = 1 is a decode step.      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * n-token append: rows cu_new[s] .. cu_new[s+1]-1 of k_new / v_new
+ * ([total][n_kv_heads][head_dim]) go to the slots of positions start_pos[s],
+ * start_pos[s] + 1, ... of sequence s.  Raw bits are copied; nothing else in
+ * the caches changes.  Every position and block is checked before anything
+ * is written.
+ */
+int ref_append_tokens(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      int32_t num_blocks, int32_t block_size, int32_t n_kv_heads, int32_t head_dim,
+                      int dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* cu_new, const int32_t* start_pos, int32_t num_seqs) {
+    const int esz = ref_elt_size(dtype);
+    if (esz == 0 || block_size < 1 || n_kv_heads < 1 || head_dim < 1 || num_seqs < 0 || cu_new[0] != 0)
+        return REF_EINVAL;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        if (cu_new[s + 1] < cu_new[s] || start_pos[s] < 0) return REF_EINVAL;
+        const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+        for (int32_t j = cu_new[s]; j < cu_new[s + 1]; ++j) {
+            const int64_t p = (int64_t)start_pos[s] + (j - cu_new[s]);
+            if (p / block_size >= max_blocks_per_seq) return REF_EINVAL;
+            const int64_t slot = ref_physical_slot(row, block_size, p);
+            if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return REF_EINVAL;
+        }
+    }
+    const int64_t row_bytes = (int64_t)n_kv_heads * head_dim * esz;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+        for (int32_t j = cu_new[s]; j < cu_new[s + 1]; ++j) {
+            const int64_t slot = ref_physical_slot(row, block_size, (int64_t)start_pos[s] + (j - cu_new[s]));
+            memcpy((char*)k_cache + slot * row_bytes, (const char*)k_new + j * row_bytes, row_bytes);
+            memcpy((char*)v_cache + slot * row_bytes, (const char*)v_new + j * row_bytes, row_bytes);
+        }
+    }
+    return REF_OK;
+}
+
+/*
+ * One query row: q at element qoff ([D]), KV head g of sequence s, keys at
+ * positions 0 .. n_keys-1; plain two-pass softmax in double.
+ */
+static void ref_prefill_one(const ref_problem* P, int32_t s, int64_t qoff, int32_t g, int32_t n_keys,
+                            double* z, double* out_row) {
+    const int32_t D = P->head_dim;
+    const int32_t* row = P->block_tables + (int64_t)s * P->max_blocks_per_seq;
+    double m = -INFINITY;
+    for (int32_t i = 0; i < n_keys; ++i) {
+        int64_t koff = ref_row_offset(ref_physical_slot(row, P->block_size, i), P->n_kv_heads, g, D);
+        double dot = 0.0;
+        for (int32_t d = 0; d < D; ++d)
+            dot += ref_load(P->q, qoff + d, P->dtype) * ref_load(P->k_cache, koff + d, P->dtype);
+        z[i] = P->scale * dot;
+        m = z[i] > m ? z[i] : m;
+    }
+    double sum_w = 0.0;
+    for (int32_t d = 0; d < D; ++d) out_row[d] = 0.0;
+    for (int32_t i = 0; i < n_keys; ++i) {
+        double w = exp(z[i] - m);
+        sum_w += w;
+        int64_t voff = ref_row_offset(ref_physical_slot(row, P->block_size, i), P->n_kv_heads, g, D);
+        for (int32_t d = 0; d < D; ++d) out_row[d] += w * ref_load(P->v_cache, voff + d, P->dtype);
+    }
+    for (int32_t d = 0; d < D; ++d) out_row[d] /= sum_w;
+}
+
+/*
+ * Prefill attention.  q, out: [total][n_q_heads][head_dim] (out in double),
+ * total = cu_q[num_seqs]; sequence s owns query rows cu_q[s] .. cu_q[s+1]-1,
+ * n_s of them, which are its last n_s tokens: row cu_q[s] + j sits at
+ * position L_s - n_s + j and attends to positions 0 .. L_s - n_s + j.
+ * Requires n_s <= L_s <= max_blocks_per_seq * block_size.  If row_ids is
+ * non-NULL only those n_rows query rows are computed (the others are left
+ * untouched), for sampled checks of large problems.
+ */
+int ref_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                          int32_t block_size, int32_t n_kv_heads, int32_t head_dim, int dtype,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                          double scale, const int32_t* row_ids, int32_t n_rows, double* out) {
+    ref_problem P = {q, k_cache, v_cache, block_size, n_kv_heads, head_dim, dtype,
+                     block_tables, max_blocks_per_seq, context_lens, n_q_heads, scale};
+    if (ref_check_problem(&P, num_seqs) != REF_OK || num_seqs < 0 || cu_q[0] != 0) return REF_EINVAL;
+    for (int32_t s = 0; s < num_seqs; ++s)
+        if (cu_q[s + 1] < cu_q[s] || cu_q[s + 1] - cu_q[s] > context_lens[s]) return REF_EINVAL;
+    const int64_t total = cu_q[num_seqs];
+    const int64_t n_sel = row_ids ? n_rows : total;
+    for (int64_t k = 0; k < n_sel; ++k)
+        if (row_ids && (row_ids[k] < 0 || row_ids[k] >= total)) return REF_EINVAL;
+    int32_t max_len = 1;
+    for (int32_t s = 0; s < num_seqs; ++s) max_len = context_lens[s] > max_len ? context_lens[s] : max_len;
+    const int32_t group = n_q_heads / n_kv_heads;
+
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * max_len);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t w = 0; w < n_sel * n_q_heads; ++w) {
+            const int64_t t = row_ids ? row_ids[w / n_q_heads] : w / n_q_heads;
+            const int32_t h = (int32_t)(w % n_q_heads);
+            int32_t s = 0;
+            while (cu_q[s + 1] <= t) ++s; /* the sequence owning query row t */
+            const int32_t n = cu_q[s + 1] - cu_q[s];
+            const int32_t pos = context_lens[s] - n + (int32_t)(t - cu_q[s]);
+            ref_prefill_one(&P, s, (t * n_q_heads + h) * head_dim, h / group, pos + 1, z,
+                            out + (t * n_q_heads + h) * head_dim);
+        }
+        free(z);
+    }
+    return REF_OK;
+}
+
 /* Number of OpenMP threads the oracle runs with (for reporting). */
 int ref_num_threads(void) {
 #ifdef _OPENMP

@@ -61,6 +61,11 @@ class Oracle:
         L.ref_gather.argtypes = [P, i32, i32, i32, ctypes.c_int, P, i32, P]
         L.ref_copy_blocks.argtypes = [P, P, i32, i32, i32, i32, ctypes.c_int, P, P, P, i32]
         L.ref_copy_blocks.restype = ctypes.c_int
+        L.ref_append_tokens.argtypes = [P, P, P, P, i32, i32, i32, i32, ctypes.c_int, P, i32, P, P, i32]
+        L.ref_append_tokens.restype = ctypes.c_int
+        L.ref_attention_prefill.argtypes = [P, P, P, i32, i32, i32, ctypes.c_int, P, i32, P, P, i32, i32, dbl,
+                                            P, i32, P]
+        L.ref_attention_prefill.restype = ctypes.c_int
         L.ref_gather.restype = ctypes.c_int
         L.ref_attention_decode.argtypes = [P, P, P, i32, i32, i32, ctypes.c_int, P, i32, P, i32,
                                            i32, dbl, P, i32, i32, P]
@@ -134,6 +139,42 @@ class Oracle:
                                     _ptr(n), s.shape[0])
         if rc:
             raise ValueError("ref_copy_blocks rejected its arguments (%d)" % rc)
+
+    def append_tokens(self, k_new, v_new, k_cache, v_cache, block_tables, cu_new, start_pos, dtype):
+        """In place: rows cu_new[s]..cu_new[s+1]-1 of k_new/v_new to positions start_pos[s], ..."""
+        for a in (k_new, v_new, k_cache, v_cache):
+            _check_store(a, dtype)
+        nb, B, Hkv, D = k_cache.shape
+        bt, cu, sp = _i32(block_tables), _i32(cu_new), _i32(start_pos)
+        S = sp.shape[0]
+        if cu.shape != (S + 1,) or k_new.shape != (int(cu[-1]), Hkv, D) or v_new.shape != k_new.shape:
+            raise ValueError("shape mismatch")
+        rc = self.L.ref_append_tokens(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), nb, B, Hkv, D,
+                                      dtype, _ptr(bt), bt.shape[1], _ptr(cu), _ptr(sp), S)
+        if rc:
+            raise ValueError("ref_append_tokens rejected its arguments (%d)" % rc)
+
+    def attention_prefill(self, q, k_cache, v_cache, block_tables, cu_q, context_lens, scale, dtype,
+                          row_ids=None):
+        """float64 [total][Hq][D] chunked-prefill attention (causal inside each chunk).
+        With row_ids, only those query rows are computed (the rest are NaN)."""
+        for a in (q, k_cache, v_cache):
+            _check_store(a, dtype)
+        nb, B, Hkv, D = k_cache.shape
+        bt, cu, lens = _i32(block_tables), _i32(cu_q), _i32(context_lens)
+        S = lens.shape[0]
+        total, Hq = q.shape[0], q.shape[1]
+        if cu.shape != (S + 1,) or int(cu[-1]) != total or q.shape[2] != D:
+            raise ValueError("shape mismatch")
+        out = np.full((total, Hq, D), np.nan)
+        ids = None if row_ids is None else _i32(row_ids)
+        rc = self.L.ref_attention_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), B, Hkv, D, dtype, _ptr(bt),
+                                          bt.shape[1], _ptr(cu), _ptr(lens), S, Hq, float(scale),
+                                          None if ids is None else _ptr(ids), 0 if ids is None else ids.shape[0],
+                                          _ptr(out))
+        if rc:
+            raise ValueError("ref_attention_prefill rejected its arguments (%d)" % rc)
+        return out
 
     def gather(self, cache, table_row, length, dtype):
         """Contiguous [Hkv][length][D] float64 copy of one sequence's cache."""
@@ -224,6 +265,14 @@ def append(*a, **k):
 
 def copy_blocks(*a, **k):
     return default().copy_blocks(*a, **k)
+
+
+def append_tokens(*a, **k):
+    return default().append_tokens(*a, **k)
+
+
+def attention_prefill(*a, **k):
+    return default().attention_prefill(*a, **k)
 
 
 def gather(*a, **k):

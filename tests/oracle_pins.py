@@ -443,4 +443,117 @@ def pin_copy_blocks_whole_and_empty(orc):
     assert np.array_equal(_bits(kc), _bits(snap)), "a rejected call wrote something"
 
 
+# ---------------------------------------------------------------------------
+# Chunked prefill
+# ---------------------------------------------------------------------------
+
+def _prefill_case(rng, dtype, Hq, Hkv, D, B, lens, chunk):
+    """A paged problem plus packed queries for each sequence's last chunk[s] tokens."""
+    p = random_problem(rng, dtype, len(lens), Hq, Hkv, D, B, lens)
+    cu = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q = to_storage(rng.standard_normal((int(cu[-1]), Hq, D)), dtype)
+    return p, q, cu
+
+
+def _sdpa_prefill(p, q, cu, scale, causal_flag=False):
+    """torch SDPA (float64, CPU) on the dense sequences, the chunk's queries being
+    the last n positions: query j may see key i iff i <= L - n + j."""
+    dtype = p["dtype"]
+    out = np.empty(q.shape)
+    for s in range(len(p["dense_k"])):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        n, L = hi - lo, len(p["dense_k"][s])
+        qs = torch.from_numpy(from_storage(q[lo:hi], dtype).transpose(1, 0, 2).copy())[None]   # [1,Hq,n,D]
+        k = torch.from_numpy(from_storage(p["dense_k"][s], dtype).transpose(1, 0, 2).copy())[None]
+        v = torch.from_numpy(from_storage(p["dense_v"][s], dtype).transpose(1, 0, 2).copy())[None]
+        if causal_flag:
+            assert n == L
+            o = torch.nn.functional.scaled_dot_product_attention(qs, k, v, scale=scale, is_causal=True,
+                                                                 enable_gqa=True)
+        else:
+            mask = torch.from_numpy(np.arange(L)[None, :] <= (L - n + np.arange(n))[:, None])
+            o = torch.nn.functional.scaled_dot_product_attention(qs, k, v, attn_mask=mask, scale=scale,
+                                                                 enable_gqa=True)
+        out[lo:hi] = o[0].numpy().transpose(1, 0, 2)
+    return out
+
+
+def pin_prefill_matches_masked_sdpa(orc):
+    rng = np.random.default_rng(51)
+    cases = [(F32, 4, 4, 16, 16, [5, 16, 17, 33], [5, 3, 17, 10]),
+             (BF16, 8, 2, 16, 4, [9, 20, 7], [4, 20, 1]),
+             (F16, 6, 3, 8, 16, [40, 33], [16, 1]),
+             (BF16, 8, 1, 16, 16, [70], [35])]
+    for dtype, Hq, Hkv, D, B, lens, chunk in cases:
+        p, q, cu = _prefill_case(rng, dtype, Hq, Hkv, D, B, lens, chunk)
+        got = orc.attention_prefill(q, p["k_cache"], p["v_cache"], p["block_tables"], cu, p["context_lens"],
+                                    0.3, dtype)
+        _close(got, _sdpa_prefill(p, q, cu, 0.3), 1e-12, "prefill vs masked SDPA (dtype %d)" % dtype)
+
+
+def pin_prefill_whole_prompt_is_causal(orc):
+    rng = np.random.default_rng(52)
+    p, q, cu = _prefill_case(rng, BF16, 4, 2, 16, 16, [37], [37])
+    got = orc.attention_prefill(q, p["k_cache"], p["v_cache"], p["block_tables"], cu, p["context_lens"], 0.25, BF16)
+    _close(got, _sdpa_prefill(p, q, cu, 0.25, causal_flag=True), 1e-12, "whole prompt vs causal SDPA")
+
+
+def pin_prefill_single_token_is_decode(orc):
+    """A one-token chunk is a decode step."""
+    rng = np.random.default_rng(53)
+    p, q, cu = _prefill_case(rng, F16, 8, 2, 16, 16, [5, 16, 17, 33], [1, 1, 1, 1])
+    got = orc.attention_prefill(q, p["k_cache"], p["v_cache"], p["block_tables"], cu, p["context_lens"], 0.4, F16)
+    want = orc.attention_decode(q, p["k_cache"], p["v_cache"], p["block_tables"], p["context_lens"], 0.4, F16)
+    _close(got, want, 1e-13, "one-token chunk vs decode")
+
+
+def pin_prefill_chunking_invariance(orc):
+    """A prompt prefilled in chunks (the context growing chunk by chunk) gives
+    every token the same output as one chunk holding the whole prompt."""
+    rng = np.random.default_rng(54)
+    L = 45
+    p, q, cu = _prefill_case(rng, BF16, 4, 2, 16, 16, [L], [L])
+    whole = orc.attention_prefill(q, p["k_cache"], p["v_cache"], p["block_tables"], cu, p["context_lens"],
+                                  0.3, BF16)
+    start = 0
+    for n in (16, 16, 13):
+        part = orc.attention_prefill(np.ascontiguousarray(q[start:start + n]), p["k_cache"], p["v_cache"],
+                                     p["block_tables"], np.array([0, n], np.int32),
+                                     np.array([start + n], np.int32), 0.3, BF16)
+        assert np.array_equal(part, whole[start:start + n]), "chunk at %d differs" % start
+        start += n
+
+
+def pin_append_tokens_builds_sequential_fill(orc):
+    """Appending each sequence's tokens in chunks of several tokens per call
+    builds the sequential-fill layout, and nothing else changes."""
+    rng = np.random.default_rng(55)
+    B, Hkv, D = 4, 2, 8
+    lens = [9, 14, 3]
+    need = [-(-L // B) for L in lens]
+    nb = sum(need) + 3
+    perm = rng.permutation(nb)
+    tables, off = [], 0
+    for n in need:
+        tables.append(perm[off:off + n])
+        off += n
+    bt = np.full((3, max(need)), -1, np.int32)
+    for s, t in enumerate(tables):
+        bt[s, :len(t)] = t
+    rows = [to_storage(rng.standard_normal((L, Hkv, D)), F16) for L in lens]
+    want = _poisoned_pool((nb, B, Hkv, D), F16)
+    for s in range(3):
+        sequential_fill(want, tables[s], rows[s])
+    kc, vc = _poisoned_pool((nb, B, Hkv, D), F16), _poisoned_pool((nb, B, Hkv, D), F16)
+    done = [0, 0, 0]
+    for step in ([4, 5, 1], [5, 9, 2], [0, 0, 0]):
+        n = [min(a, L - d) for a, L, d in zip(step, lens, done)]
+        cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        kn = np.ascontiguousarray(np.concatenate([rows[s][done[s]:done[s] + n[s]] for s in range(3)]))
+        orc.append_tokens(kn, kn.copy(), kc, vc, bt, cu, np.array(done, np.int32), F16)
+        done = [d + k for d, k in zip(done, n)]
+    assert done == lens
+    assert np.array_equal(_bits(kc), _bits(want)) and np.array_equal(_bits(vc), _bits(want)), "n-token append"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

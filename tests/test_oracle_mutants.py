@@ -70,6 +70,19 @@ MUTANTS = [
      "const int64_t to = (int64_t)dst[i] + r;"),
     ("copy moves whole blocks whatever n_rows", "for (int32_t r = 0; r < n_rows[i]; ++r) {",
      "for (int32_t r = 0; r < (n_rows[i] ? block_size : 0); ++r) {"),
+    ("prefill query misses its own key", "h / group, pos + 1, z,", "h / group, pos, z,"),
+    ("prefill query sees the whole chunk (no causal mask)", "h / group, pos + 1, z,",
+     "h / group, context_lens[s], z,"),
+    ("prefill position ignores the earlier context",
+     "const int32_t pos = context_lens[s] - n + (int32_t)(t - cu_q[s]);",
+     "const int32_t pos = (int32_t)(t - cu_q[s]);"),
+    ("prefill GQA: interleaved head mapping", "h / group, pos + 1, z,", "h % n_kv_heads, pos + 1, z,"),
+    ("n-token append ignores the start position",
+     "ref_physical_slot(row, block_size, (int64_t)start_pos[s] + (j - cu_new[s]));",
+     "ref_physical_slot(row, block_size, (int64_t)(j - cu_new[s]));"),
+    ("n-token append repeats the chunk's first row",
+     "memcpy((char*)k_cache + slot * row_bytes, (const char*)k_new + j * row_bytes, row_bytes);",
+     "memcpy((char*)k_cache + slot * row_bytes, (const char*)k_new + cu_new[s] * row_bytes, row_bytes);"),
 ]
 
 
