@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged-attn decode: KV-read GB/s (% of HBM peak), tokens/s at Llama-2-7B shape"
-KERNEL_SOURCES = ["paged_kv_cache_227_amd/csrc/decode.hip", "paged_kv_cache_227_amd/csrc/pkv_device.h"]
+KERNEL_SOURCES = ["paged_kv_cache_227_amd/csrc/decode.hip", "paged_kv_cache_227_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_227_amd/csrc/pkv_mfma.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{config}.json")
 
 
@@ -332,6 +333,124 @@ def main_copy(a):
     return 0
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+
+
+def run_prefill(w, steps, warmup):
+    """Time the chunked-prefill step (n-token append, then attention) on the
+    workload: `steps` steps between two synchronisations, then the same steps
+    with HIP events around each kernel."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_227_amd as P
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to("cuda:0")
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda:0")
+
+    kc, vc, q, kn, vn = (dev(a) for a in (w.k_cache, w.v_cache, w.q, w.k_new, w.v_new))
+    bt, cu, lens, sp = i32(w.block_tables), i32(w.cu_q), i32(w.context_lens), i32(w.start_pos)
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        P.paged_kv_append_tokens(kn, vn, kc, vc, bt, cu, sp)
+        if ev:
+            ev[1].record()
+        P.paged_attention_prefill(q, kc, vc, bt, cu, lens, w.scale, out, w.max_q_len)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        step(e)
+    torch.cuda.synchronize()
+    t_app = [e[0].elapsed_time(e[1]) for e in ev]
+    t_att = [e[1].elapsed_time(e[2]) for e in ev]
+    del kc, vc, q, kn, vn, out
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms_step, prefill_ms_mean=statistics.fmean(t_att),
+                prefill_ms_median=statistics.median(t_att), append_ms_mean=statistics.fmean(t_app))
+
+
+def cpu_baseline_prefill(w, budget_s=10.0):
+    """The oracle's prefill attention on sampled query rows (each sequence's
+    rows in turn, spread evenly) until budget_s is spent; flops per second of
+    the rows computed."""
+    import numpy as np
+    from oracle import ref
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    orc = ref.default()
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    orc.append_tokens(w.k_new, w.v_new, kc, vc, w.block_tables, w.cu_q, w.start_pos, w.dtype_code)
+    total = int(w.cu_q[-1])
+    order = np.random.default_rng(0).permutation(total)
+    seq_of = np.searchsorted(w.cu_q, np.arange(total), side="right") - 1
+    pos = w.start_pos[seq_of] + (np.arange(total) - w.cu_q[seq_of])
+    done, flops, elapsed = 0, 0, 0.0
+    batch = 64
+    while done < total and elapsed < budget_s:
+        ids = np.sort(order[done:done + batch])
+        t0 = time.perf_counter()
+        orc.attention_prefill(w.q, kc, vc, w.block_tables, w.cu_q, w.context_lens, w.scale, w.dtype_code,
+                              row_ids=ids)
+        elapsed += time.perf_counter() - t0
+        flops += int(np.sum(pos[ids] + 1)) * 4 * w.head_dim * w.n_q_heads
+        done += len(ids)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": "%d of %d query rows (all heads), %.1f s" % (done, total, elapsed)}
+
+
+def main_prefill(a):
+    from paged_kv_cache_227_amd import workloads as W
+    if a.config not in W.PREFILL_CONFIGS:
+        raise SystemExit("prefill workloads: %s" % ", ".join(W.PREFILL_CONFIGS))
+    w = W.PREFILL_CONFIGS[a.config]()
+    flops = w.attention_flops()
+    log("prefill workload %s: %d sequences, chunks %s, contexts %s, %.2f GFLOP" % (
+        w.name, w.num_seqs, list(w.chunk_lens), list(w.context_lens), flops / 1e9))
+    g = run_prefill(w, a.steps, a.warmup)
+    log("gpu: %.4f ms/step, prefill %.4f ms, append %.4f ms" % (g["ms_per_step"], g["prefill_ms_mean"],
+                                                                 g["append_ms_mean"]))
+    value = flops / (g["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (g["prefill_ms_mean"] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    res = {
+        "metric": "chunked prefill: attention TFLOP/s (causal flops of the step's chunks)", "value": round(value, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(g["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "chunk_lens": [int(x) for x in w.chunk_lens],
+                   "context_lens": [int(x) for x in w.context_lens], "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "attention_flops": flops, "seed": w.seed, "notes": w.notes},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "prefill_kernel",
+                     "algorithmic_flops_per_launch": flops,
+                     "timing": "HIP events around each launch, %d steps right after the timed region" % a.steps,
+                     "mean_launch_ms": round(g["prefill_ms_mean"], 5)},
+        "kernel_ms": {k: round(g[k], 5) for k in ("prefill_ms_mean", "prefill_ms_median", "append_ms_mean")},
+        "tokens_per_s": round(int(w.cu_q[-1]) / (g["ms_per_step"] * 1e-3), 1),
+        "kv_read_gbs": round(w.kv_bytes() / (g["prefill_ms_mean"] * 1e-3) / 1e9, 1),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(w)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def summarize_pmc(d):
     """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
     --pmc CSV output under directory d."""
@@ -390,8 +509,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks"],
-                    help="decode: the append + decode step (default); copy_blocks: the copy-on-write block copy")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "prefill"],
+                    help="decode: the append + decode step (default); copy_blocks: the copy-on-write block "
+                         "copy; prefill: the chunked-prefill step (n-token append + attention)")
     ap.add_argument("--config", default=None,
                     help="workload (default llama2_7b for decode, copy_whole_llama2_7b for copy_blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -407,7 +527,8 @@ def main():
                          "(a launch of known traffic for calibrating hardware counters)")
     a = ap.parse_args()
     if a.config is None:
-        a.config = "llama2_7b" if a.op == "decode" else "copy_whole_llama2_7b"
+        a.config = {"decode": "llama2_7b", "copy_blocks": "copy_whole_llama2_7b",
+                    "prefill": "prefill_llama2_7b"}[a.op]
 
     if a.summarize_pmc:
         print(json.dumps(summarize_pmc(a.summarize_pmc), indent=1))
@@ -439,6 +560,8 @@ def main():
         return 2
     if a.op == "copy_blocks":
         return main_copy(a)
+    if a.op == "prefill":
+        return main_prefill(a)
 
     t = time.perf_counter()
     w = make_workload(a.config)

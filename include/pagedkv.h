@@ -8,8 +8,9 @@
  *   decode  -- attention of each sequence's query over its cached keys and
  *              values, read in place through the block table;
  *
- * and the block copy that copy-on-write needs before an append into a block
- * that another sequence also holds.
+ * and, next to them, the block copy that copy-on-write needs before an append
+ * into a block that another sequence also holds, and the chunked-prefill pair
+ * (an n-token append and the attention of a chunk of queries).
  *
  * Append and decode use the address translation of "How a serving engine actually works"
  * (paperfordummies.in), section "The one formula":
@@ -106,6 +107,63 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_cache, 
                            const pkv_layout* layout, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* positions, int32_t num_seqs,
                            void* stream);
+
+/*
+ * Chunked prefill ("How a serving engine actually works", paperfordummies.in,
+ * section "Prefill and decode are two different jobs": a long prompt is
+ * processed one chunk per step; "Paged Attention and the Block Manager",
+ * snowch.github.io ch08, "The build": the host grows the table by the blocks
+ * n new tokens need).  Rows of several sequences are packed: sequence s owns
+ * rows cu[s] .. cu[s+1]-1 of a [total][heads][head_dim] array (cu[0] = 0,
+ * non-decreasing, total = cu[num_seqs]).
+ */
+
+/*
+ * paged_kv_append_tokens -- the n-token append.  For every s and every row
+ * x in [cu_new[s], cu_new[s+1]):
+ *     k_cache[slot(s, start_pos[s] + x - cu_new[s])] = k_new[x]   (and v)
+ * a bit-exact copy.  Nothing else in the caches changes.
+ *
+ *   k_new, v_new  [total_new][n_kv_heads][head_dim], element type layout->dtype
+ *   cu_new        [num_seqs + 1] int32 device array; total_new = cu_new[num_seqs]
+ *                 (passed by value too, to size the grid)
+ *   start_pos     [num_seqs] int32: position of each sequence's first new row
+ *   other arguments as for paged_kv_append (any block_size)
+ *
+ * Preconditions: target slots pairwise distinct; the table covers every
+ * position.  A row whose position or block lies outside its range is skipped.
+ */
+pkv_status paged_kv_append_tokens(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const pkv_layout* layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* cu_new, const int32_t* start_pos, int32_t num_seqs,
+                                  int32_t total_new, void* stream);
+
+/*
+ * paged_attention_prefill -- attention of a chunk's queries.  Sequence s holds
+ * L = context_lens[s] tokens in the cache, its chunk's n = cu_q[s+1] - cu_q[s]
+ * included as the last n (append them first).  Query row cu_q[s] + j sits at
+ * position L - n + j and attends to positions 0 .. L - n + j (the earlier
+ * context and the chunk up to itself); for query head h, KV head
+ * g = h / (n_q_heads / n_kv_heads):
+ *     out[cu_q[s] + j][h] = sum_{i <= L-n+j} softmax_i(scale * <q[cu_q[s]+j][h], K_i>) V_i
+ * accumulated in fp32, rounded to the cache dtype (round to nearest even).
+ * n = 1 gives the same value as paged_attention_decode.
+ *
+ *   q, out        [total][n_q_heads][head_dim], element type layout->dtype
+ *   cu_q          [num_seqs + 1] int32 device array
+ *   context_lens  [num_seqs] int32: n <= L <= max_blocks_per_seq * block_size
+ *   max_q_len     host int: the longest chunk (sizes the grid); rows of a
+ *                 longer chunk are not computed
+ *
+ * Supported: fp16 / bf16 caches, block_size 16, head_dim 64 or 128, group
+ * 1, 2, 4 or 8 (PKV_ENOTSUP otherwise; fp32 prefill is not served).  A
+ * sequence whose chunk is empty or longer than its context is skipped.
+ * pkv_validate_prefill() checks cu_q, the lengths and the tables on the host.
+ */
+pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* layout,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                                   int32_t n_q_heads, float scale, void* out, void* stream);
 
 /*
  * paged_kv_copy_blocks -- the data half of copy-on-write.
@@ -253,6 +311,16 @@ pkv_status pkv_validate(const pkv_layout* layout, const int32_t* block_tables,
  */
 pkv_status pkv_validate_copies(const pkv_layout* layout, const int32_t* src_blocks, const int32_t* dst_blocks,
                                const int32_t* n_rows, int32_t n_copies);
+
+/*
+ * pkv_validate_prefill -- host-side check of a prefill step (HOST pointers):
+ * cu_q starts at 0 and never decreases, every chunk fits max_q_len and its
+ * context (n <= L <= max_blocks_per_seq * block_size), and every table entry
+ * the context uses lies in the pool.  PKV_OK, PKV_EINVAL or PKV_EOOB.
+ */
+pkv_status pkv_validate_prefill(const pkv_layout* layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* cu_q, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_q_len);
 
 /* Message of this thread's last non-OK call ("" if none).  Owned by the library. */
 const char* pkv_last_error(void);

@@ -46,6 +46,9 @@ SIGNATURES = {
     "pkv_partition_tokens_for": (_I32, [_I32, _I32, _I32, _LP]),
     "pkv_validate": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _I32]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_P, _P, _LP, _P, _P, _P, _I32, _P]),
+    "paged_kv_append_tokens": (ctypes.c_int, [_P, _P, _P, _P, _LP, _P, _I32, _P, _P, _I32, _I32, _P]),
+    "paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _P, _I32, _I32, _I32, _F32, _P, _P]),
+    "pkv_validate_prefill": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _I32, _I32]),
     "pkv_validate_copies": (ctypes.c_int, [_LP, _P, _P, _P, _I32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
@@ -181,6 +184,50 @@ def paged_kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, n_rows, strea
            "paged_kv_copy_blocks")
 
 
+def paged_kv_append_tokens(k_new, v_new, k_cache, v_cache, block_tables, cu_new, start_pos, stream=None) -> None:
+    """Rows cu_new[s] .. cu_new[s+1]-1 of k_new / v_new ([total][Hkv][D]) into
+    the slots of positions start_pos[s], start_pos[s] + 1, ... (the n-token append)."""
+    _check_caches(k_cache, v_cache)
+    L = layout_of(k_cache)
+    S = start_pos.shape[0]
+    if cu_new.dim() != 1 or cu_new.shape[0] != S + 1:
+        raise ValueError("cu_new must be [num_seqs + 1]")
+    total = k_new.shape[0]
+    want = (total, L.n_kv_heads, L.head_dim)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+        raise ValueError("k_new / v_new must be [total][n_kv_heads][head_dim]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("k_new / v_new must have the cache dtype")
+    _check_tables(block_tables, start_pos, S, "start_pos")
+    _check(lib().paged_kv_append_tokens(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"),
+                                        _dev(v_cache, "v_cache"), ctypes.byref(L),
+                                        _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                        _i32(cu_new, "cu_new"), _i32(start_pos, "start_pos"), S, total,
+                                        _stream(stream, k_cache.device)), "paged_kv_append_tokens")
+
+
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, cu_q, context_lens, scale, out, max_q_len,
+                            stream=None) -> None:
+    """out[cu_q[s] + j][h] = attention of that query (position L_s - n_s + j)
+    over positions 0 .. L_s - n_s + j of sequence s, read through its table.
+    q and out are [total][n_q_heads][head_dim]; max_q_len is the longest chunk."""
+    _check_caches(k_cache, v_cache)
+    L = layout_of(k_cache)
+    if q.dim() != 3 or q.shape[2] != L.head_dim:
+        raise ValueError("q must be [total][n_q_heads][head_dim]")
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must have the cache dtype and equal shapes")
+    S = context_lens.shape[0]
+    if cu_q.dim() != 1 or cu_q.shape[0] != S + 1:
+        raise ValueError("cu_q must be [num_seqs + 1]")
+    _check_tables(block_tables, context_lens, S, "context_lens")
+    _check(lib().paged_attention_prefill(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                         ctypes.byref(L), _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                         _i32(cu_q, "cu_q"), _i32(context_lens, "context_lens"), S, int(max_q_len),
+                                         q.shape[1], float(scale), _dev(out, "out"), _stream(stream, q.device)),
+           "paged_attention_prefill")
+
+
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
     _check_caches(k_cache, v_cache)
     L = layout_of(k_cache)
@@ -281,6 +328,18 @@ def validate_copies(layout: Layout, src_blocks, dst_blocks, n_rows) -> None:
                                      a[0].shape[0]), "pkv_validate_copies")
 
 
+def validate_prefill(layout: Layout, block_tables, cu_q, context_lens, max_q_len) -> None:
+    """Host-side check of a prefill step (numpy int32 arrays)."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_q, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.ndim != 2 or lens.shape != (bt.shape[0],) or cu.shape != (bt.shape[0] + 1,):
+        raise ValueError("block_tables [S][max_blocks], cu_q [S + 1], context_lens [S]")
+    _check(lib().pkv_validate_prefill(ctypes.byref(layout), ctypes.c_void_p(bt.ctypes.data), bt.shape[1],
+                                      ctypes.c_void_p(cu.ctypes.data), ctypes.c_void_p(lens.ctypes.data),
+                                      bt.shape[0], int(max_q_len)), "pkv_validate_prefill")
+
+
 def probe_read(buf, sink, stream=None) -> None:
     _check(lib().pkv_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(sink, "sink"),
                                 _stream(stream, buf.device)), "pkv_probe_read")
@@ -305,6 +364,13 @@ class PagedKVCache:
 
     def append(self, k_new, v_new, block_tables, positions, stream=None) -> None:
         paged_kv_append(k_new, v_new, self.k_cache, self.v_cache, block_tables, positions, stream)
+
+    def append_tokens(self, k_new, v_new, block_tables, cu_new, start_pos, stream=None) -> None:
+        paged_kv_append_tokens(k_new, v_new, self.k_cache, self.v_cache, block_tables, cu_new, start_pos, stream)
+
+    def prefill(self, q, block_tables, cu_q, context_lens, scale, out, max_q_len, stream=None) -> None:
+        paged_attention_prefill(q, self.k_cache, self.v_cache, block_tables, cu_q, context_lens, scale, out,
+                                max_q_len, stream)
 
     def copy_blocks(self, src_blocks, dst_blocks, n_rows, stream=None) -> None:
         paged_kv_copy_blocks(self.k_cache, self.v_cache, src_blocks, dst_blocks, n_rows, stream)

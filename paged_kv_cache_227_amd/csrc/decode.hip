@@ -37,9 +37,11 @@
 //     the length mix.  Segments are cut where a range ends; segment (pair j,
 //     wave w) keeps its record at index j + w, unique because j + w grows by
 //     at least one from one segment to the next.
-//   * fixed partitions: one workgroup per (P-token partition, KV head,
-//     sequence); its waves share the partition's blocks and combine through
-//     LDS.
+//   * fixed partitions: one wave per (P-token partition, head group,
+//     sequence), NW consecutive partitions of one sequence per workgroup;
+//     each wave writes its partition's record (or the output, for a
+//     sequence with one partition) and a workgroup per (sequence, query head)
+//     merges the records.
 //
 // Everything is bound by HBM bandwidth: each (token, KV head) costs
 // 2 * head_dim * element bytes of reads and 4 * head_dim * G flops.
@@ -49,6 +51,7 @@
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_mfma.h"
 
 namespace pkv {
 
@@ -274,59 +277,6 @@ struct WaveAttn {
 // sum hi + lo of two 16-bit values, so the product keeps ~16 bits of P.
 // ----------------------------------------------------------------------------
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-template <class E>
-struct MfmaOps;
-
-template <>
-struct MfmaOps<BF16> {
-    typedef __bf16 v8_t __attribute__((ext_vector_type(8)));
-    typedef __bf16 tr_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
-    typedef s16x4_t op4_t;
-    __device__ static __forceinline__ f32x4_t qk(const Vec16& a, const Vec16& b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8_t, a), __builtin_bit_cast(v8_t, b), c, 0,
-                                                       0, 0);
-    }
-    __device__ static __forceinline__ op4_t read_tr(const char* p) {
-        auto q = (__attribute__((address_space(3))) tr_t*)((__attribute__((address_space(3))) char*)(p));
-        return __builtin_bit_cast(op4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q));
-    }
-    __device__ static __forceinline__ f32x4_t pv(op4_t a, op4_t b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-    }
-    __device__ static __forceinline__ void split(float x, short& hi, short& lo) {
-        const __bf16 h = (__bf16)x;
-        hi = __builtin_bit_cast(short, h);
-        lo = __builtin_bit_cast(short, (__bf16)(x - (float)h));
-    }
-};
-
-template <>
-struct MfmaOps<F16> {
-    typedef _Float16 v8_t __attribute__((ext_vector_type(8)));
-    typedef _Float16 v4h_t __attribute__((ext_vector_type(4)));
-    typedef __fp16 tr_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
-    typedef v4h_t op4_t;
-    __device__ static __forceinline__ f32x4_t qk(const Vec16& a, const Vec16& b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8_t, a), __builtin_bit_cast(v8_t, b), c, 0, 0,
-                                                      0);
-    }
-    __device__ static __forceinline__ op4_t read_tr(const char* p) {
-        auto q = (__attribute__((address_space(3))) tr_t*)((__attribute__((address_space(3))) char*)(p));
-        return __builtin_bit_cast(op4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16(q));
-    }
-    __device__ static __forceinline__ f32x4_t pv(op4_t a, op4_t b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-    }
-    __device__ static __forceinline__ void split(float x, short& hi, short& lo) {
-        const _Float16 h = (_Float16)x;
-        hi = __builtin_bit_cast(short, h);
-        lo = __builtin_bit_cast(short, (_Float16)(x - (float)h));
-    }
-};
-
 template <class E, int D, int G, class TU>
 struct MfmaAttn {
     static constexpr int NH = TU::NH;            // adjacent KV heads per wave
@@ -358,17 +308,6 @@ struct MfmaAttn {
 
     __device__ __forceinline__ static uint32_t lds_pos(int row, int head, int chunk) {
         return (uint32_t)(row * ROW + head * RB + ((chunk ^ (row % CH)) * 16));
-    }
-    __device__ __forceinline__ static void lds_store16(char* base, uint32_t off, const Vec16& v) {
-        typedef __attribute__((address_space(3))) v4u32_t lds_v4;
-        typedef __attribute__((address_space(3))) char lds_c;
-        *(lds_v4*)((lds_c*)base + off) = v4u32_t{v.w[0], v.w[1], v.w[2], v.w[3]};
-    }
-    __device__ __forceinline__ static Vec16 lds_load16(const char* base, uint32_t off) {
-        typedef const __attribute__((address_space(3))) v4u32_t lds_v4;
-        typedef const __attribute__((address_space(3))) char lds_c;
-        const v4u32_t u = *(lds_v4*)((lds_c*)base + off);
-        return Vec16{{u.x, u.y, u.z, u.w}};
     }
 
     __device__ __forceinline__ void init(int lane, uint32_t row_stride, char* lds_wave) {

@@ -1,8 +1,8 @@
 // pagedkv_abi.hip -- the C ABI declared in include/pagedkv.h: argument
 // checks, dtype / head_dim / group dispatch, split-K planning, the library's
 // workspace, status codes and the per-thread error message.  Host code only;
-// every step of the decode path runs in the kernels of append.hip,
-// copy_blocks.hip and decode.hip.
+// every step of the path runs in the kernels of append.hip, copy_blocks.hip,
+// decode.hip and prefill.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -287,6 +287,84 @@ pkv_status paged_kv_copy_blocks(void* k_cache, void* v_cache, const pkv_layout* 
     return ok();
 }
 
+pkv_status paged_kv_append_tokens(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const pkv_layout* layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* cu_new, const int32_t* start_pos, int32_t num_seqs,
+                                  int32_t total_new, void* stream) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || total_new < 0)
+        return fail(PKV_EINVAL, "num_seqs %d or total_new %d < 0", num_seqs, total_new);
+    if (max_blocks_per_seq < 1) return fail(PKV_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+    if (num_seqs == 0 || total_new == 0) return ok();
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !cu_new || !start_pos)
+        return fail(PKV_EINVAL, "a required pointer is NULL");
+    pkv::AppendTokensParams p{};
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.cu_new = cu_new;
+    p.start_pos = start_pos;
+    p.num_blocks = layout->num_blocks;
+    p.block_size = layout->block_size;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_seqs = num_seqs;
+    p.total = total_new;
+    p.row_bytes = layout->n_kv_heads * layout->head_dim * elt_bytes(layout->dtype);
+    hipError_t e = pkv::launch_append_tokens(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "append_tokens launch");
+    return ok();
+}
+
+pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* layout,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                                   int32_t n_q_heads, float scale, void* out, void* stream) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || max_q_len < 0) return fail(PKV_EINVAL, "num_seqs %d or max_q_len %d < 0", num_seqs, max_q_len);
+    if (max_blocks_per_seq < 1) return fail(PKV_EINVAL, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+    if (n_q_heads < 1 || n_q_heads % layout->n_kv_heads != 0)
+        return fail(PKV_EINVAL, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads,
+                    layout->n_kv_heads);
+    if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+    if ((int64_t)max_blocks_per_seq * layout->block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "max_blocks_per_seq * block_size overflows int32");
+    if (num_seqs > 0 && max_q_len > 0 && (!q || !k_cache || !v_cache || !block_tables || !cu_q || !context_lens || !out))
+        return fail(PKV_EINVAL, "a required pointer is NULL");
+    if (layout->block_size != kGpuBlockSize)
+        return fail(PKV_ENOTSUP, "the GPU path serves block_size %d only (got %d)", kGpuBlockSize,
+                    layout->block_size);
+    const int group = n_q_heads / layout->n_kv_heads;
+    if (!pkv::prefill_supported(layout->dtype, layout->head_dim, group))
+        return fail(PKV_ENOTSUP, "no prefill kernel for dtype %d, head_dim %d, group %d (16-bit caches only)",
+                    layout->dtype, layout->head_dim, group);
+    if (num_seqs > 65535) return fail(PKV_ENOTSUP, "num_seqs %d exceeds 65535", num_seqs);
+    if (layout->n_kv_heads > 65535) return fail(PKV_ENOTSUP, "n_kv_heads %d exceeds 65535", layout->n_kv_heads);
+    if ((int64_t)max_q_len * group > INT32_MAX / 2) return fail(PKV_EINVAL, "max_q_len %d is too large", max_q_len);
+    if (num_seqs == 0 || max_q_len == 0) return ok();
+    pkv::PrefillParams p{};
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.cu_q = cu_q;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.num_blocks = layout->num_blocks;
+    p.n_kv_heads = layout->n_kv_heads;
+    p.n_q_heads = n_q_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_seqs = num_seqs;
+    p.max_q_len = max_q_len;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    hipError_t e = pkv::launch_prefill(p, layout->dtype, layout->head_dim, group, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+}
+
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks_per_seq,
                                       const pkv_layout* layout, int32_t part_tokens) {
     if (check_layout(layout) != PKV_OK || num_seqs < 0 || n_q_heads < 1 || max_blocks_per_seq < 1) return 0;
@@ -439,6 +517,32 @@ pkv_status pkv_validate(const pkv_layout* layout, const int32_t* block_tables, i
         for (size_t i = 1; i < sorted.size(); ++i)
             if (sorted[i] == sorted[i - 1])
                 return fail(PKV_EINVAL, "two sequences append to slot %lld", (long long)sorted[i]);
+    }
+    return PKV_OK;
+}
+
+pkv_status pkv_validate_prefill(const pkv_layout* layout, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* cu_q, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_q_len) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || max_blocks_per_seq < 1) return fail(PKV_EINVAL, "bad num_seqs or max_blocks_per_seq");
+    if (num_seqs > 0 && (!block_tables || !cu_q || !context_lens)) return fail(PKV_EINVAL, "a required pointer is NULL");
+    if (num_seqs > 0 && cu_q[0] != 0) return fail(PKV_EINVAL, "cu_q[0] = %d, not 0", cu_q[0]);
+    const int64_t B = layout->block_size;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t n = (int64_t)cu_q[s + 1] - cu_q[s];
+        const int64_t L = context_lens[s];
+        if (n < 0) return fail(PKV_EINVAL, "cu_q decreases at sequence %d", s);
+        if (n > max_q_len) return fail(PKV_EINVAL, "sequence %d: chunk of %lld tokens > max_q_len %d", s, (long long)n, max_q_len);
+        if (L < n || L > (int64_t)max_blocks_per_seq * B)
+            return fail(PKV_EOOB, "sequence %d: context length %lld outside [%lld, %lld]", s, (long long)L,
+                        (long long)n, (long long)max_blocks_per_seq * B);
+        const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+        for (int64_t b = 0; b < (L + B - 1) / B; ++b)
+            if (row[b] < 0 || row[b] >= layout->num_blocks)
+                return fail(PKV_EOOB, "sequence %d: table entry %lld = %d outside [0, %d)", s, (long long)b, row[b],
+                            layout->num_blocks);
     }
     return PKV_OK;
 }

@@ -21,6 +21,39 @@ struct AppendParams {
     int32_t row_bytes;  // n_kv_heads * head_dim * element bytes
 };
 
+struct AppendTokensParams {
+    const void* k_new;  // [total][n_kv_heads][head_dim]
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* cu_new;     // [num_seqs + 1]: sequence s owns rows cu_new[s] .. cu_new[s+1]-1
+    const int32_t* start_pos;  // [num_seqs]: position of each sequence's first new row
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t total;      // rows in k_new (the host's cu_new[num_seqs])
+    int32_t row_bytes;  // n_kv_heads * head_dim * element bytes
+};
+
+struct PrefillParams {
+    const void* q;  // [total][n_q_heads][head_dim]
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* cu_q;          // [num_seqs + 1]
+    const int32_t* context_lens;  // [num_seqs]: tokens in the cache, the chunk included
+    void* out;                    // [total][n_q_heads][head_dim]
+    int32_t num_blocks;
+    int32_t n_kv_heads;
+    int32_t n_q_heads;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t max_q_len;  // longest chunk (sizes the grid)
+    float scale_log2;   // scale * log2(e)
+};
+
 struct CopyParams {
     void* k_cache;
     void* v_cache;
@@ -72,6 +105,9 @@ struct DecodeParams {
 // Each returns hipSuccess or the launch error.  dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
+hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int group, hipStream_t stream);
+bool prefill_supported(int dtype, int head_dim, int group);
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int group,
                                     hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, int dtype, int head_dim, int group, hipStream_t stream);

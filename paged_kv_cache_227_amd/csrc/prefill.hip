@@ -1,0 +1,339 @@
+// prefill.hip -- chunked prefill on gfx950: the n-token append and the
+// attention of a chunk's queries over the paged cache.
+//
+// A long prompt is processed a chunk at a time ("How a serving engine actually
+// works", paperfordummies.in, section "Prefill and decode are two different
+// jobs"), and the block table grows by as many blocks as the chunk's tokens
+// need ("Paged Attention and the Block Manager", snowch.github.io ch08, "The
+// build").  A sequence whose cache holds L tokens after the step received its
+// last n of them in the step (positions L-n .. L-1); the query of chunk token j
+// (position L-n+j) attends to positions 0 .. L-n+j: the whole earlier context
+// and the chunk up to itself.  With n = 1 this is a decode step.
+//
+// n-token append: workgroup x copies new row x (of all sequences' packed rows)
+// into the slot of its position, found through the block table.
+//
+// Attention: unlike decode, a chunk makes QK^T and PV real matrix products
+// (n x G query rows against every key), so the work runs on the matrix cores.
+// A query row is one (chunk token, head of the KV head's group) pair; rows of
+// one (sequence, KV head) are ordered token-major.  One workgroup holds
+// NW x 16 x NQ consecutive rows of one (sequence, KV head):
+//   * the 16-token K and V tiles of each block up to the workgroup's last
+//     causal position are loaded once per workgroup (16-byte loads, the next
+//     block in flight while the current one is computed) and stored in LDS,
+//     double-buffered, 16-byte chunks XOR-swizzled by row;
+//   * each wave owns NQ groups of 16 rows.  Per block and group:
+//       S^T = K Q^T   (v_mfma_f32_16x16x32, K from LDS as the A operand, the
+//                      group's q rows as B, held in registers),
+//     the prefix-causal mask (key position <= the row's position) by select,
+//     an online softmax per row in base-2 units (each row's state lives in one
+//     lane column), then
+//       O^T += V^T P^T (v_mfma_f32_16x16x16, V^T read transposed from LDS,
+//                      P^T straight from S^T's accumulator layout),
+//     with P split into high and low 16-bit parts so about 16 bits of each
+//     weight survive;
+//   * blocks wholly past a wave's last position are skipped by that wave;
+//     tiles are started longest first (the last rows see the most keys).
+// Rows past L in a sequence's last block are loaded as zeros, so whatever
+// those slots hold never reaches the output.
+#include <math.h>
+
+#include <type_traits>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+#include "pkv_mfma.h"
+
+namespace pkv {
+
+// ---- n-token append ---------------------------------------------------------
+
+template <int VB>
+__global__ __launch_bounds__(256) void append_tokens_kernel(AppendTokensParams p) {
+    const int x = blockIdx.x;
+    const int S = p.num_seqs;
+    if (x >= p.cu_new[S] || p.cu_new[0] > x) return;
+    // the sequence owning row x: cu_new[s] <= x < cu_new[s + 1]
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu_new[mid] <= x) lo = mid;
+        else hi = mid;
+    }
+    const int s = lo;
+    const int64_t pos = (int64_t)p.start_pos[s] + (x - p.cu_new[s]);
+    if (p.start_pos[s] < 0 || pos < 0 || pos / p.block_size >= p.max_blocks) return;
+    const int blk = p.block_tables[(int64_t)s * p.max_blocks + pos / p.block_size];
+    if (blk < 0 || blk >= p.num_blocks) return;
+    const int64_t slot = (int64_t)blk * p.block_size + pos % p.block_size;
+    const bool is_v = blockIdx.y != 0;
+    const char* src = static_cast<const char*>(is_v ? p.v_new : p.k_new) + (int64_t)x * p.row_bytes;
+    char* dst = static_cast<char*>(is_v ? p.v_cache : p.k_cache) + slot * p.row_bytes;
+    for (int off = threadIdx.x * VB; off < p.row_bytes; off += blockDim.x * VB) {
+        if constexpr (VB == 16) {
+            const v4u32_t v = *reinterpret_cast<const v4u32_t*>(src + off);
+            *reinterpret_cast<v4u32_t*>(dst + off) = v;
+        } else if constexpr (VB == 4) {
+            *reinterpret_cast<uint32_t*>(dst + off) = *reinterpret_cast<const uint32_t*>(src + off);
+        } else {
+            *reinterpret_cast<uint16_t*>(dst + off) = *reinterpret_cast<const uint16_t*>(src + off);
+        }
+    }
+}
+
+hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream) {
+    if (p.total <= 0 || p.num_seqs <= 0) return hipSuccess;
+    const dim3 grid(p.total, 2);
+    if (p.row_bytes % 16 == 0)
+        hipLaunchKernelGGL(append_tokens_kernel<16>, grid, dim3(256), 0, stream, p);
+    else if (p.row_bytes % 4 == 0)
+        hipLaunchKernelGGL(append_tokens_kernel<4>, grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(append_tokens_kernel<2>, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+// ---- attention ---------------------------------------------------------------
+
+template <class E, int D, int G, int NW, int NQ, bool SPLIT>
+struct PrefillShape {
+    static constexpr int RB = D * 2;            // bytes per head row
+    static constexpr int CH = RB / 16;          // 16-byte chunks per head row
+    static constexpr int KK = D / 32;           // 16x16x32 products per score tile
+    static constexpr int TT = D / 16;           // 16-wide output tiles
+    static constexpr int ROWS_W = 16 * NQ;      // query rows per wave
+    static constexpr int ROWS = NW * ROWS_W;    // query rows per workgroup
+    static constexpr int NT = NW * kWave;
+    static constexpr int TILE = kBlock * RB;    // bytes of one K (or V) tile
+    static constexpr int NCH = 2 * kBlock * CH; // 16-byte chunks of a K + V tile pair
+    static constexpr int PER_T = (NCH + NT - 1) / NT;
+    static_assert(E::kBytes == 2 && D % 32 == 0 && CH == 4 * KK, "16-bit caches, head_dim a multiple of 32");
+};
+
+// Position of (row, 16-byte chunk) in an LDS tile of one head: rows of RB
+// bytes, chunks XOR-swizzled by row so that transposed and row reads spread
+// over the banks.
+template <int RB>
+__device__ __forceinline__ uint32_t tile_pos(int row, int chunk) {
+    constexpr int CH = RB / 16;
+    return (uint32_t)(row * RB + ((chunk ^ (row % CH)) * 16));
+}
+
+template <class E, int D, int G, int NW, int NQ, bool SPLIT>
+__global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
+    using SH = PrefillShape<E, D, G, NW, NQ, SPLIT>;
+    using OPS = MfmaOps<E>;
+    using op4_t = typename OPS::op4_t;
+    using el_t = typename std::remove_reference<decltype(op4_t{}[0])>::type;
+    constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT;
+    __shared__ __attribute__((aligned(16))) char lds[2][2][SH::TILE];  // [buffer][K, V]
+
+    const int s = blockIdx.z;
+    const int kvh = blockIdx.y;
+    const int Hq = p.n_q_heads;
+    const int q0 = p.cu_q[s];
+    const int n = p.cu_q[s + 1] - q0;
+    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
+    if (n <= 0 || n > L) return;  // an empty or impossible chunk
+    const int nrows = n * G;
+    const int ntiles = (nrows + SH::ROWS - 1) / SH::ROWS;
+    const int tile = ntiles - 1 - (int)blockIdx.x;  // longest tiles first
+    if (tile < 0) return;
+    const int r0 = tile * SH::ROWS;
+    const int ctx = L - n;  // tokens before the chunk
+    const int wg_last_pos = ctx + (min(r0 + SH::ROWS, nrows) - 1) / G;
+    const int nblk = wg_last_pos / kBlock + 1;
+
+    const int tid = threadIdx.x;
+    const int w = wave_id_uniform();
+    const int lane = tid % kWave;
+    const int gq = lane / 16;  // MFMA lane coordinates
+    const int jq = lane % 16;
+    const int wr0 = r0 + w * SH::ROWS_W;  // this wave's first row
+    const int wave_last_pos = wr0 < nrows ? ctx + (min(wr0 + SH::ROWS_W, nrows) - 1) / G : -1;
+
+    // q rows of this wave: group c, column jq is row wr0 + 16c + jq.
+    Vec16 qf[NQ][KK];
+    int qpos[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+        const int row = wr0 + 16 * c + jq;
+        const bool ok = row < nrows;
+        const int tok = row / G;
+        qpos[c] = ok ? ctx + tok : -1;
+        const char* qrow = static_cast<const char*>(p.q) +
+                           (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qf[c][kk] = ok ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
+    }
+    float m[NQ], l[NQ];
+    f32x4_t acc[NQ][TT];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+        m[c] = -INFINITY;
+        l[c] = 0.f;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[c][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Cooperative tile loads: chunk e of the K + V pair is K row e / CH (e < 16 CH)
+    // or V row (e - 16 CH) / CH, 16-byte column e % CH.
+    const uint32_t row_stride = (uint32_t)p.n_kv_heads * RB;
+    const int64_t blk_bytes = (int64_t)row_stride * kBlock;
+    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
+    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
+    const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
+    Vec16 pre[SH::PER_T];
+    auto fetch = [&](int b) {
+        int pb = table[b];
+        const bool blk_ok = pb >= 0 && pb < p.num_blocks;
+        const int valid = min(kBlock, L - b * kBlock);  // rows of this block inside the sequence
+#pragma unroll
+        for (int k = 0; k < SH::PER_T; ++k) {
+            const int e = tid + k * SH::NT;
+            const int ee = e % (kBlock * CH);
+            const int row = ee / CH;
+            const bool ok = e < SH::NCH && blk_ok && row < valid;
+            const char* base = e < kBlock * CH ? kbase : vbase;
+            pre[k] = ok ? load16(base + (int64_t)pb * blk_bytes + (int64_t)row * row_stride + (ee % CH) * 16)
+                        : Vec16{{0u, 0u, 0u, 0u}};
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < SH::PER_T; ++k) {
+            const int e = tid + k * SH::NT;
+            if (e < SH::NCH) {
+                const int ee = e % (kBlock * CH);
+                lds_store16(lds[buf][e < kBlock * CH ? 0 : 1], tile_pos<RB>(ee / CH, ee % CH), pre[k]);
+            }
+        }
+    };
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+        const int buf = b & 1;
+        if (b + 1 < nblk) fetch(b + 1);
+        if (b * kBlock <= wave_last_pos) {
+            const char* kl = lds[buf][0];
+            const char* vl = lds[buf][1];
+            Vec16 ka[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) ka[kk] = lds_load16(kl, tile_pos<RB>(jq, 4 * kk + gq));
+            op4_t ph[NQ], pl[NQ];
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) sacc = OPS::qk(ka[kk], qf[c][kk], sacc);
+                // lane (gq, jq) holds keys b*16 + 4gq + r of row column jq
+                float sc[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kpos = b * kBlock + 4 * gq + r;
+                    sc[r] = kpos <= qpos[c] ? sacc[r] * p.scale_log2 : -INFINITY;
+                }
+                float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                mx = fmaxf(mx, shfl_xor(mx, 16));
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                const float mn = fmaxf(m[c], mx);
+                const float ms = mn == -INFINITY ? 0.f : mn;
+                if (__builtin_amdgcn_ballot_w64(mn > m[c])) {
+                    const float alpha = __builtin_amdgcn_exp2f(m[c] - ms);
+                    l[c] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) acc[c][t] *= alpha;
+                    m[c] = mn;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = __builtin_amdgcn_exp2f(sc[r] - ms);
+                    l[c] += pr;
+                    short hs, ls;
+                    OPS::split(pr, hs, ls);
+                    ph[c][r] = __builtin_bit_cast(el_t, hs);
+                    pl[c][r] = __builtin_bit_cast(el_t, ls);
+                }
+            }
+            // V^T read transposed: lane (gq, jq) takes key row 4gq + jq/4, bytes 32t + 8(jq%4).
+            const int trow = 4 * gq + jq / 4;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const op4_t a = OPS::read_tr(vl + tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2));
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    acc[c][t] = OPS::pv(a, ph[c], acc[c][t]);
+                    if constexpr (SPLIT) acc[c][t] = OPS::pv(a, pl[c], acc[c][t]);
+                }
+            }
+        }
+        if (b + 1 < nblk) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Each lane summed its own 4 keys per block: add the other lane groups.
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+        float lt = l[c];
+        lt += shfl_xor(lt, 16);
+        lt += shfl_xor(lt, 32);
+        const int row = wr0 + 16 * c + jq;
+        if (row >= nrows) continue;
+        const float inv = 1.f / lt;
+        char* orow = static_cast<char*>(p.out) + (((int64_t)(q0 + row / G) * Hq + kvh * G + row % G) * D) * 2;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) E::store(orow + (16 * t + 4 * gq + r) * 2, acc[c][t][r] * inv);
+    }
+}
+
+template <class E, int D, int G>
+static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
+    constexpr int NW = 4, NQ = 2;
+    constexpr int ROWS = NW * 16 * NQ;
+    const int64_t tiles = ((int64_t)p.max_q_len * G + ROWS - 1) / ROWS;
+    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)tiles, p.n_kv_heads, p.num_seqs);
+    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, true>), grid, dim3(NW * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <class E, int D>
+static hipError_t launch_prefill_d(const PrefillParams& p, int group, hipStream_t stream) {
+    switch (group) {
+        case 1: return launch_prefill_g<E, D, 1>(p, stream);
+        case 2: return launch_prefill_g<E, D, 2>(p, stream);
+        case 4: return launch_prefill_g<E, D, 4>(p, stream);
+        case 8: return launch_prefill_g<E, D, 8>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class E>
+static hipError_t launch_prefill_e(const PrefillParams& p, int head_dim, int group, hipStream_t stream) {
+    switch (head_dim) {
+        case 64: return launch_prefill_d<E, 64>(p, group, stream);
+        case 128: return launch_prefill_d<E, 128>(p, group, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool prefill_supported(int dtype, int head_dim, int group) {
+    return (dtype == 1 || dtype == 2) && (head_dim == 64 || head_dim == 128) &&
+           (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int group, hipStream_t stream) {
+    if (p.num_seqs <= 0 || p.max_q_len <= 0) return hipSuccess;
+    switch (dtype) {
+        case 1: return launch_prefill_e<F16>(p, head_dim, group, stream);
+        case 2: return launch_prefill_e<BF16>(p, head_dim, group, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pkv

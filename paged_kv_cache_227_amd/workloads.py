@@ -335,6 +335,121 @@ CONFIGS = {
 
 
 # --------------------------------------------------------------------------
+# Chunked prefill
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    """One chunked-prefill step.  Sequence s holds context_lens[s] tokens once
+    its chunk of n_s = cu_q[s+1] - cu_q[s] tokens is appended (positions
+    context_lens[s] - n_s ..); q, k_new and v_new are the packed chunk rows.
+    The caches hold data for every position, the chunk's slots included (the
+    append overwrites those)."""
+    name: str
+    dtype: str
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    context_lens: np.ndarray   # int32 [S]
+    cu_q: np.ndarray           # int32 [S + 1]
+    block_tables: np.ndarray   # int32 [S][max_blocks]
+    q: np.ndarray              # [total][Hq][D]
+    k_new: np.ndarray          # [total][Hkv][D]
+    v_new: np.ndarray          # [total][Hkv][D]
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    scale: float
+    seed: int
+    notes: str = ""
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def chunk_lens(self) -> np.ndarray:
+        return np.diff(self.cu_q).astype(np.int32)
+
+    @property
+    def start_pos(self) -> np.ndarray:
+        return (self.context_lens - self.chunk_lens).astype(np.int32)
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.chunk_lens.max()) if self.num_seqs else 0
+
+    @property
+    def dtype_code(self) -> int:
+        return DTYPE_CODES[self.dtype]
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    def attention_flops(self) -> int:
+        """Algorithmic flops of the attention: 4 * head_dim per (query head, key)
+        pair a query sees (QK and PV, a multiply-add counted as two)."""
+        n = self.chunk_lens.astype(np.int64)
+        ctx = self.start_pos.astype(np.int64)
+        pairs = int(np.sum(n * ctx + n * (n + 1) // 2))
+        return 4 * self.head_dim * self.n_q_heads * pairs
+
+    def kv_bytes(self) -> int:
+        """K and V bytes of all positions the chunk's queries see (each once)."""
+        return int(np.sum(self.context_lens, dtype=np.int64)) * 2 * self.n_kv_heads * self.head_dim * \
+            ELT_BYTES[self.dtype]
+
+
+def build_prefill(name: str, context: _Seq[int], chunk: _Seq[int], n_q_heads: int, n_kv_heads: int,
+                  head_dim: int, dtype: str, seed: int, pool_factor: float = 1.0, data_mult: float = 1.0,
+                  notes: str = "") -> PrefillWorkload:
+    """Sequence s has context[s] tokens cached and a chunk of chunk[s] new ones.
+    Tables, caches and scale come from ``build`` (same seeded streams); the
+    chunk's q / k_new / v_new rows come from a stream of their own."""
+    context = np.asarray(context, dtype=np.int64)
+    chunk = np.asarray(chunk, dtype=np.int64)
+    lens = context + chunk
+    w = build(name, lens, n_q_heads, n_kv_heads, head_dim, dtype, seed, pool_factor=pool_factor,
+              data_mult=data_mult, notes=notes)
+    c_q, c_kn, c_vn = np.random.SeedSequence([seed, 11]).spawn(3)
+    total = int(chunk.sum())
+    cu = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    return PrefillWorkload(
+        name=name, dtype=dtype, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
+        block_size=w.block_size, num_blocks=w.num_blocks, context_lens=lens.astype(np.int32), cu_q=cu,
+        block_tables=w.block_tables, q=normal_fill((total, n_q_heads, head_dim), dtype, c_q, data_mult),
+        k_new=normal_fill((total, n_kv_heads, head_dim), dtype, c_kn, data_mult),
+        v_new=normal_fill((total, n_kv_heads, head_dim), dtype, c_vn, data_mult),
+        k_cache=w.k_cache, v_cache=w.v_cache, scale=w.scale, seed=seed, notes=notes)
+
+
+def prefill_llama2_7b(chunk: int = 512, seed: int = SEED_BASE + 7) -> PrefillWorkload:
+    """Chunked prefill of 2,048-token prompts on the Llama-2-7B layer (32/32
+    heads, D=128, fp16; data N(0,1)/sqrt(128)), one step with four prompts at
+    the four stages of a 512-token chunking: contexts 0, 512, 1024 and 1536
+    tokens cached, each with its next 512-token chunk."""
+    stages = 2048 // chunk
+    return build_prefill("prefill_llama2_7b", [i * chunk for i in range(stages)], [chunk] * stages, 32, 32, 128,
+                         "f16", seed, data_mult=1.0 / math.sqrt(128.0),
+                         notes="2048-token prompts in %d-token chunks, one prompt per stage" % chunk)
+
+
+def prefill_gqa_8b(chunk: int = 512, seed: int = SEED_BASE + 8) -> PrefillWorkload:
+    """The same chunking on the GQA 8B layer (32 q heads, 8 KV heads, D=128, bf16)."""
+    stages = 2048 // chunk
+    return build_prefill("prefill_gqa_8b", [i * chunk for i in range(stages)], [chunk] * stages, 32, 8, 128,
+                         "bf16", seed, notes="2048-token prompts in %d-token chunks, one prompt per stage" % chunk)
+
+
+PREFILL_CONFIGS = {
+    "prefill_llama2_7b": prefill_llama2_7b,
+    "prefill_gqa_8b": prefill_gqa_8b,
+}
+
+
+# --------------------------------------------------------------------------
 # Block copies (copy-on-write, whole-block moves)
 # --------------------------------------------------------------------------
 

@@ -160,3 +160,53 @@ def test_validate_copies(L):
         _lib.validate_copies(lay, [1, 3], [3, 4], [4, 4])
     with pytest.raises(ValueError, match="equal-length"):
         _lib.validate_copies(lay, [1, 2], [3], [4])
+
+
+def test_prefill_rejects(L):
+    lay = _layout(dtype=1, head_dim=128)
+    def call(lay=lay, S=2, maxq=8, Hq=4, scale=0.1, q=FAKE):
+        return L.paged_attention_prefill(q, FAKE, FAKE, ctypes.byref(lay), FAKE, 4, FAKE, FAKE, S, maxq, Hq, scale,
+                                         FAKE, None)
+    assert call(Hq=6) == _lib.PKV_EINVAL
+    assert call(q=None) == _lib.PKV_EINVAL
+    assert call(scale=float("inf")) == _lib.PKV_EINVAL
+    assert call(S=-1) == _lib.PKV_EINVAL
+    assert call(maxq=-1) == _lib.PKV_EINVAL
+    assert call(lay=_layout(dtype=0, head_dim=128)) == _lib.PKV_ENOTSUP     # fp32 prefill is not served
+    assert "16-bit" in _lib.last_error()
+    assert call(lay=_layout(dtype=2, head_dim=96)) == _lib.PKV_ENOTSUP
+    assert call(lay=_layout(dtype=2, block_size=32)) == _lib.PKV_ENOTSUP
+    assert call(Hq=12) == _lib.PKV_ENOTSUP                                 # group of 3
+    assert call(S=0) == _lib.PKV_OK and call(maxq=0) == _lib.PKV_OK        # nothing to do
+
+
+def test_append_tokens_rejects(L):
+    lay = _layout()
+    args = [FAKE, FAKE, FAKE, FAKE, ctypes.byref(lay), FAKE, 3, FAKE, FAKE, 2, 5, None]
+    assert L.paged_kv_append_tokens(None, *args[1:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_append_tokens(*args[:7], None, *args[8:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_append_tokens(*args[:9], -1, 5, None) == _lib.PKV_EINVAL
+    assert L.paged_kv_append_tokens(*args[:10], -5, None) == _lib.PKV_EINVAL
+    assert L.paged_kv_append_tokens(*args[:6], 0, *args[7:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_append_tokens(*args[:10], 0, None) == _lib.PKV_OK   # no rows: nothing to do
+
+
+def test_validate_prefill(L):
+    lay = _layout(num_blocks=10, block_size=4)
+    bt = np.array([[5, 2, 9, -1], [0, 1, 3, 4]], np.int32)
+    _lib.validate_prefill(lay, bt, [0, 3, 8], [10, 16], 5)
+    _lib.validate_prefill(lay, bt, [0, 0, 8], [10, 16], 8)           # an empty chunk
+    with pytest.raises(ValueError, match="max_q_len"):
+        _lib.validate_prefill(lay, bt, [0, 3, 8], [10, 16], 4)
+    with pytest.raises(ValueError, match="decreases"):
+        _lib.validate_prefill(lay, bt, [0, 3, 2], [10, 16], 8)
+    with pytest.raises(ValueError, match="context length"):
+        _lib.validate_prefill(lay, bt, [0, 3, 8], [2, 16], 8)         # chunk longer than the context
+    with pytest.raises(ValueError, match="context length"):
+        _lib.validate_prefill(lay, bt, [0, 3, 8], [10, 17], 8)        # longer than the table
+    with pytest.raises(ValueError, match="not 0"):
+        _lib.validate_prefill(lay, bt, [1, 3, 8], [10, 16], 8)
+    bt2 = bt.copy()
+    bt2[0, 1] = 10
+    with pytest.raises(ValueError, match="outside"):
+        _lib.validate_prefill(lay, bt2, [0, 3, 8], [10, 16], 8)
