@@ -18,11 +18,13 @@
 // A query row is one (chunk token, head of the KV head's group) pair; rows of
 // one (sequence, KV head) are ordered token-major.  One workgroup holds
 // NW x 16 x NQ consecutive rows of one (sequence, KV head):
-//   * the 16-token K and V tiles of each block up to the workgroup's last
-//     causal position are loaded once per workgroup (16-byte loads, the next
-//     block in flight while the current one is computed) and stored in LDS,
-//     double-buffered, 16-byte chunks XOR-swizzled by row;
-//   * each wave owns NQ groups of 16 rows.  Per block and group:
+//   * the K and V tiles of NB blocks at a time, up to the workgroup's last
+//     causal position, are loaded once per workgroup (the iteration's table
+//     entries first, then every 16-byte load in flight at once, one iteration
+//     ahead of the compute) and stored in LDS, double-buffered, 16-byte
+//     chunks XOR-swizzled by row;
+//   * each wave owns NQ groups of 16 rows; one softmax rescale per iteration
+//     covers its NB x 16 keys.  Per block and group:
 //       S^T = K Q^T   (v_mfma_f32_16x16x32, K from LDS as the A operand, the
 //                      group's q rows as B, held in registers),
 //     the prefix-causal mask (key position <= the row's position) by select,
@@ -95,7 +97,7 @@ hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream)
 
 // ---- attention ---------------------------------------------------------------
 
-template <class E, int D, int G, int NW, int NQ, bool SPLIT>
+template <class E, int D, int G, int NW, int NQ, int NB>
 struct PrefillShape {
     static constexpr int RB = D * 2;            // bytes per head row
     static constexpr int CH = RB / 16;          // 16-byte chunks per head row
@@ -104,10 +106,12 @@ struct PrefillShape {
     static constexpr int ROWS_W = 16 * NQ;      // query rows per wave
     static constexpr int ROWS = NW * ROWS_W;    // query rows per workgroup
     static constexpr int NT = NW * kWave;
-    static constexpr int TILE = kBlock * RB;    // bytes of one K (or V) tile
-    static constexpr int NCH = 2 * kBlock * CH; // 16-byte chunks of a K + V tile pair
+    static constexpr int TILE = kBlock * RB;    // bytes of one block's K (or V) rows of one head
+    static constexpr int SPAN = NB * TILE;      // bytes of an iteration's K (or V) rows
+    static constexpr int NCH = 2 * NB * kBlock * CH;  // 16-byte chunks of an iteration's K + V
     static constexpr int PER_T = (NCH + NT - 1) / NT;
     static_assert(E::kBytes == 2 && D % 32 == 0 && CH == 4 * KK, "16-bit caches, head_dim a multiple of 32");
+    static_assert(NCH % NT == 0, "every thread moves the same number of chunks");
 };
 
 // Position of (row, 16-byte chunk) in an LDS tile of one head: rows of RB
@@ -119,14 +123,16 @@ __device__ __forceinline__ uint32_t tile_pos(int row, int chunk) {
     return (uint32_t)(row * RB + ((chunk ^ (row % CH)) * 16));
 }
 
-template <class E, int D, int G, int NW, int NQ, bool SPLIT>
+// One iteration covers NB consecutive blocks: their K and V tiles are loaded
+// together (one iteration ahead) and one softmax rescale covers all NB x 16 keys.
+template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT>
 __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
-    using SH = PrefillShape<E, D, G, NW, NQ, SPLIT>;
+    using SH = PrefillShape<E, D, G, NW, NQ, NB>;
     using OPS = MfmaOps<E>;
     using op4_t = typename OPS::op4_t;
     using el_t = typename std::remove_reference<decltype(op4_t{}[0])>::type;
     constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT;
-    __shared__ __attribute__((aligned(16))) char lds[2][2][SH::TILE];  // [buffer][K, V]
+    __shared__ __attribute__((aligned(16))) char lds[2][2][SH::SPAN];  // [buffer][K, V][block][row][RB]
 
     const int s = blockIdx.z;
     const int kvh = blockIdx.y;
@@ -143,6 +149,7 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
     const int ctx = L - n;  // tokens before the chunk
     const int wg_last_pos = ctx + (min(r0 + SH::ROWS, nrows) - 1) / G;
     const int nblk = wg_last_pos / kBlock + 1;
+    const int nit = (nblk + NB - 1) / NB;
 
     const int tid = threadIdx.x;
     const int w = wave_id_uniform();
@@ -177,66 +184,92 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
         for (int t = 0; t < TT; ++t) acc[c][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Cooperative tile loads: chunk e of the K + V pair is K row e / CH (e < 16 CH)
-    // or V row (e - 16 CH) / CH, 16-byte column e % CH.
+    // Cooperative loads: chunk e of an iteration is (cache e / (NB 16 CH), block,
+    // row, 16-byte column); consecutive threads read consecutive chunks of a row.
     const uint32_t row_stride = (uint32_t)p.n_kv_heads * RB;
     const int64_t blk_bytes = (int64_t)row_stride * kBlock;
     const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
     const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
+    constexpr int PER_CACHE = NB * kBlock * CH;
+    // This thread's chunks: block, row and column within an iteration (fixed).
+    int c_nb[SH::PER_T], c_row[SH::PER_T], c_col[SH::PER_T];
+#pragma unroll
+    for (int k = 0; k < SH::PER_T; ++k) {
+        const int ee = (tid + k * SH::NT) % PER_CACHE;
+        c_nb[k] = ee / (kBlock * CH);
+        c_row[k] = (ee / CH) % kBlock;
+        c_col[k] = ee % CH;
+    }
     Vec16 pre[SH::PER_T];
-    auto fetch = [&](int b) {
-        int pb = table[b];
-        const bool blk_ok = pb >= 0 && pb < p.num_blocks;
-        const int valid = min(kBlock, L - b * kBlock);  // rows of this block inside the sequence
+    auto fetch = [&](int it) {
+        // the iteration's table entries first (uniform loads), then every chunk load in flight at once
+        int pbs[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int b = it * NB + nb;
+            const int pb = b < nblk ? table[b] : -1;
+            pbs[nb] = pb >= 0 && pb < p.num_blocks ? pb : -1;
+        }
 #pragma unroll
         for (int k = 0; k < SH::PER_T; ++k) {
-            const int e = tid + k * SH::NT;
-            const int ee = e % (kBlock * CH);
-            const int row = ee / CH;
-            const bool ok = e < SH::NCH && blk_ok && row < valid;
-            const char* base = e < kBlock * CH ? kbase : vbase;
-            pre[k] = ok ? load16(base + (int64_t)pb * blk_bytes + (int64_t)row * row_stride + (ee % CH) * 16)
+            int pb = pbs[0];
+#pragma unroll
+            for (int nb = 1; nb < NB; ++nb) pb = c_nb[k] == nb ? pbs[nb] : pb;
+            const int b = it * NB + c_nb[k];
+            const bool ok = pb >= 0 && c_row[k] < L - b * kBlock;  // rows of the block inside the sequence
+            const char* base = tid + k * SH::NT < PER_CACHE ? kbase : vbase;
+            pre[k] = ok ? load16(base + (int64_t)pb * blk_bytes + (int64_t)c_row[k] * row_stride + c_col[k] * 16)
                         : Vec16{{0u, 0u, 0u, 0u}};
         }
     };
     auto stash = [&](int buf) {
 #pragma unroll
-        for (int k = 0; k < SH::PER_T; ++k) {
-            const int e = tid + k * SH::NT;
-            if (e < SH::NCH) {
-                const int ee = e % (kBlock * CH);
-                lds_store16(lds[buf][e < kBlock * CH ? 0 : 1], tile_pos<RB>(ee / CH, ee % CH), pre[k]);
-            }
-        }
+        for (int k = 0; k < SH::PER_T; ++k)
+            lds_store16(lds[buf][tid + k * SH::NT < PER_CACHE ? 0 : 1] + c_nb[k] * SH::TILE,
+                        tile_pos<RB>(c_row[k], c_col[k]), pre[k]);
     };
 
     fetch(0);
     stash(0);
     __syncthreads();
-    for (int b = 0; b < nblk; ++b) {
-        const int buf = b & 1;
-        if (b + 1 < nblk) fetch(b + 1);
-        if (b * kBlock <= wave_last_pos) {
+    for (int it = 0; it < nit; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < nit) fetch(it + 1);
+        const int b0 = it * NB;
+        if (b0 * kBlock <= wave_last_pos) {
             const char* kl = lds[buf][0];
             const char* vl = lds[buf][1];
-            Vec16 ka[KK];
+            // scores: lane (gq, jq) holds keys (b0 + nb) * 16 + 4gq + r of row column jq
+            f32x4_t sacc[NQ][NB];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) ka[kk] = lds_load16(kl, tile_pos<RB>(jq, 4 * kk + gq));
-            op4_t ph[NQ], pl[NQ];
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) sacc[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if ((b0 + nb) * kBlock <= wave_last_pos) {
+                    Vec16 ka[KK];
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        ka[kk] = lds_load16(kl + nb * SH::TILE, tile_pos<RB>(jq, 4 * kk + gq));
+#pragma unroll
+                    for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                        for (int kk = 0; kk < KK; ++kk) sacc[c][nb] = OPS::qk(ka[kk], qf[c][kk], sacc[c][nb]);
+                }
+            }
+            op4_t ph[NQ][NB], pl[NQ][NB];
 #pragma unroll
             for (int c = 0; c < NQ; ++c) {
-                f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+                float sc[NB][4];
+                float mx = -INFINITY;
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) sacc = OPS::qk(ka[kk], qf[c][kk], sacc);
-                // lane (gq, jq) holds keys b*16 + 4gq + r of row column jq
-                float sc[4];
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kpos = b * kBlock + 4 * gq + r;
-                    sc[r] = kpos <= qpos[c] ? sacc[r] * p.scale_log2 : -INFINITY;
-                }
-                float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                    for (int r = 0; r < 4; ++r) {
+                        const int kpos = (b0 + nb) * kBlock + 4 * gq + r;
+                        sc[nb][r] = kpos <= qpos[c] ? sacc[c][nb][r] * p.scale_log2 : -INFINITY;
+                        mx = fmaxf(mx, sc[nb][r]);
+                    }
                 mx = fmaxf(mx, shfl_xor(mx, 16));
                 mx = fmaxf(mx, shfl_xor(mx, 32));
                 const float mn = fmaxf(m[c], mx);
@@ -249,28 +282,35 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
                     m[c] = mn;
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float pr = __builtin_amdgcn_exp2f(sc[r] - ms);
-                    l[c] += pr;
-                    short hs, ls;
-                    OPS::split(pr, hs, ls);
-                    ph[c][r] = __builtin_bit_cast(el_t, hs);
-                    pl[c][r] = __builtin_bit_cast(el_t, ls);
-                }
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float pr = __builtin_amdgcn_exp2f(sc[nb][r] - ms);
+                        l[c] += pr;
+                        short hs, ls;
+                        OPS::split(pr, hs, ls);
+                        ph[c][nb][r] = __builtin_bit_cast(el_t, hs);
+                        pl[c][nb][r] = __builtin_bit_cast(el_t, ls);
+                    }
             }
             // V^T read transposed: lane (gq, jq) takes key row 4gq + jq/4, bytes 32t + 8(jq%4).
             const int trow = 4 * gq + jq / 4;
 #pragma unroll
-            for (int t = 0; t < TT; ++t) {
-                const op4_t a = OPS::read_tr(vl + tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2));
+            for (int nb = 0; nb < NB; ++nb) {
+                if ((b0 + nb) * kBlock > wave_last_pos) continue;
 #pragma unroll
-                for (int c = 0; c < NQ; ++c) {
-                    acc[c][t] = OPS::pv(a, ph[c], acc[c][t]);
-                    if constexpr (SPLIT) acc[c][t] = OPS::pv(a, pl[c], acc[c][t]);
+                for (int t = 0; t < TT; ++t) {
+                    const op4_t a =
+                        OPS::read_tr(vl + nb * SH::TILE + tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2));
+#pragma unroll
+                    for (int c = 0; c < NQ; ++c) {
+                        acc[c][t] = OPS::pv(a, ph[c][nb], acc[c][t]);
+                        if constexpr (SPLIT) acc[c][t] = OPS::pv(a, pl[c][nb], acc[c][t]);
+                    }
                 }
             }
         }
-        if (b + 1 < nblk) stash(buf ^ 1);
+        if (it + 1 < nit) stash(buf ^ 1);
         __syncthreads();
     }
 
@@ -291,15 +331,27 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
     }
 }
 
-template <class E, int D, int G>
-static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
-    constexpr int NW = 4, NQ = 2;
+template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT>
+hipError_t launch_prefill_shape(const PrefillParams& p, hipStream_t stream) {
     constexpr int ROWS = NW * 16 * NQ;
     const int64_t tiles = ((int64_t)p.max_q_len * G + ROWS - 1) / ROWS;
     if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles, p.n_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, true>), grid, dim3(NW * kWave), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, NB, SPLIT>), grid, dim3(NW * kWave), 0, stream, p);
     return hipGetLastError();
+}
+
+// Launch shape (measured on MI355X): 8 waves of 16 query rows (128 rows per
+// workgroup); 32 keys per iteration at head_dim 128 (64 at 64), i.e. 16 KiB of
+// K and V per LDS buffer.  It needs no accumulator registers beyond the
+// architectural VGPRs and runs 4 waves per SIMD.  fp16 keeps one 16-bit P per
+// weight (11 significant bits); bf16 splits P into high and low parts, since
+// one bf16 keeps only 8.
+template <class E, int D, int G>
+static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
+    constexpr int NB = D == 128 ? 2 : 4;
+    constexpr bool SPLIT = std::is_same<E, BF16>::value;
+    return launch_prefill_shape<E, D, G, 8, 1, NB, SPLIT>(p, stream);
 }
 
 template <class E, int D>
