@@ -52,8 +52,11 @@
  *     [0, num_blocks) are a precondition violation: the kernels skip such a
  *     block (no out-of-bounds access) and the result is unspecified;
  *     pkv_validate() reports them.
- *   - Supported by the GPU path: dtype f32 / f16 / bf16, block_size 16,
- *     head_dim 64 or 128, n_q_heads / n_kv_heads in {1, 2, 4, 8}.
+ *   - Supported by the GPU path: dtype f32 / f16 / bf16, head_dim 64 or 128,
+ *     n_q_heads / n_kv_heads in {1, 2, 4, 8}; block_size 8, 16, 32 or 64 for
+ *     decode (the block size is "the one tuning knob" of "How a serving engine
+ *     actually works", section "The one formula"), 16 for prefill, any for the
+ *     appends and block copies.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -235,9 +238,9 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads,
  *
  *   part_tokens  0 for the library's choice (the flat schedule, unless a
  *                different default was set with pkv_set_partition_tokens), or
- *                a fixed partition length: a positive multiple of
+ *                a fixed partition length: a positive multiple of 16 and of
  *                layout->block_size; each P-token partition of a sequence is
- *                one workgroup's work and the partitions are merged by the
+ *                one wave's work and the partitions are merged by the
  *                log-sum-exp rule
  *   workspace    device buffer of at least
  *                paged_attention_workspace_size(..., part_tokens) bytes,
@@ -279,7 +282,8 @@ pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_pe
 
 /*
  * Process-wide partition length used when a call passes 0 (and by
- * paged_attention_decode): a positive multiple of the block size, or 0 to
+ * paged_attention_decode): a positive multiple of 16 (and, at call time, of
+ * the block size), or 0 to
  * restore the library's choice (the flat schedule; batches of more than 8000
  * sequences, or with more than 2^30 tiles, use 512-token partitions).
  * Returns PKV_EINVAL otherwise.

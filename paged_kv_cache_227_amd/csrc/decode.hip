@@ -126,15 +126,19 @@ struct WaveAttn {
         }
     }
 
-    // Loads of one tile: rows of head g at kbase/vbase + boff.
-    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t boff) {
+    // Loads of one tile: row r of head g at kbase/vbase + (r < 8 ? lo : hi) + r * row_stride.
+    // A load instruction covers RPS consecutive rows, all in the same half.
+    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi) {
+        static_assert(8 % RPS == 0, "a load instruction stays within one half of the tile");
 #pragma unroll
-        for (int j = 0; j < J; ++j)
+        for (int j = 0; j < J; ++j) {
+            const int64_t boff = j * RPS < 8 ? lo : hi;
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
                 kb[slot][j][k] = load16_policy<TU::STREAM>(kbase + boff + lane_off[j][k]);
                 vb[slot][j][k] = load16_policy<TU::STREAM>(vbase + boff + lane_off[j][k]);
             }
+        }
     }
 
     // Online-softmax update with one tile; `valid` rows (wave-uniform) belong
@@ -341,10 +345,11 @@ struct MfmaAttn {
         for (int t = 0; t < TT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t boff) {
+    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi) {
+        static_assert(8 % RPI == 0, "a load instruction stays within one half of the tile");
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int64_t off = boff + ld_base + (int64_t)i * RPI * row_stride_;
+            const int64_t off = (i * RPI < 8 ? lo : hi) + ld_base + (int64_t)i * RPI * row_stride_;
             kt[slot][i] = load16_policy<TU::STREAM>(kbase + off);
             vt[slot][i] = load16_policy<TU::STREAM>(vbase + off);
         }
@@ -450,6 +455,38 @@ struct MfmaAttn {
 template <class E, int D, int G, class TU>
 using Engine = typename std::conditional<TU::MFMA, MfmaAttn<E, D, G, TU>, WaveAttn<E, D, G, TU>>::type;
 
+// Where tile t (tokens 16t .. 16t+15) of a sequence lives.  The table row lists
+// ntab blocks of B = 1 << shift tokens (B in {8, 16, 32, 64}); rows 0-7 of the
+// tile are at lo + r * row_stride and rows 8-15 at hi + r * row_stride.  With
+// B >= 16 the tile lies inside one block (hi = lo); with B = 8 it spans two,
+// and a second block past the sequence (whose rows are masked) is replaced by
+// rows 0-7 of the first.  ok is false if a block the tile needs lies outside
+// the pool; the offsets then point at block 0, inside the cache.
+struct TileAddr {
+    int64_t lo, hi;
+    bool ok;
+};
+
+__device__ __forceinline__ TileAddr tile_addr(const int32_t* table, int t, int ntab, int shift, int num_blocks,
+                                              uint32_t row_stride) {
+    const int tok0 = t * kBlock;
+    const int bmask = (1 << shift) - 1;
+    const int64_t blk_bytes = (int64_t)row_stride << shift;
+    const int bi0 = tok0 >> shift;
+    const int bi1 = (tok0 + 8) >> shift;
+    const bool second = bi1 != bi0 && bi1 < ntab;
+    int pb0 = __builtin_amdgcn_readfirstlane(table[bi0]);
+    int pb1 = second ? __builtin_amdgcn_readfirstlane(table[bi1]) : pb0;
+    TileAddr a;
+    a.ok = pb0 >= 0 && pb0 < num_blocks && pb1 >= 0 && pb1 < num_blocks;
+    if (!a.ok) pb0 = pb1 = 0;
+    a.lo = (int64_t)pb0 * blk_bytes + (int64_t)(tok0 & bmask) * row_stride;
+    if (bi1 == bi0) a.hi = a.lo;
+    else if (second) a.hi = (int64_t)pb1 * blk_bytes - 8 * (int64_t)row_stride;
+    else a.hi = a.lo - 8 * (int64_t)row_stride;
+    return a;
+}
+
 // ============================================================================
 // Flat schedule: a persistent grid deals equal ranges of the tile stream.
 // ============================================================================
@@ -468,7 +505,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     int32_t* pre = Ls + S;  // pre[s] = tiles of sequences < s; pre[S] = all tiles
 
     // Tile counts and their prefix sums (every workgroup computes them).
-    const int max_len = p.max_blocks * kBlock;
+    const int max_len = p.max_blocks << p.block_shift;
     for (int i = threadIdx.x; i < S; i += blockDim.x) Ls[i] = min(max(p.context_lens[i], 0), max_len);
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -506,7 +543,6 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
 
     const int lane = threadIdx.x % kWave;
     const uint32_t row_stride = (uint32_t)Hkv * A::RB;
-    const int64_t blk_bytes = (int64_t)row_stride * kBlock;
     const char* kcache = static_cast<const char*>(p.k_cache);
     const char* vcache = static_cast<const char*>(p.v_cache);
 
@@ -548,13 +584,15 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
 
     A a;
     a.init(lane, row_stride, dyn_lds + wave_id_uniform() * A::kLdsBytes);
-    int pbs[NS];
+    bool oks[NS];
+    const int bmask = (1 << p.block_shift) - 1;
     auto issue = [&](int slot, const Cur& q) {
-        int pb = __builtin_amdgcn_readfirstlane(p.block_tables[(int64_t)q.s * p.max_blocks + q.b]);
-        if (pb < 0 || pb >= p.num_blocks) pb = -1;
-        const int64_t boff = pb < 0 ? 0 : (int64_t)pb * blk_bytes;
-        a.issue(slot, kcache + (int64_t)q.kvh * A::NH * A::RB, vcache + (int64_t)q.kvh * A::NH * A::RB, boff);
-        pbs[slot] = pb;
+        const int ntab = (Ls[q.s] + bmask) >> p.block_shift;
+        const TileAddr ta = tile_addr(p.block_tables + (int64_t)q.s * p.max_blocks, q.b, ntab, p.block_shift,
+                                      p.num_blocks, row_stride);
+        a.issue(slot, kcache + (int64_t)q.kvh * A::NH * A::RB, vcache + (int64_t)q.kvh * A::NH * A::RB, ta.lo,
+                ta.hi);
+        oks[slot] = ta.ok;
     };
 
     Cur cur = locate(t0);
@@ -602,8 +640,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
                     a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
                     a.reset();
                 }
-                const int pb = pbs[u];
-                const int valid = pb < 0 ? 0 : (cur.b == cur.nb - 1 ? Ls[cur.s] - cur.b * kBlock : kBlock);
+                const int valid = !oks[u] ? 0 : (cur.b == cur.nb - 1 ? Ls[cur.s] - cur.b * kBlock : kBlock);
                 a.process(u, valid, p.scale_log2);
                 advance(cur);
             }
@@ -682,7 +719,7 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
     const int hg = h / HG;
     const int gi = h % HG;
     char* out_row = static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes;
-    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
+    const int L = min(max(p.context_lens[s], 0), (p.max_blocks << p.block_shift));
     if (L == 0) {
 #pragma unroll
         for (int k = 0; k < PER; ++k)
@@ -724,7 +761,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     char* out_rows = static_cast<char*>(p.out) + ((int64_t)s * Hq + hg * HG) * D * E::kBytes;
     // A length beyond the table is a caller error; clamping keeps every table
     // read inside the row and every partition inside the workspace.
-    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
+    const int L = min(max(p.context_lens[s], 0), (p.max_blocks << p.block_shift));
     const int P = p.part_tokens;
     const int n_parts = (L + P - 1) / P;
 
@@ -741,7 +778,6 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     const int tail_rows = L - (nblk - 1) * kBlock;  // valid rows of the last block, 1..16
 
     const uint32_t row_stride = (uint32_t)p.n_kv_heads * A::RB;
-    const int64_t blk_bytes = (int64_t)row_stride * kBlock;
     const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)hg * A::NH * A::RB;
     const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)hg * A::NH * A::RB;
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
@@ -750,12 +786,12 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     a.init(lane, row_stride, sm_eng + w * A::kLdsBytes);
     a.load_q(static_cast<const char*>(p.q) + ((int64_t)s * Hq + hg * HG) * A::RB);
     a.reset();
-    int pbs[NS];
+    bool oks[NS];
+    const int ntab = (L + (1 << p.block_shift) - 1) >> p.block_shift;
     auto issue = [&](int slot, int bi) {
-        int pb = __builtin_amdgcn_readfirstlane(table[bi]);
-        if (pb < 0 || pb >= p.num_blocks) pb = -1;
-        a.issue(slot, kbase, vbase, pb < 0 ? 0 : (int64_t)pb * blk_bytes);
-        pbs[slot] = pb;
+        const TileAddr ta = tile_addr(table, bi, ntab, p.block_shift, p.num_blocks, row_stride);
+        a.issue(slot, kbase, vbase, ta.lo, ta.hi);
+        oks[slot] = ta.ok;
     };
 
     // Block b_begin + k goes through register slot k % NS, DEPTH blocks ahead.
@@ -768,7 +804,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
             const int b = bi + u;
             if (b + DEPTH < b_end) issue((u + DEPTH) % NS, b + DEPTH);
             if (b < b_end) {
-                const int valid = pbs[u] < 0 ? 0 : (b == nblk - 1 ? tail_rows : kBlock);
+                const int valid = !oks[u] ? 0 : (b == nblk - 1 ? tail_rows : kBlock);
                 a.process(u, valid, p.scale_log2);
             }
         }
@@ -802,7 +838,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     const int pair = blockIdx.x;
     const int s = pair / p.n_q_heads;
     const int h = pair % p.n_q_heads;
-    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
+    const int L = min(max(p.context_lens[s], 0), (p.max_blocks << p.block_shift));
     const int n = (L + p.part_tokens - 1) / p.part_tokens;
     if (n < 2) return;  // uniform over the workgroup
     const int HG = p.n_q_heads / p.n_kv_heads * p.heads_per_wave;  // query heads per record

@@ -22,7 +22,20 @@ namespace {
 thread_local std::string g_last_error;
 std::atomic<int32_t> g_part_tokens{0};
 
-constexpr int kGpuBlockSize = 16;
+constexpr int kGpuBlockSize = 16;  // prefill serves this block size only
+constexpr int kTileTokens = 16;    // the decode kernels stream 16-token tiles
+
+// Block sizes the decode kernels serve: powers of two from 8 to 64 tokens (a
+// 16-token tile then lies in one block, or in two when B = 8).
+int decode_block_shift(int32_t B) {
+    switch (B) {
+        case 8: return 3;
+        case 16: return 4;
+        case 32: return 5;
+        case 64: return 6;
+        default: return -1;
+    }
+}
 constexpr int32_t kDefaultPartTokens = 512;
 constexpr int32_t kMinTilesPerWorker = 4;
 constexpr size_t kWsAlign = 256;
@@ -65,8 +78,8 @@ pkv_status hip_fail(hipError_t e, const char* what) {
 // The flat schedule serves a batch when its per-workgroup LDS holds the batch
 // and its tile count fits comfortably in int32.
 bool flat_fits(int32_t num_seqs, int32_t max_blocks, const pkv_layout* L) {
-    return num_seqs <= pkv::kMaxFlatSeqs &&
-           (int64_t)num_seqs * L->n_kv_heads * max_blocks <= ((int64_t)1 << 30);
+    const int64_t tiles = ((int64_t)max_blocks * L->block_size + kTileTokens - 1) / kTileTokens;
+    return num_seqs <= pkv::kMaxFlatSeqs && (int64_t)num_seqs * L->n_kv_heads * tiles <= ((int64_t)1 << 30);
 }
 
 // 0 (the library's choice) selects the flat schedule: equal tile ranges per
@@ -76,9 +89,10 @@ pkv_status resolve_partition(int32_t requested, int32_t num_seqs, int32_t max_bl
                              int32_t* out) {
     int32_t P = requested;
     if (P == 0) P = g_part_tokens.load();
-    if (P < 0 || P % L->block_size != 0)
-        return fail(PKV_EINVAL, "partition length %d is not a positive multiple of block_size %d", P,
-                    L->block_size);
+    const int32_t unit = std::max<int32_t>(L->block_size, kTileTokens);
+    if (P < 0 || P % unit != 0)
+        return fail(PKV_EINVAL, "partition length %d is not a positive multiple of %d (the block size and 16)", P,
+                    unit);
     if (P == 0 && !flat_fits(num_seqs, max_blocks, L)) P = kDefaultPartTokens;
     *out = P;
     return PKV_OK;
@@ -136,9 +150,8 @@ pkv_status check_decode(const void* q, const void* k_cache, const void* v_cache,
         return fail(PKV_EINVAL, "max_blocks_per_seq * block_size overflows int32");
     if ((int64_t)num_seqs * n_q_heads > INT32_MAX / 4)
         return fail(PKV_EINVAL, "num_seqs * n_q_heads is too large");
-    if (L->block_size != kGpuBlockSize)
-        return fail(PKV_ENOTSUP, "the GPU path serves block_size %d only (got %d)", kGpuBlockSize,
-                    L->block_size);
+    if (decode_block_shift(L->block_size) < 0)
+        return fail(PKV_ENOTSUP, "decode serves block sizes 8, 16, 32 and 64 (got %d)", L->block_size);
     const int group = n_q_heads / L->n_kv_heads;
     if (!pkv::decode_supported(L->dtype, L->head_dim, group))
         return fail(PKV_ENOTSUP, "no kernel for dtype %d, head_dim %d, group %d", L->dtype, L->head_dim,
@@ -171,6 +184,7 @@ pkv::DecodeParams make_params(const void* q, const void* k_cache, const void* v_
     p.num_seqs = num_seqs;
     p.part_tokens = pl.part_tokens;
     p.n_parts_max = pl.n_parts_max;
+    p.block_shift = decode_block_shift(L->block_size);
     p.scale_log2 = scale * 1.4426950408889634f;
     return p;
 }
@@ -335,7 +349,7 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
     if (num_seqs > 0 && max_q_len > 0 && (!q || !k_cache || !v_cache || !block_tables || !cu_q || !context_lens || !out))
         return fail(PKV_EINVAL, "a required pointer is NULL");
     if (layout->block_size != kGpuBlockSize)
-        return fail(PKV_ENOTSUP, "the GPU path serves block_size %d only (got %d)", kGpuBlockSize,
+        return fail(PKV_ENOTSUP, "prefill serves block_size %d only (got %d)", kGpuBlockSize,
                     layout->block_size);
     const int group = n_q_heads / layout->n_kv_heads;
     if (!pkv::prefill_supported(layout->dtype, layout->head_dim, group))
@@ -410,8 +424,8 @@ pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_pe
         return fail(PKV_EINVAL, "bad sizes (num_seqs %d, max_blocks_per_seq %d, n_q_heads %d)", num_seqs,
                     max_blocks_per_seq, n_q_heads);
     if (num_seqs > 0 && (!context_lens || !out)) return fail(PKV_EINVAL, "a required pointer is NULL");
-    if (layout->block_size != kGpuBlockSize)
-        return fail(PKV_ENOTSUP, "the GPU path serves block_size %d only", kGpuBlockSize);
+    if (decode_block_shift(layout->block_size) < 0)
+        return fail(PKV_ENOTSUP, "decode serves block sizes 8, 16, 32 and 64 (got %d)", layout->block_size);
     if (!pkv::decode_supported(layout->dtype, layout->head_dim, n_q_heads / layout->n_kv_heads))
         return fail(PKV_ENOTSUP, "no kernel for dtype %d, head_dim %d", layout->dtype, layout->head_dim);
     int32_t P = 0;
@@ -466,9 +480,9 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
 }
 
 pkv_status pkv_set_partition_tokens(int32_t tokens) {
-    if (tokens < 0 || tokens % kGpuBlockSize != 0)
+    if (tokens < 0 || tokens % kTileTokens != 0)
         return fail(PKV_EINVAL, "partition length %d is not 0 or a positive multiple of %d", tokens,
-                    kGpuBlockSize);
+                    kTileTokens);
     g_part_tokens.store(tokens);
     return PKV_OK;
 }

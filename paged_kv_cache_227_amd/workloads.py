@@ -324,6 +324,24 @@ def long_context(seed: int = SEED_BASE + 5, num_seqs: int = 8) -> Workload:
     return build("long_context", lens, 64, 8, 128, "bf16", seed, pool_factor=1.05, part_tokens=512)
 
 
+def with_block_size(base: str, B: int) -> Workload:
+    """A decode configuration with cache blocks of B tokens instead of 16: the
+    same lengths, head shape, dtype and data; the pool holds the same number of
+    tokens (or, if the coarser blocks waste more, just enough blocks)."""
+    if base == "llama2_7b":
+        lens, seed = _llama_lengths_and_seed(SEED_BASE + 2)
+        need = sum(-(-int(L) // B) for L in lens)
+        return build("llama2_7b_b%d" % B, lens, 32, 32, 128, "f16", seed, num_blocks=max(5120 * 16 // B, need),
+                     block_size=B, data_mult=1.0 / math.sqrt(128.0))
+    if base == "gqa_8b":
+        seed = SEED_BASE + 3
+        r = _lens_rng(seed)
+        prompt = np.clip(np.rint(r.lognormal(math.log(512.0), 1.0, size=256)), 16, 4096).astype(np.int64)
+        gen = r.choice(np.array([8, 16, 32, 64, 128]), size=256)
+        return build("gqa_8b_b%d" % B, prompt + gen, 32, 8, 128, "bf16", seed, pool_factor=1.25, block_size=B)
+    raise ValueError("block-size variants exist for llama2_7b and gqa_8b")
+
+
 CONFIGS = {
     "tiny": tiny,
     "llama2_7b": llama2_7b,
@@ -332,6 +350,10 @@ CONFIGS = {
     "prefix_copied": lambda: prefix_sharing("copied"),
     "long_context": long_context,
 }
+# the block-size sweep: B in {8, 32, 64} next to the 16 of the configurations above
+for _base in ("llama2_7b", "gqa_8b"):
+    for _B in (8, 32, 64):
+        CONFIGS["%s_b%d" % (_base, _B)] = (lambda b=_base, B=_B: with_block_size(b, B))
 
 
 # --------------------------------------------------------------------------

@@ -71,7 +71,9 @@ def test_decode_rejects(L):
     assert _decode(L, _layout(), scale=float("nan")) == _lib.PKV_EINVAL
     assert _decode(L, _layout(), S=-1) == _lib.PKV_EINVAL
     assert _decode(L, _layout(), maxb=0) == _lib.PKV_EINVAL
-    assert _decode(L, _layout(block_size=8)) == _lib.PKV_ENOTSUP
+    assert _decode(L, _layout(block_size=12)) == _lib.PKV_ENOTSUP   # decode serves 8, 16, 32, 64
+    assert _decode(L, _layout(block_size=128)) == _lib.PKV_ENOTSUP
+    assert "block sizes" in _lib.last_error()
     assert _decode(L, _layout(head_dim=96)) == _lib.PKV_ENOTSUP
     assert _decode(L, _layout(), Hq=12) == _lib.PKV_ENOTSUP        # group of 3
     assert _decode(L, _layout(n_kv_heads=1), Hq=16) == _lib.PKV_ENOTSUP
