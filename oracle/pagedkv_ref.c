@@ -411,6 +411,43 @@ int ref_attention_decode(const void* q, const void* k_cache, const void* v_cache
 }
 
 /* ------------------------------------------------------------------------ */
+/* Swap ("How a serving engine actually works", section "When there are no   */
+/* free blocks left"; "Paged Attention and the Block Manager", "Running out  */
+/* of memory becomes a scheduling decision"): a preempted sequence's cache is */
+/* copied to host memory, all of it, and later back into whatever blocks the */
+/* allocator hands out then.  Slot i of the host buffer holds block blocks[i]. */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Swap out: host_k[i] = k_cache[blocks[i]] (whole blocks: B rows of all heads),
+ * and likewise for v; host buffers are [n][B][n_kv_heads][head_dim].  Swap in
+ * (to_cache != 0): k_cache[blocks[i]] = host_k[i].  Bit copies; every block
+ * index is checked before anything is written.
+ */
+int ref_swap(void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+             int32_t head_dim, int dtype, const int32_t* blocks, int32_t n, void* host_k, void* host_v,
+             int to_cache) {
+    const int esz = ref_elt_size(dtype);
+    if (esz == 0 || block_size < 1 || n_kv_heads < 1 || head_dim < 1 || n < 0) return REF_EINVAL;
+    for (int32_t i = 0; i < n; ++i)
+        if (blocks[i] < 0 || blocks[i] >= num_blocks) return REF_EINVAL;
+    const int64_t row_bytes = (int64_t)n_kv_heads * head_dim * esz;
+    for (int32_t i = 0; i < n; ++i)
+        for (int32_t r = 0; r < block_size; ++r) {
+            const int64_t slot = (int64_t)blocks[i] * block_size + r; /* row r of the block */
+            const int64_t h = (int64_t)i * block_size + r;            /* row r of host slot i */
+            if (to_cache) {
+                memcpy((char*)k_cache + slot * row_bytes, (const char*)host_k + h * row_bytes, row_bytes);
+                memcpy((char*)v_cache + slot * row_bytes, (const char*)host_v + h * row_bytes, row_bytes);
+            } else {
+                memcpy((char*)host_k + h * row_bytes, (const char*)k_cache + slot * row_bytes, row_bytes);
+                memcpy((char*)host_v + h * row_bytes, (const char*)v_cache + slot * row_bytes, row_bytes);
+            }
+        }
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Chunked prefill ("How a serving engine actually works", section "Prefill  */
 /* and decode are two different jobs": a long prompt is processed a slice at */
 /* a time; "Paged Attention and the Block Manager", section "The build":     */

@@ -63,6 +63,8 @@ class Oracle:
         L.ref_copy_blocks.restype = ctypes.c_int
         L.ref_append_tokens.argtypes = [P, P, P, P, i32, i32, i32, i32, ctypes.c_int, P, i32, P, P, i32]
         L.ref_append_tokens.restype = ctypes.c_int
+        L.ref_swap.argtypes = [P, P, i32, i32, i32, i32, ctypes.c_int, P, i32, P, P, ctypes.c_int]
+        L.ref_swap.restype = ctypes.c_int
         L.ref_attention_prefill.argtypes = [P, P, P, i32, i32, i32, ctypes.c_int, P, i32, P, P, i32, i32, dbl,
                                             P, i32, P]
         L.ref_attention_prefill.restype = ctypes.c_int
@@ -176,6 +178,33 @@ class Oracle:
             raise ValueError("ref_attention_prefill rejected its arguments (%d)" % rc)
         return out
 
+    def swap_out(self, k_cache, v_cache, blocks, dtype):
+        """Host copies [n][B][Hkv][D] of blocks `blocks` of both caches."""
+        for a in (k_cache, v_cache):
+            _check_store(a, dtype)
+        b = _i32(blocks)
+        hk = np.empty((b.shape[0],) + k_cache.shape[1:], k_cache.dtype)
+        hv = np.empty_like(hk)
+        nb, B, Hkv, D = k_cache.shape
+        rc = self.L.ref_swap(_ptr(k_cache), _ptr(v_cache), nb, B, Hkv, D, dtype, _ptr(b), b.shape[0], _ptr(hk),
+                             _ptr(hv), 0)
+        if rc:
+            raise ValueError("ref_swap rejected its arguments (%d)" % rc)
+        return hk, hv
+
+    def swap_in(self, k_cache, v_cache, blocks, host_k, host_v, dtype):
+        """In place: block blocks[i] of both caches = host slot i."""
+        for a in (k_cache, v_cache, host_k, host_v):
+            _check_store(a, dtype)
+        b = _i32(blocks)
+        nb, B, Hkv, D = k_cache.shape
+        if host_k.shape != (b.shape[0], B, Hkv, D) or host_v.shape != host_k.shape:
+            raise ValueError("host buffers must be [n][B][Hkv][D]")
+        rc = self.L.ref_swap(_ptr(k_cache), _ptr(v_cache), nb, B, Hkv, D, dtype, _ptr(b), b.shape[0],
+                             _ptr(host_k), _ptr(host_v), 1)
+        if rc:
+            raise ValueError("ref_swap rejected its arguments (%d)" % rc)
+
     def gather(self, cache, table_row, length, dtype):
         """Contiguous [Hkv][length][D] float64 copy of one sequence's cache."""
         _check_store(cache, dtype)
@@ -273,6 +302,14 @@ def append_tokens(*a, **k):
 
 def attention_prefill(*a, **k):
     return default().attention_prefill(*a, **k)
+
+
+def swap_out(*a, **k):
+    return default().swap_out(*a, **k)
+
+
+def swap_in(*a, **k):
+    return default().swap_in(*a, **k)
 
 
 def gather(*a, **k):

@@ -556,4 +556,74 @@ def pin_append_tokens_builds_sequential_fill(orc):
     assert np.array_equal(_bits(kc), _bits(want)) and np.array_equal(_bits(vc), _bits(want)), "n-token append"
 
 
+# ---------------------------------------------------------------------------
+# Swap (preemption)
+# ---------------------------------------------------------------------------
+
+def pin_swap_round_trip_out_of_blocks_example(orc):
+    """The pages' full pool ("How a serving engine actually works", section
+    "When there are no free blocks left"), with data: 4 sequences x 2 blocks
+    fill all 8 blocks; the victim (seq-3) is swapped out, its blocks go back to
+    the pool and seq-0's next token lands in one of them; later the victim is
+    swapped back into other blocks.  Its gathered cache is its original rows,
+    and its attention is bit-identical to before the preemption."""
+    g = read_golden("out_of_blocks_b16.txt")
+    B = ints(g["block_size"][0])[0]
+    n_blocks = ints(g["n_blocks"][0])[0]
+    n_seq = ints(g["seqs"][0])[0]
+    L = ints(g["tokens_per_seq"][0])[0]
+    victim = ints(g["preempt"][0])[0]
+    freed = ints(g["free_after_preempt"][0])
+    seq0_after = ints(g["seq0_table_after_append"][0])
+    rng = np.random.default_rng(61)
+    Hkv, D, Hq = 2, 16, 4
+    for dtype in (F32, BF16):
+        # tables as the pages print them: sequence s holds blocks 2s, 2s + 1
+        tables = [[2 * s, 2 * s + 1] for s in range(n_seq)]
+        assert tables[victim] == freed
+        rows = [to_storage(rng.standard_normal((L, Hkv, D)), dtype) for _ in range(n_seq)]
+        kc, vc = _poisoned_pool((n_blocks, B, Hkv, D), dtype), _poisoned_pool((n_blocks, B, Hkv, D), dtype)
+        for s in range(n_seq):
+            sequential_fill(kc, tables[s], rows[s])
+            sequential_fill(vc, tables[s], [r[::-1] for r in rows[s]])
+        q = to_storage(rng.standard_normal((1, Hq, D)), dtype)
+        bt = np.array([tables[victim]], np.int32)
+        before = orc.attention_decode(q, kc, vc, bt, np.array([L], np.int32), 0.3, dtype)
+        hk, hv = orc.swap_out(kc, vc, tables[victim], dtype)
+        # seq-0 grows into the first freed block (its table as printed) and writes token L there
+        assert seq0_after[:2] == tables[0] and seq0_after[2] == freed[0]
+        new_k = to_storage(rng.standard_normal((1, Hkv, D)), dtype)
+        orc.append(new_k, new_k.copy(), kc, vc, np.array([seq0_after], np.int32), np.array([L], np.int32), dtype)
+        # seq-0 and seq-1 finish; the victim comes back into blocks 1 and 2
+        back = [1, 2]
+        orc.swap_in(kc, vc, back, hk, hv, dtype)
+        assert np.array_equal(orc.gather(kc, back, L, dtype), from_storage(rows[victim], dtype).transpose(1, 0, 2))
+        after = orc.attention_decode(q, kc, vc, np.array([back], np.int32), np.array([L], np.int32), 0.3, dtype)
+        assert np.array_equal(before, after), "attention changed across swap-out / swap-in (dtype %d)" % dtype
+        # block 6 now holds seq-0's token in row 0 and the victim's old rows after it, untouched by the swap
+        assert np.array_equal(_bits(kc[freed[0], 0]), _bits(new_k[0]))
+        assert np.array_equal(_bits(kc[freed[0], 1:]), _bits(hk[0, 1:]))
+
+
+def pin_swap_rejects_bad_blocks(orc):
+    k = _poisoned_pool((4, 4, 2, 8), F16)
+    v = k.copy()
+    snap = k.copy()
+    for bad in ([4], [-1], [0, 9]):
+        try:
+            orc.swap_out(k, v, bad, F16)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("swap_out accepted %r" % (bad,))
+    hk, hv = orc.swap_out(k, v, [1, 3], F16)
+    try:
+        orc.swap_in(k, v, [1, 7], hk, hv, F16)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("swap_in accepted block 7 of 4")
+    assert np.array_equal(_bits(k), _bits(snap)), "a rejected swap wrote something"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

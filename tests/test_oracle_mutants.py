@@ -80,6 +80,13 @@ MUTANTS = [
     ("n-token append ignores the start position",
      "ref_physical_slot(row, block_size, (int64_t)start_pos[s] + (j - cu_new[s]));",
      "ref_physical_slot(row, block_size, (int64_t)(j - cu_new[s]));"),
+    ("swap moves one row too few", "        for (int32_t r = 0; r < block_size; ++r) {\n            const int64_t slot = (int64_t)blocks[i] * block_size + r; /* row r of the block */",
+     "        for (int32_t r = 0; r < block_size - 1; ++r) {\n            const int64_t slot = (int64_t)blocks[i] * block_size + r; /* row r of the block */"),
+    ("swap ignores the block list", "const int64_t slot = (int64_t)blocks[i] * block_size + r; /* row r of the block */",
+     "const int64_t slot = (int64_t)i * block_size + r; /* row r of the block */"),
+    ("swap in writes the host slot into every row's first slot",
+     "const int64_t h = (int64_t)i * block_size + r;            /* row r of host slot i */",
+     "const int64_t h = (int64_t)i * block_size;            /* row r of host slot i */"),
     ("n-token append repeats the chunk's first row",
      "memcpy((char*)k_cache + slot * row_bytes, (const char*)k_new + j * row_bytes, row_bytes);",
      "memcpy((char*)k_cache + slot * row_bytes, (const char*)k_new + cu_new[s] * row_bytes, row_bytes);"),
