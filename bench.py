@@ -451,6 +451,121 @@ def main_prefill(a):
     return 0
 
 
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, each direction
+
+
+def run_swap(cw, steps, warmup):
+    """Time the swap round trip (swap-out, then swap-in) of the workload's
+    blocks: `steps` round trips between two synchronisations, then each call
+    again with HIP events; also a contiguous DMA copy of the same bytes
+    (hipMemcpyAsync through torch) each way, for reference."""
+    import torch
+    import paged_kv_cache_227_amd as P
+    shape = (cw.num_blocks, cw.block_size, cw.n_kv_heads, cw.head_dim)
+    kc = torch.zeros(shape, dtype=torch.float16, device="cuda:0")
+    vc = torch.zeros_like(kc)
+    blocks = torch.from_numpy(cw.src).to("cuda:0")
+    hk = torch.empty((len(cw.src),) + shape[1:], dtype=torch.float16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        P.paged_kv_swap_out(kc, vc, blocks, hk, hv)
+        if ev:
+            ev[1].record()
+        P.paged_kv_swap_in(kc, vc, blocks, hk, hv)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        step(e)
+    torch.cuda.synchronize()
+    t_out = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
+    t_in = statistics.fmean(e[1].elapsed_time(e[2]) for e in ev)
+    # reference: one contiguous buffer of the same size, each way, on the DMA engine
+    dev = torch.empty(2 * hk.numel(), dtype=torch.float16, device="cuda:0")
+    host = torch.empty(2 * hk.numel(), dtype=torch.float16, pin_memory=True)
+    for _ in range(2):
+        host.copy_(dev, non_blocking=True)
+        dev.copy_(host, non_blocking=True)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    host.copy_(dev, non_blocking=True)
+    e[1].record()
+    dev.copy_(host, non_blocking=True)
+    e[2].record()
+    torch.cuda.synchronize()
+    dma_out, dma_in = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    del kc, vc, hk, hv, dev, host
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms_step, out_ms=t_out, in_ms=t_in, dma_out_ms=dma_out, dma_in_ms=dma_in)
+
+
+def cpu_baseline_swap(cw, min_s=3.0):
+    """The oracle's swap (out, then in) on host copies of the caches."""
+    import numpy as np
+    from oracle import ref
+    orc = ref.default()
+    shape = (cw.num_blocks, cw.block_size, cw.n_kv_heads, cw.head_dim)
+    kc, vc = np.zeros(shape, np.uint16), np.zeros(shape, np.uint16)
+    n, elapsed = 0, 0.0
+    while elapsed < min_s:
+        t0 = time.perf_counter()
+        hk, hv = orc.swap_out(kc, vc, cw.src, 1)
+        orc.swap_in(kc, vc, cw.dst, hk, hv, 1)
+        elapsed += time.perf_counter() - t0
+        n += 1
+    return {"value": 2 * 2 * cw.moved_bytes() * n / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d round trips of %d blocks, %.1f s" % (n, len(cw.src), elapsed)}
+
+
+def main_swap(a):
+    from paged_kv_cache_227_amd import workloads as W
+    if a.config not in W.SWAP_CONFIGS:
+        raise SystemExit("swap workloads: %s" % ", ".join(W.SWAP_CONFIGS))
+    cw = W.SWAP_CONFIGS[a.config]()
+    each_way = cw.moved_bytes()  # both caches' blocks, one direction
+    log("swap workload %s: %d blocks, %.1f MB each way" % (cw.name, len(cw.src), each_way / 1e6))
+    g = run_swap(cw, a.steps, a.warmup)
+    gbs = lambda ms: each_way / (ms * 1e-3) / 1e9
+    log("gpu: %.3f ms per round trip; out %.3f ms (%.1f GB/s), in %.3f ms (%.1f GB/s); DMA %.1f / %.1f GB/s"
+        % (g["ms_per_step"], g["out_ms"], gbs(g["out_ms"]), g["in_ms"], gbs(g["in_ms"]), gbs(g["dma_out_ms"]),
+           gbs(g["dma_in_ms"])))
+    achieved = 2 * each_way / ((g["out_ms"] + g["in_ms"]) * 1e-3) / 1e9  # per direction, over both launches
+    res = {
+        "metric": "paged KV swap (preemption): bytes moved per second over the host link, out + in",
+        "value": round(2 * each_way / (g["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(g["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cw.dtype, "data": "synthetic",
+        "config": {"workload": cw.name, "n_blocks": int(len(cw.src)), "bytes_each_way": each_way,
+                   "num_blocks": cw.num_blocks, "n_kv_heads": cw.n_kv_heads, "head_dim": cw.head_dim,
+                   "block_size": cw.block_size, "seed": cw.seed, "notes": cw.notes},
+        "roofline": {"bound": "host_link", "achieved": round(achieved, 2), "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HOST_LINK_PEAK_GBS, 4), "traffic": None, "kernel": "swap_kernel",
+                     "algorithmic_bytes_per_launch": each_way,
+                     "timing": "HIP events around each launch, %d round trips after the timed region" % a.steps,
+                     "mean_launch_ms": {"out": round(g["out_ms"], 4), "in": round(g["in_ms"], 4)}},
+        "swap_out_gbs": round(gbs(g["out_ms"]), 2), "swap_in_gbs": round(gbs(g["in_ms"]), 2),
+        "dma_reference_gbs": {"out": round(gbs(g["dma_out_ms"]), 2), "in": round(gbs(g["dma_in_ms"]), 2),
+                              "what": "one contiguous buffer of the same size, hipMemcpyAsync"},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_swap(cw)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def summarize_pmc(d):
     """Mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from rocprofv3
     --pmc CSV output under directory d."""
@@ -509,9 +624,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "prefill"],
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "prefill", "swap"],
                     help="decode: the append + decode step (default); copy_blocks: the copy-on-write block "
-                         "copy; prefill: the chunked-prefill step (n-token append + attention)")
+                         "copy; prefill: the chunked-prefill step (n-token append + attention); swap: a "
+                         "preempted sequence's blocks out to pinned host memory and back")
     ap.add_argument("--config", default=None,
                     help="workload (default llama2_7b for decode, copy_whole_llama2_7b for copy_blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -528,7 +644,7 @@ def main():
     a = ap.parse_args()
     if a.config is None:
         a.config = {"decode": "llama2_7b", "copy_blocks": "copy_whole_llama2_7b",
-                    "prefill": "prefill_llama2_7b"}[a.op]
+                    "prefill": "prefill_llama2_7b", "swap": "swap_llama2_7b"}[a.op]
 
     if a.summarize_pmc:
         print(json.dumps(summarize_pmc(a.summarize_pmc), indent=1))
@@ -562,6 +678,8 @@ def main():
         return main_copy(a)
     if a.op == "prefill":
         return main_prefill(a)
+    if a.op == "swap":
+        return main_swap(a)
 
     t = time.perf_counter()
     w = make_workload(a.config)

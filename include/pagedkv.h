@@ -9,8 +9,9 @@
  *              values, read in place through the block table;
  *
  * and, next to them, the block copy that copy-on-write needs before an append
- * into a block that another sequence also holds, and the chunked-prefill pair
- * (an n-token append and the attention of a chunk of queries).
+ * into a block that another sequence also holds, the chunked-prefill pair
+ * (an n-token append and the attention of a chunk of queries), and the swap
+ * of a preempted sequence's blocks to host memory and back.
  *
  * Append and decode use the address translation of "How a serving engine actually works"
  * (paperfordummies.in), section "The one formula":
@@ -110,6 +111,37 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_cache, 
                            const pkv_layout* layout, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* positions, int32_t num_seqs,
                            void* stream);
+
+/*
+ * paged_kv_swap_out / paged_kv_swap_in -- swap a preempted sequence's cache.
+ *
+ * When no block is free and no sequence can grow, a victim is preempted whole
+ * and comes back later either by recomputing its cache (prefill) or by having
+ * its blocks swapped to host memory and back ("How a serving engine actually
+ * works", paperfordummies.in, section "When there are no free blocks left";
+ * "Paged Attention and the Block Manager", snowch.github.io ch08, "Running out
+ * of memory becomes a scheduling decision": swapping costs bandwidth, twice).
+ *
+ *   swap_out:  host_k[i] = k_cache[blocks[i]], host_v[i] = v_cache[blocks[i]]
+ *   swap_in:   k_cache[blocks[i]] = host_k[i], v_cache[blocks[i]] = host_v[i]
+ *
+ * whole blocks, bit-exact; swap-in may target other blocks than the ones
+ * swapped out (the host allocator hands out whatever is free).
+ *
+ *   blocks          [n] int32 device array of physical blocks
+ *   host_k, host_v  PINNED host buffers (hipHostMalloc, or a pinned torch
+ *                   tensor) of n blocks each: [n][block_size][n_kv_heads][head_dim];
+ *                   owned by the caller, who must not touch them until the
+ *                   call's work on `stream` has completed
+ *
+ * The GPU moves the data through the device mapping of the host buffers, so
+ * scattered blocks need no staging.  A block index outside the pool skips its
+ * slot.  PKV_EINVAL for memory that is not pinned host memory.
+ */
+pkv_status paged_kv_swap_out(const void* k_cache, const void* v_cache, const pkv_layout* layout,
+                             const int32_t* blocks, int32_t n, void* host_k, void* host_v, void* stream);
+pkv_status paged_kv_swap_in(void* k_cache, void* v_cache, const pkv_layout* layout, const int32_t* blocks,
+                            int32_t n, const void* host_k, const void* host_v, void* stream);
 
 /*
  * Chunked prefill ("How a serving engine actually works", paperfordummies.in,

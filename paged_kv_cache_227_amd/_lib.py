@@ -49,6 +49,8 @@ SIGNATURES = {
     "paged_kv_append_tokens": (ctypes.c_int, [_P, _P, _P, _P, _LP, _P, _I32, _P, _P, _I32, _I32, _P]),
     "paged_attention_prefill": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _P, _I32, _I32, _I32, _F32, _P, _P]),
     "pkv_validate_prefill": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _I32, _I32]),
+    "paged_kv_swap_out": (ctypes.c_int, [_P, _P, _LP, _P, _I32, _P, _P, _P]),
+    "paged_kv_swap_in": (ctypes.c_int, [_P, _P, _LP, _P, _I32, _P, _P, _P]),
     "pkv_validate_copies": (ctypes.c_int, [_LP, _P, _P, _P, _I32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
@@ -228,6 +230,42 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, cu_q, context_len
            "paged_attention_prefill")
 
 
+def _pinned(t, name):
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("%s must be a pinned host tensor (pin_memory=True)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _swap_args(k_cache, v_cache, blocks, host_k, host_v):
+    _check_caches(k_cache, v_cache)
+    L = layout_of(k_cache)
+    if blocks.dim() != 1:
+        raise ValueError("blocks must be a vector")
+    want = (blocks.shape[0],) + tuple(k_cache.shape[1:])
+    for t, name in ((host_k, "host_k"), (host_v, "host_v")):
+        if tuple(t.shape) != want or t.dtype != k_cache.dtype:
+            raise ValueError("%s must be %r of the cache dtype" % (name, want))
+    return L
+
+
+def paged_kv_swap_out(k_cache, v_cache, blocks, host_k, host_v, stream=None) -> None:
+    """host_k[i] = k_cache[blocks[i]] (and v): whole blocks into pinned host tensors."""
+    L = _swap_args(k_cache, v_cache, blocks, host_k, host_v)
+    _check(lib().paged_kv_swap_out(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L),
+                                   _i32(blocks, "blocks"), blocks.shape[0], _pinned(host_k, "host_k"),
+                                   _pinned(host_v, "host_v"), _stream(stream, k_cache.device)), "paged_kv_swap_out")
+
+
+def paged_kv_swap_in(k_cache, v_cache, blocks, host_k, host_v, stream=None) -> None:
+    """k_cache[blocks[i]] = host_k[i] (and v): whole blocks from pinned host tensors."""
+    L = _swap_args(k_cache, v_cache, blocks, host_k, host_v)
+    _check(lib().paged_kv_swap_in(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L),
+                                  _i32(blocks, "blocks"), blocks.shape[0], _pinned(host_k, "host_k"),
+                                  _pinned(host_v, "host_v"), _stream(stream, k_cache.device)), "paged_kv_swap_in")
+
+
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
     _check_caches(k_cache, v_cache)
     L = layout_of(k_cache)
@@ -371,6 +409,12 @@ class PagedKVCache:
     def prefill(self, q, block_tables, cu_q, context_lens, scale, out, max_q_len, stream=None) -> None:
         paged_attention_prefill(q, self.k_cache, self.v_cache, block_tables, cu_q, context_lens, scale, out,
                                 max_q_len, stream)
+
+    def swap_out(self, blocks, host_k, host_v, stream=None) -> None:
+        paged_kv_swap_out(self.k_cache, self.v_cache, blocks, host_k, host_v, stream)
+
+    def swap_in(self, blocks, host_k, host_v, stream=None) -> None:
+        paged_kv_swap_in(self.k_cache, self.v_cache, blocks, host_k, host_v, stream)
 
     def copy_blocks(self, src_blocks, dst_blocks, n_rows, stream=None) -> None:
         paged_kv_copy_blocks(self.k_cache, self.v_cache, src_blocks, dst_blocks, n_rows, stream)

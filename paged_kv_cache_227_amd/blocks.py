@@ -163,6 +163,25 @@ class Sequence:
         child.n_tokens = self.n_tokens
         return child
 
+    def preempt_swap(self) -> List[int]:
+        """Preemption by swapping, all or nothing: the blocks whose contents the
+        caller copies to host memory (table order), after which every one is
+        released.  The tokens stay (``n_tokens`` is kept); only the cache leaves."""
+        blocks = list(self.table)
+        for b in blocks:
+            self.alloc.free_block(b)
+        self.table = []
+        return blocks
+
+    def resume_swapped(self, n_blocks: int) -> List[int]:
+        """Fresh blocks for a swapped-out sequence, all or none; host slot i goes
+        into the i-th returned block.  Blocks it once shared come back private."""
+        if n_blocks != self.alloc.blocks_needed(self.n_tokens):
+            raise ValueError("a swapped-out sequence of %d tokens needs %d blocks, not %d"
+                             % (self.n_tokens, self.alloc.blocks_needed(self.n_tokens), n_blocks))
+        self.table = self.alloc.allocate(n_blocks)
+        return list(self.table)
+
     def release(self) -> None:
         for b in self.table:
             self.alloc.free_block(b)

@@ -2,7 +2,7 @@
 // checks, dtype / head_dim / group dispatch, split-K planning, the library's
 // workspace, status codes and the per-thread error message.  Host code only;
 // every step of the path runs in the kernels of append.hip, copy_blocks.hip,
-// decode.hip and prefill.hip.
+// decode.hip, prefill.hip and swap.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -377,6 +377,58 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
     hipError_t e = pkv::launch_prefill(p, layout->dtype, layout->head_dim, group, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return ok();
+}
+
+namespace {
+
+// Device view of a pinned host buffer, or an error for memory that is not.
+pkv_status device_view_of_host(const void* host, void** dev, const char* name) {
+    hipError_t e = hipHostGetDevicePointer(dev, const_cast<void*>(host), 0);
+    if (e != hipSuccess || !*dev) {
+        (void)hipGetLastError();  // clear the sticky error of the failed lookup
+        return fail(PKV_EINVAL, "%s is not pinned host memory (allocate it with hipHostMalloc)", name);
+    }
+    return PKV_OK;
+}
+
+pkv_status swap_common(void* k_cache, void* v_cache, const pkv_layout* layout, const int32_t* blocks, int32_t n,
+                       const void* host_k, const void* host_v, bool to_cache, void* stream) {
+    pkv_status st = check_layout(layout);
+    if (st != PKV_OK) return st;
+    if (n < 0) return fail(PKV_EINVAL, "n %d < 0", n);
+    if (n == 0) return ok();
+    if (!k_cache || !v_cache || !blocks || !host_k || !host_v) return fail(PKV_EINVAL, "a required pointer is NULL");
+    const int64_t blk_bytes =
+        (int64_t)layout->block_size * layout->n_kv_heads * layout->head_dim * elt_bytes(layout->dtype);
+    if (blk_bytes % 16 != 0) return fail(PKV_ENOTSUP, "a block of %lld bytes is not a multiple of 16", (long long)blk_bytes);
+    pkv::SwapParams p{};
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.blocks = blocks;
+    st = device_view_of_host(host_k, &p.host_k, "host_k");
+    if (st != PKV_OK) return st;
+    st = device_view_of_host(host_v, &p.host_v, "host_v");
+    if (st != PKV_OK) return st;
+    p.num_blocks = layout->num_blocks;
+    p.n = n;
+    p.blk_bytes = blk_bytes;
+    hipError_t e = pkv::launch_swap(p, to_cache, static_cast<hipStream_t>(stream));
+    if (e == hipErrorInvalidConfiguration) return fail(PKV_EINVAL, "%d blocks exceed the launch grid", n);
+    if (e != hipSuccess) return hip_fail(e, "swap launch");
+    return ok();
+}
+
+}  // namespace
+
+pkv_status paged_kv_swap_out(const void* k_cache, const void* v_cache, const pkv_layout* layout,
+                             const int32_t* blocks, int32_t n, void* host_k, void* host_v, void* stream) {
+    return swap_common(const_cast<void*>(k_cache), const_cast<void*>(v_cache), layout, blocks, n, host_k, host_v,
+                       false, stream);
+}
+
+pkv_status paged_kv_swap_in(void* k_cache, void* v_cache, const pkv_layout* layout, const int32_t* blocks,
+                            int32_t n, const void* host_k, const void* host_v, void* stream) {
+    return swap_common(k_cache, v_cache, layout, blocks, n, host_k, host_v, true, stream);
 }
 
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks_per_seq,

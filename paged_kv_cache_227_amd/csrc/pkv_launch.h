@@ -54,6 +54,18 @@ struct PrefillParams {
     float scale_log2;   // scale * log2(e)
 };
 
+struct SwapParams {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* blocks;  // [n]: the block of each host slot
+    void* host_k;           // device view of pinned host buffers [n][block bytes]
+    void* host_v;
+    int32_t num_blocks;
+    int32_t n;
+    int32_t chunks;     // workgroups per block (set by the launcher)
+    int64_t blk_bytes;  // block_size * n_kv_heads * head_dim * element bytes (a multiple of 16)
+};
+
 struct CopyParams {
     void* k_cache;
     void* v_cache;
@@ -106,6 +118,7 @@ struct DecodeParams {
 // Each returns hipSuccess or the launch error.  dtype: 0 f32, 1 f16, 2 bf16.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
+hipError_t launch_swap(SwapParams p, bool to_cache, hipStream_t stream);
 hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int group, hipStream_t stream);
 bool prefill_supported(int dtype, int head_dim, int group);

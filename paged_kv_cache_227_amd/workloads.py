@@ -535,6 +535,22 @@ def copy_whole_llama2_7b(n: int = 2048, seed: int = SEED_BASE + 6) -> CopyWorklo
                         np.full(n, BLOCK_SIZE, np.int32), seed)
 
 
+def swap_llama2_7b(n_victims: int = 8, seed: int = SEED_BASE + 2) -> CopyWorkload:
+    """Preemption by swapping on the Llama-2-7B layer: the `n_victims` longest of
+    its 64 sequences are swapped out (all their blocks, in table order) and back.
+    src = the blocks swapped out; dst = the blocks swapped back into (the same
+    ones here: the pool is otherwise idle); rows = whole blocks."""
+    w = llama2_7b(seed)
+    order = np.argsort(-w.context_lens, kind="stable")[:n_victims]
+    blocks = np.concatenate([w.block_tables[s][w.block_tables[s] >= 0] for s in order]).astype(np.int32)
+    return CopyWorkload("swap_llama2_7b", "f16", 32, 128, BLOCK_SIZE, w.num_blocks, blocks, blocks.copy(),
+                        np.full(len(blocks), BLOCK_SIZE, np.int32), seed,
+                        notes="the %d longest sequences (%d tokens)" % (n_victims, int(w.context_lens[order].sum())))
+
+
+SWAP_CONFIGS = {"swap_llama2_7b": swap_llama2_7b}
+
+
 COPY_CONFIGS = {
     "cow_llama2_7b": cow_llama2_7b,
     "copy_whole_llama2_7b": copy_whole_llama2_7b,

@@ -212,3 +212,14 @@ def test_validate_prefill(L):
     bt2[0, 1] = 10
     with pytest.raises(ValueError, match="outside"):
         _lib.validate_prefill(lay, bt2, [0, 3, 8], [10, 16], 8)
+
+
+def test_swap_rejects(L):
+    lay = _layout()
+    args = [FAKE, FAKE, ctypes.byref(lay), FAKE, 3, FAKE, FAKE, None]
+    assert L.paged_kv_swap_out(None, *args[1:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_swap_in(*args[:3], None, *args[4:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_swap_out(*args[:4], -1, *args[5:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_swap_in(*args[:5], None, FAKE, None) == _lib.PKV_EINVAL
+    assert L.paged_kv_swap_out(*args[:2], ctypes.byref(_layout(dtype=5)), *args[3:]) == _lib.PKV_EINVAL
+    assert L.paged_kv_swap_out(*args[:4], 0, *args[5:]) == _lib.PKV_OK   # nothing to move

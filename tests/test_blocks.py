@@ -141,3 +141,32 @@ def test_random_traffic_never_leaks(ops, B):
     for s in live:
         s.release()
     assert alloc.is_whole()
+
+
+def test_swap_preemption_out_of_blocks_example():
+    """The pages' full pool, preempted by swapping: the victim's two blocks are
+    returned (and handed to seq-0's next block), the victim keeps its tokens,
+    and it resumes into fresh blocks once others finish."""
+    g = read_golden("out_of_blocks_b16.txt")
+    B = ints(g["block_size"][0])[0]
+    alloc = BlockAllocator(ints(g["n_blocks"][0])[0], B)
+    seqs = [Sequence("seq-%d" % i, alloc) for i in range(ints(g["seqs"][0])[0])]
+    for s in seqs:
+        s.append_tokens(ints(g["tokens_per_seq"][0])[0])
+    victim = seqs[ints(g["preempt"][0])[0]]
+    swapped = victim.preempt_swap()
+    assert swapped == ints(g["free_after_preempt"][0]) and alloc.free_list == swapped
+    assert victim.n_tokens == ints(g["tokens_per_seq"][0])[0] and victim.table == []
+    seqs[0].append_tokens(1)
+    assert seqs[0].table == ints(g["seq0_table_after_append"][0])
+    with pytest.raises(OutOfBlocks):
+        victim.resume_swapped(len(swapped))       # nothing free yet
+    assert victim.table == []
+    with pytest.raises(ValueError):
+        victim.resume_swapped(len(swapped) + 1)
+    seqs[1].release()
+    back = victim.resume_swapped(len(swapped))
+    assert len(back) == len(swapped) and victim.table == back
+    for s in seqs:
+        s.release()
+    assert alloc.is_whole()
