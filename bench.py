@@ -159,7 +159,21 @@ def run_gpu(w, steps, warmup, extras, graph=False):
         s1.record()
         torch.cuda.synchronize()
         res["probe_read_gbs"] = buf.numel() * 10 / (s0.elapsed_time(s1) * 1e-3) / 1e9
-        del buf, sink
+        # the decode kernel after a flush: a 2 GiB copy (8x the 256 MB last-level
+        # cache) before each launch, so no K/V byte can be served from cache
+        src, dst = buf[:1 << 30], buf[1 << 30:2 << 30]
+        t_fl = []
+        for _ in range(10):
+            P.probe_copy(src, dst)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            P.paged_attention_partitions(q, kc, vc, bt, lens, w.scale, out, part, ws)
+            e1.record()
+            P.paged_attention_merge(kc, bt, lens, out, part, ws)
+            torch.cuda.synchronize()
+            t_fl.append(e0.elapsed_time(e1))
+        res["partition_ms_flushed_median"] = statistics.median(t_fl)
+        del buf, sink, src, dst
     del T, q, kc, vc, out, ws
     torch.cuda.empty_cache()
     return res
@@ -719,6 +733,7 @@ def main():
     if not a.no_extras:
         from paged_kv_cache_227_amd import workloads as W
         res["probe_read_gbs"] = round(g["probe_read_gbs"], 1)
+        res["decode_kernel_gbs_after_flush"] = round(kv / (g["partition_ms_flushed_median"] * 1e-3) / 1e9, 1)
         if a.config == "llama2_7b":
             import math
             lens = w.context_lens

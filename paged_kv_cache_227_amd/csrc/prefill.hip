@@ -125,7 +125,7 @@ __device__ __forceinline__ uint32_t tile_pos(int row, int chunk) {
 
 // One iteration covers NB consecutive blocks: their K and V tiles are loaded
 // together (one iteration ahead) and one softmax rescale covers all NB x 16 keys.
-template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT>
+template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int PD>
 __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
     using SH = PrefillShape<E, D, G, NW, NQ, NB>;
     using OPS = MfmaOps<E>;
@@ -201,8 +201,9 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
         c_row[k] = (ee / CH) % kBlock;
         c_col[k] = ee % CH;
     }
-    Vec16 pre[SH::PER_T];
-    auto fetch = [&](int it) {
+    // register ring: slot d holds the loads of an iteration PD ahead of the compute
+    Vec16 pre[PD][SH::PER_T];
+    auto fetch = [&](int it, Vec16(&dst)[SH::PER_T]) {
         // the iteration's table entries first (uniform loads), then every chunk load in flight at once
         int pbs[NB];
 #pragma unroll
@@ -219,23 +220,19 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
             const int b = it * NB + c_nb[k];
             const bool ok = pb >= 0 && c_row[k] < L - b * kBlock;  // rows of the block inside the sequence
             const char* base = tid + k * SH::NT < PER_CACHE ? kbase : vbase;
-            pre[k] = ok ? load16(base + (int64_t)pb * blk_bytes + (int64_t)c_row[k] * row_stride + c_col[k] * 16)
+            dst[k] = ok ? load16(base + (int64_t)pb * blk_bytes + (int64_t)c_row[k] * row_stride + c_col[k] * 16)
                         : Vec16{{0u, 0u, 0u, 0u}};
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int buf, const Vec16(&src)[SH::PER_T]) {
 #pragma unroll
         for (int k = 0; k < SH::PER_T; ++k)
             lds_store16(lds[buf][tid + k * SH::NT < PER_CACHE ? 0 : 1] + c_nb[k] * SH::TILE,
-                        tile_pos<RB>(c_row[k], c_col[k]), pre[k]);
+                        tile_pos<RB>(c_row[k], c_col[k]), src[k]);
     };
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int it = 0; it < nit; ++it) {
+    auto compute = [&](int it) {
         const int buf = it & 1;
-        if (it + 1 < nit) fetch(it + 1);
         const int b0 = it * NB;
         if (b0 * kBlock <= wave_last_pos) {
             const char* kl = lds[buf][0];
@@ -310,8 +307,25 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
                 }
             }
         }
-        if (it + 1 < nit) stash(buf ^ 1);
-        __syncthreads();
+    };
+
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+        if (d < nit) fetch(d, pre[d]);
+    stash(0, pre[0]);
+    __syncthreads();
+    for (int it0 = 0; it0 < nit; it0 += PD) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int it = it0 + d;
+            if (it < nit) {  // uniform over the workgroup
+                // slot d's iteration is in LDS already: refill it PD iterations ahead
+                if (it + PD < nit) fetch(it + PD, pre[d]);
+                compute(it);
+                if (it + 1 < nit) stash((it + 1) & 1, pre[(d + 1) % PD]);
+                __syncthreads();
+            }
+        }
     }
 
     // Each lane summed its own 4 keys per block: add the other lane groups.
@@ -331,13 +345,13 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
     }
 }
 
-template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT>
+template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int PD>
 hipError_t launch_prefill_shape(const PrefillParams& p, hipStream_t stream) {
     constexpr int ROWS = NW * 16 * NQ;
     const int64_t tiles = ((int64_t)p.max_q_len * G + ROWS - 1) / ROWS;
     if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles, p.n_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, NB, SPLIT>), grid, dim3(NW * kWave), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, NB, SPLIT, PD>), grid, dim3(NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -351,7 +365,7 @@ template <class E, int D, int G>
 static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
     constexpr int NB = D == 128 ? 2 : 4;
     constexpr bool SPLIT = std::is_same<E, BF16>::value;
-    return launch_prefill_shape<E, D, G, 8, 1, NB, SPLIT>(p, stream);
+    return launch_prefill_shape<E, D, G, 8, 1, NB, SPLIT, 1>(p, stream);
 }
 
 template <class E, int D>
