@@ -6,6 +6,10 @@
 //     B lane l = B[8(l/16) .. +7][l % 16], C lane l = C[4(l/16) + r][l % 16];
 //   v_mfma_f32_16x16x16{bf16_1k,f16}: the same with 4 instead of 8, so the C
 //     layout of a 16x16 product is the B layout of the next one;
+//   the order of the contracted index inside one product is free as long as
+//     A and B agree, so two 4-element halves (from two 16x16 C tiles) make the
+//     8 elements of a 16x16x32 operand (pv2), which on gfx950 does twice the
+//     work of a 16x16x16 in the same issue time;
 //   ds_read_b64_tr_b16: within each 16-lane group, element r of lane j is
 //     element j % 4 of the 8-byte row (4r + j / 4) of the 4 x 16 block read.
 #pragma once
@@ -36,6 +40,12 @@ struct MfmaOps<BF16> {
     __device__ static __forceinline__ f32x4_t pv(op4_t a, op4_t b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
     }
+    // One 16x16x32 product over two 4-key halves: A = (a0, a1), B = (b0, b1).
+    __device__ static __forceinline__ f32x4_t pv2(op4_t a0, op4_t a1, op4_t b0, op4_t b1, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(v8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7)),
+            __builtin_bit_cast(v8_t, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7)), c, 0, 0, 0);
+    }
     __device__ static __forceinline__ void split(float x, short& hi, short& lo) {
         const __bf16 h = (__bf16)x;
         hi = __builtin_bit_cast(short, h);
@@ -59,6 +69,11 @@ struct MfmaOps<F16> {
     }
     __device__ static __forceinline__ f32x4_t pv(op4_t a, op4_t b, f32x4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4_t pv2(op4_t a0, op4_t a1, op4_t b0, op4_t b1, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                      __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, 0,
+                                                      0, 0);
     }
     __device__ static __forceinline__ void split(float x, short& hi, short& lo) {
         const _Float16 h = (_Float16)x;

@@ -29,11 +29,12 @@
 //                      group's q rows as B, held in registers),
 //     the prefix-causal mask (key position <= the row's position) by select,
 //     an online softmax per row in base-2 units (each row's state lives in one
-//     lane column), then
-//       O^T += V^T P^T (v_mfma_f32_16x16x16, V^T read transposed from LDS,
-//                      P^T straight from S^T's accumulator layout),
-//     with P split into high and low 16-bit parts so about 16 bits of each
-//     weight survive;
+//     lane column), then, for each pair of blocks,
+//       O^T += V^T P^T (v_mfma_f32_16x16x32, V^T read transposed from LDS,
+//                      P^T straight from S^T's accumulator layout; the two
+//                      blocks' 4-key lane slices make the 8 contraction slots),
+//     with P split into high and low 16-bit parts for bf16 so about 16 bits of
+//     each weight survive;
 //   * blocks wholly past a wave's last position are skipped by that wave;
 //     tiles are started longest first (the last rows see the most keys).
 // Rows past L in a sequence's last block are loaded as zeros, so whatever
@@ -112,7 +113,12 @@ struct PrefillShape {
     static constexpr int PER_T = (NCH + NT - 1) / NT;
     static_assert(E::kBytes == 2 && D % 32 == 0 && CH == 4 * KK, "16-bit caches, head_dim a multiple of 32");
     static_assert(NCH % NT == 0, "every thread moves the same number of chunks");
+    static_assert(NB % 2 == 0, "PV takes blocks in pairs");
 };
+
+// Headroom of the online softmax's reference maximum (log2 units): weights
+// reach at most 2^8, well inside fp16 and bf16 range.
+constexpr float kLazy = 8.f;
 
 // Position of (row, 16-byte chunk) in an LDS tile of one head: rows of RB
 // bytes, chunks XOR-swizzled by row so that transposed and row reads spread
@@ -126,7 +132,7 @@ __device__ __forceinline__ uint32_t tile_pos(int row, int chunk) {
 // One iteration covers NB consecutive blocks: their K and V tiles are loaded
 // together (one iteration ahead) and one softmax rescale covers all NB x 16 keys.
 template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int PD>
-__global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p) {
     using SH = PrefillShape<E, D, G, NW, NQ, NB>;
     using OPS = MfmaOps<E>;
     using op4_t = typename OPS::op4_t;
@@ -158,7 +164,14 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
     const int jq = lane % 16;
     const int wr0 = r0 + w * SH::ROWS_W;  // this wave's first row
     const int wave_last_pos = wr0 < nrows ? ctx + (min(wr0 + SH::ROWS_W, nrows) - 1) / G : -1;
+    const int wave_first_pos = ctx + wr0 / G;
 
+    // The softmax below needs a positive scale: a negative one moves into q's
+    // sign bits (exact), and a zero one becomes the smallest normal float,
+    // which leaves every weight at exactly 1 as zero would (|score| x 2^-126
+    // is far below half an ulp of 1 for any 16-bit q and K).
+    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+    const float scale_log2 = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
     // q rows of this wave: group c, column jq is row wr0 + 16c + jq.
     Vec16 qf[NQ][KK];
     int qpos[NQ];
@@ -171,8 +184,11 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
         const char* qrow = static_cast<const char*>(p.q) +
                            (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
+        for (int kk = 0; kk < KK; ++kk) {
             qf[c][kk] = ok ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qf[c][kk].w[e] ^= qsign;
+        }
     }
     float m[NQ], l[NQ];
     f32x4_t acc[NQ][TT];
@@ -238,11 +254,27 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
             const char* kl = lds[buf][0];
             const char* vl = lds[buf][1];
             // scores: lane (gq, jq) holds keys (b0 + nb) * 16 + 4gq + r of row column jq
+            // The prefix-causal mask enters as the products' initial value (0,
+            // or -inf for a key past the row's position), built only in the
+            // iterations that hold such keys for some row of the wave.
             f32x4_t sacc[NQ][NB];
+            if ((b0 + NB) * kBlock - 1 <= wave_first_pos) {
+#pragma unroll
+                for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) sacc[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            } else {
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    const int lim = qpos[c] - b0 * kBlock - 4 * gq;  // last visible key offset of this lane
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sacc[c][nb][r] = 16 * nb + r <= lim ? 0.f : -INFINITY;
+                }
+            }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-                for (int c = 0; c < NQ; ++c) sacc[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 if ((b0 + nb) * kBlock <= wave_last_pos) {
                     Vec16 ka[KK];
 #pragma unroll
@@ -257,32 +289,31 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
             op4_t ph[NQ][NB], pl[NQ][NB];
 #pragma unroll
             for (int c = 0; c < NQ; ++c) {
-                float sc[NB][4];
                 float mx = -INFINITY;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int kpos = (b0 + nb) * kBlock + 4 * gq + r;
-                        sc[nb][r] = kpos <= qpos[c] ? sacc[c][nb][r] * p.scale_log2 : -INFINITY;
-                        mx = fmaxf(mx, sc[nb][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[c][nb][r]);
                 mx = fmaxf(mx, shfl_xor(mx, 16));
                 mx = fmaxf(mx, shfl_xor(mx, 32));
-                const float mn = fmaxf(m[c], mx);
-                const float ms = mn == -INFINITY ? 0.f : mn;
-                if (__builtin_amdgcn_ballot_w64(mn > m[c])) {
-                    const float alpha = __builtin_amdgcn_exp2f(m[c] - ms);
+                const float mn = mx * scale_log2;  // the row's largest scaled score here
+                // The reference m[c] moves only when a row's scores pass it by
+                // more than kLazy (log2 units), so the weights stay below 2^kLazy
+                // and most iterations skip the rescale.
+                if (__builtin_amdgcn_ballot_w64(mn > m[c] + kLazy)) {
+                    const float nm = fmaxf(m[c], mn);
+                    const float alpha = __builtin_amdgcn_exp2f(m[c] - (nm == -INFINITY ? 0.f : nm));
                     l[c] *= alpha;
 #pragma unroll
                     for (int t = 0; t < TT; ++t) acc[c][t] *= alpha;
-                    m[c] = mn;
+                    m[c] = nm;
                 }
+                const float ms = m[c] == -INFINITY ? 0.f : m[c];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float pr = __builtin_amdgcn_exp2f(sc[nb][r] - ms);
+                        const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[c][nb][r], scale_log2, -ms));
                         l[c] += pr;
                         short hs, ls;
                         OPS::split(pr, hs, ls);
@@ -291,18 +322,23 @@ __global__ __launch_bounds__(NW * kWave) void prefill_kernel(PrefillParams p) {
                     }
             }
             // V^T read transposed: lane (gq, jq) takes key row 4gq + jq/4, bytes 32t + 8(jq%4).
+            // Blocks nb and nb + 1 make one 16x16x32 product: contraction
+            // slots 0-3 are keys 4gq + r of block nb, slots 4-7 those of
+            // block nb + 1, in V^T and P^T alike.  A block past the wave's
+            // last position has P = 0 (masked) and finite V (loaded, or zero).
             const int trow = 4 * gq + jq / 4;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NB; nb += 2) {
                 if ((b0 + nb) * kBlock > wave_last_pos) continue;
 #pragma unroll
                 for (int t = 0; t < TT; ++t) {
-                    const op4_t a =
-                        OPS::read_tr(vl + nb * SH::TILE + tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2));
+                    const uint32_t off = tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2);
+                    const op4_t a0 = OPS::read_tr(vl + nb * SH::TILE + off);
+                    const op4_t a1 = OPS::read_tr(vl + (nb + 1) * SH::TILE + off);
 #pragma unroll
                     for (int c = 0; c < NQ; ++c) {
-                        acc[c][t] = OPS::pv(a, ph[c][nb], acc[c][t]);
-                        if constexpr (SPLIT) acc[c][t] = OPS::pv(a, pl[c][nb], acc[c][t]);
+                        acc[c][t] = OPS::pv2(a0, a1, ph[c][nb], ph[c][nb + 1], acc[c][t]);
+                        if constexpr (SPLIT) acc[c][t] = OPS::pv2(a0, a1, pl[c][nb], pl[c][nb + 1], acc[c][t]);
                     }
                 }
             }

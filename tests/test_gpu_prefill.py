@@ -174,3 +174,28 @@ def test_prefill_is_deterministic():
         outs.append(out.view(torch.int16).cpu().numpy())
     assert not np.isnan(out.float().cpu().numpy()).any()
     assert all(np.array_equal(outs[0], o) for o in outs[1:]), "prefill output changed between identical runs"
+
+
+@pytest.mark.parametrize("scale", [-0.11, 0.0])
+def test_prefill_negative_and_zero_scale(scale):
+    """Any finite scale: a negative one flips which key is the largest score,
+    zero makes every visible key weigh the same (the output is V's mean)."""
+    import copy
+    w = copy.copy(W.build_prefill("scale_case", [0, 40, 300], [70, 33, 129], 8, 2, 128, "bf16", 3400))
+    w.scale = scale
+    _check(w)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_rising_scores(dtype):
+    """Key rows grow with their position, so each row's largest score keeps
+    rising along the keys, by small and by large steps: the softmax's running
+    reference has to move many times."""
+    import copy
+    from pkv_testutil import from_storage, to_storage
+    w = copy.copy(W.build_prefill("rising", [0, 0], [600, 257], 8, 4, 64, dtype, 3500))
+    code = w.dtype_code
+    k = from_storage(w.k_new, code).astype(np.float64)
+    pos = np.concatenate([np.arange(int(w.cu_q[s + 1] - w.cu_q[s])) for s in range(w.num_seqs)])
+    w.k_new = to_storage(k * (1.0 + pos / 16.0)[:, None, None], code)
+    _check(w)
