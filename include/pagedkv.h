@@ -191,8 +191,9 @@ pkv_status paged_kv_append_tokens(const void* k_new, const void* v_new, void* k_
  *                 longer chunk are not computed
  *
  * Supported: fp16 / bf16 caches, block_size 16, head_dim 64 or 128, group
- * 1, 2, 4 or 8 (PKV_ENOTSUP otherwise; fp32 prefill is not served).  A
- * sequence whose chunk is empty or longer than its context is skipped.
+ * 1, 2, 4 or 8, num_seqs <= 65535 and max_q_len x group <= 65535 x 128 query
+ * rows (PKV_ENOTSUP otherwise; fp32 prefill is not served).  A sequence whose
+ * chunk is empty or longer than its context is skipped.
  * pkv_validate_prefill() checks cu_q, the lengths and the tables on the host.
  */
 pkv_status paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const pkv_layout* layout,

@@ -356,8 +356,9 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
         return fail(PKV_ENOTSUP, "no prefill kernel for dtype %d, head_dim %d, group %d (16-bit caches only)",
                     layout->dtype, layout->head_dim, group);
     if (num_seqs > 65535) return fail(PKV_ENOTSUP, "num_seqs %d exceeds 65535", num_seqs);
-    if (layout->n_kv_heads > 65535) return fail(PKV_ENOTSUP, "n_kv_heads %d exceeds 65535", layout->n_kv_heads);
-    if ((int64_t)max_q_len * group > INT32_MAX / 2) return fail(PKV_EINVAL, "max_q_len %d is too large", max_q_len);
+    if ((int64_t)max_q_len * group > pkv::kMaxPrefillTiles * pkv::kPrefillRows)
+        return fail(PKV_ENOTSUP, "max_q_len %d x group %d exceeds %lld query rows", max_q_len, group,
+                    (long long)(pkv::kMaxPrefillTiles * pkv::kPrefillRows));
     if (num_seqs == 0 || max_q_len == 0) return ok();
     pkv::PrefillParams p{};
     p.q = q;

@@ -120,6 +120,10 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 hipError_t launch_swap(SwapParams p, bool to_cache, hipStream_t stream);
 hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream);
+// Prefill grid: (KV head, tile of kPrefillRows query rows, sequence); a grid's
+// second and third dimensions hold at most 65535.
+constexpr int kPrefillRows = 128;
+constexpr int64_t kMaxPrefillTiles = 65535;
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, int group, hipStream_t stream);
 bool prefill_supported(int dtype, int head_dim, int group);
 hipError_t launch_decode_partitions(const DecodeParams& p, int dtype, int head_dim, int group,

@@ -98,7 +98,7 @@ hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream)
 
 // ---- attention ---------------------------------------------------------------
 
-template <class E, int D, int G, int NW, int NQ, int NB>
+template <class E, int D, int G, int NW, int NQ, int NB, int KS>
 struct PrefillShape {
     static constexpr int RB = D * 2;            // bytes per head row
     static constexpr int CH = RB / 16;          // 16-byte chunks per head row
@@ -106,14 +106,19 @@ struct PrefillShape {
     static constexpr int TT = D / 16;           // 16-wide output tiles
     static constexpr int ROWS_W = 16 * NQ;      // query rows per wave
     static constexpr int ROWS = NW * ROWS_W;    // query rows per workgroup
-    static constexpr int NT = NW * kWave;
+    static constexpr int NT_G = NW * kWave;     // threads of one key group
     static constexpr int TILE = kBlock * RB;    // bytes of one block's K (or V) rows of one head
     static constexpr int SPAN = NB * TILE;      // bytes of an iteration's K (or V) rows
     static constexpr int NCH = 2 * NB * kBlock * CH;  // 16-byte chunks of an iteration's K + V
-    static constexpr int PER_T = (NCH + NT - 1) / NT;
+    static constexpr int PER_T = NCH / NT_G;
+    static constexpr int LOOP_BYTES = KS * 2 * 2 * SPAN;  // [group][buffer][K, V] tiles
+    static constexpr int STATE = TT * 4 + 2;              // floats of one lane's row state (acc, m, l)
+    static constexpr int MERGE_BYTES = KS > 1 ? NW * NQ * STATE * kWave * 4 : 0;
+    static constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
     static_assert(E::kBytes == 2 && D % 32 == 0 && CH == 4 * KK, "16-bit caches, head_dim a multiple of 32");
-    static_assert(NCH % NT == 0, "every thread moves the same number of chunks");
+    static_assert(NCH % NT_G == 0, "every thread moves the same number of chunks");
     static_assert(NB % 2 == 0, "PV takes blocks in pairs");
+    static_assert(KS == 1 || KS == 2, "one or two key groups");
 };
 
 // Headroom of the online softmax's reference maximum (log2 units): weights
@@ -131,17 +136,26 @@ __device__ __forceinline__ uint32_t tile_pos(int row, int chunk) {
 
 // One iteration covers NB consecutive blocks: their K and V tiles are loaded
 // together (one iteration ahead) and one softmax rescale covers all NB x 16 keys.
-template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int PD>
-__global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p) {
-    using SH = PrefillShape<E, D, G, NW, NQ, NB>;
+// With KS = 2 the workgroup holds two key groups of NW waves over the same rows:
+// group 0 takes the first half of the iterations, group 1 the rest, and their
+// softmax states (the same combination rule as the decode split merge) meet in
+// LDS at the end, so a tile that sees many keys gets twice the waves.
+template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int KS>
+__global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillParams p) {
+    using SH = PrefillShape<E, D, G, NW, NQ, NB, KS>;
     using OPS = MfmaOps<E>;
     using op4_t = typename OPS::op4_t;
     using el_t = typename std::remove_reference<decltype(op4_t{}[0])>::type;
     constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT;
-    __shared__ __attribute__((aligned(16))) char lds[2][2][SH::SPAN];  // [buffer][K, V][block][row][RB]
+    __shared__ __attribute__((aligned(16))) char smem[SH::LDS_BYTES];
 
+    // Grid (KV head, tile rank, sequence), KV head fastest: workgroups are
+    // dealt to the XCDs round-robin in launch order, so 8 consecutive ones of
+    // equal work (the same tile of 8 heads) give every XCD the same mix of
+    // long and short tiles; within a sequence the last tile (most keys) goes
+    // first.
     const int s = blockIdx.z;
-    const int kvh = blockIdx.y;
+    const int kvh = blockIdx.x;
     const int Hq = p.n_q_heads;
     const int q0 = p.cu_q[s];
     const int n = p.cu_q[s + 1] - q0;
@@ -149,7 +163,7 @@ __global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p)
     if (n <= 0 || n > L) return;  // an empty or impossible chunk
     const int nrows = n * G;
     const int ntiles = (nrows + SH::ROWS - 1) / SH::ROWS;
-    const int tile = ntiles - 1 - (int)blockIdx.x;  // longest tiles first
+    const int tile = ntiles - 1 - (int)blockIdx.y;
     if (tile < 0) return;
     const int r0 = tile * SH::ROWS;
     const int ctx = L - n;  // tokens before the chunk
@@ -158,8 +172,14 @@ __global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p)
     const int nit = (nblk + NB - 1) / NB;
 
     const int tid = threadIdx.x;
-    const int w = wave_id_uniform();
+    const int kg = wave_id_uniform() / NW;  // key group
+    const int w = wave_id_uniform() % NW;   // row wave within the group
+    const int tid_g = tid % SH::NT_G;
     const int lane = tid % kWave;
+    // iterations [kb, ke) belong to this wave's key group
+    const int half = KS == 1 ? nit : (nit + 1) / 2;
+    const int kb = kg == 0 ? 0 : half;
+    const int ke = kg == 0 ? half : nit;
     const int gq = lane / 16;  // MFMA lane coordinates
     const int jq = lane % 16;
     const int wr0 = r0 + w * SH::ROWS_W;  // this wave's first row
@@ -212,13 +232,12 @@ __global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p)
     int c_nb[SH::PER_T], c_row[SH::PER_T], c_col[SH::PER_T];
 #pragma unroll
     for (int k = 0; k < SH::PER_T; ++k) {
-        const int ee = (tid + k * SH::NT) % PER_CACHE;
+        const int ee = (tid_g + k * SH::NT_G) % PER_CACHE;
         c_nb[k] = ee / (kBlock * CH);
         c_row[k] = (ee / CH) % kBlock;
         c_col[k] = ee % CH;
     }
-    // register ring: slot d holds the loads of an iteration PD ahead of the compute
-    Vec16 pre[PD][SH::PER_T];
+    Vec16 pre[SH::PER_T];  // the next iteration's chunks
     auto fetch = [&](int it, Vec16(&dst)[SH::PER_T]) {
         // the iteration's table entries first (uniform loads), then every chunk load in flight at once
         int pbs[NB];
@@ -235,24 +254,25 @@ __global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p)
             for (int nb = 1; nb < NB; ++nb) pb = c_nb[k] == nb ? pbs[nb] : pb;
             const int b = it * NB + c_nb[k];
             const bool ok = pb >= 0 && c_row[k] < L - b * kBlock;  // rows of the block inside the sequence
-            const char* base = tid + k * SH::NT < PER_CACHE ? kbase : vbase;
+            const char* base = tid_g + k * SH::NT_G < PER_CACHE ? kbase : vbase;
             dst[k] = ok ? load16(base + (int64_t)pb * blk_bytes + (int64_t)c_row[k] * row_stride + c_col[k] * 16)
                         : Vec16{{0u, 0u, 0u, 0u}};
         }
     };
+    // LDS tiles of this key group: [buffer][K, V][block][row][RB]
+    auto tiles = [&](int buf, int kv) { return smem + ((kg * 2 + buf) * 2 + kv) * SH::SPAN; };
     auto stash = [&](int buf, const Vec16(&src)[SH::PER_T]) {
 #pragma unroll
         for (int k = 0; k < SH::PER_T; ++k)
-            lds_store16(lds[buf][tid + k * SH::NT < PER_CACHE ? 0 : 1] + c_nb[k] * SH::TILE,
+            lds_store16(tiles(buf, tid_g + k * SH::NT_G < PER_CACHE ? 0 : 1) + c_nb[k] * SH::TILE,
                         tile_pos<RB>(c_row[k], c_col[k]), src[k]);
     };
 
-    auto compute = [&](int it) {
-        const int buf = it & 1;
+    auto compute = [&](int buf, int it) {
         const int b0 = it * NB;
         if (b0 * kBlock <= wave_last_pos) {
-            const char* kl = lds[buf][0];
-            const char* vl = lds[buf][1];
+            const char* kl = tiles(buf, 0);
+            const char* vl = tiles(buf, 1);
             // scores: lane (gq, jq) holds keys (b0 + nb) * 16 + 4gq + r of row column jq
             // The prefix-causal mask enters as the products' initial value (0,
             // or -inf for a key past the row's position), built only in the
@@ -345,34 +365,68 @@ __global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p)
         }
     };
 
-#pragma unroll
-    for (int d = 0; d < PD; ++d)
-        if (d < nit) fetch(d, pre[d]);
-    stash(0, pre[0]);
+    // Both groups step together (the barrier is the workgroup's); a group
+    // whose range is shorter idles through its last step.
+    if (kb < ke) {
+        fetch(kb, pre);
+        stash(0, pre);
+    }
     __syncthreads();
-    for (int it0 = 0; it0 < nit; it0 += PD) {
-#pragma unroll
-        for (int d = 0; d < PD; ++d) {
-            const int it = it0 + d;
-            if (it < nit) {  // uniform over the workgroup
-                // slot d's iteration is in LDS already: refill it PD iterations ahead
-                if (it + PD < nit) fetch(it + PD, pre[d]);
-                compute(it);
-                if (it + 1 < nit) stash((it + 1) & 1, pre[(d + 1) % PD]);
-                __syncthreads();
-            }
-        }
+    for (int j = 0; j < half; ++j) {
+        const int it = kb + j;
+        const bool more = it + 1 < ke;  // uniform over the group
+        if (more) fetch(it + 1, pre);
+        if (it < ke) compute(j & 1, it);
+        if (more) stash((j + 1) & 1, pre);
+        __syncthreads();
     }
 
     // Each lane summed its own 4 keys per block: add the other lane groups.
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-        float lt = l[c];
-        lt += shfl_xor(lt, 16);
-        lt += shfl_xor(lt, 32);
+        l[c] += shfl_xor(l[c], 16);
+        l[c] += shfl_xor(l[c], 32);
+    }
+    if constexpr (KS == 2) {
+        // Group 1 leaves its state in LDS (the tiles are no longer read: the
+        // loop ended on a barrier); group 0 folds it into its own.  Lane-major
+        // layout, so each store and load is one conflict-free row of 64 words.
+        float* st = reinterpret_cast<float*>(smem);
+        if (kg == 1) {
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                float* b = st + (w * NQ + c) * SH::STATE * kWave + lane;
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) b[(4 * t + r) * kWave] = acc[c][t][r];
+                b[4 * TT * kWave] = m[c];
+                b[(4 * TT + 1) * kWave] = l[c];
+            }
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            const float* b = st + (w * NQ + c) * SH::STATE * kWave + lane;
+            const float m1 = b[4 * TT * kWave];
+            const float l1 = b[(4 * TT + 1) * kWave];
+            const float mm = fmaxf(m[c], m1);
+            const float mr = mm == -INFINITY ? 0.f : mm;
+            const float a0 = __builtin_amdgcn_exp2f(m[c] - mr);
+            const float a1 = __builtin_amdgcn_exp2f(m1 - mr);
+            l[c] = l[c] * a0 + l1 * a1;
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[c][t][r] = acc[c][t][r] * a0 + b[(4 * t + r) * kWave] * a1;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
         const int row = wr0 + 16 * c + jq;
         if (row >= nrows) continue;
-        const float inv = 1.f / lt;
+        const float inv = 1.f / l[c];
         char* orow = static_cast<char*>(p.out) + (((int64_t)(q0 + row / G) * Hq + kvh * G + row % G) * D) * 2;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
@@ -381,27 +435,28 @@ __global__ __launch_bounds__(NW * kWave, 4) void prefill_kernel(PrefillParams p)
     }
 }
 
-template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int PD>
+template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int KS>
 hipError_t launch_prefill_shape(const PrefillParams& p, hipStream_t stream) {
     constexpr int ROWS = NW * 16 * NQ;
     const int64_t tiles = ((int64_t)p.max_q_len * G + ROWS - 1) / ROWS;
-    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)tiles, p.n_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, NB, SPLIT, PD>), grid, dim3(NW * kWave), 0, stream, p);
+    if (tiles > kMaxPrefillTiles || p.num_seqs > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid(p.n_kv_heads, (unsigned)tiles, (unsigned)p.num_seqs);
+    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, NB, SPLIT, KS>), grid, dim3(KS * NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
 // Launch shape (measured on MI355X): 8 waves of 16 query rows (128 rows per
-// workgroup); 32 keys per iteration at head_dim 128 (64 at 64), i.e. 16 KiB of
-// K and V per LDS buffer.  It needs no accumulator registers beyond the
-// architectural VGPRs and runs 4 waves per SIMD.  fp16 keeps one 16-bit P per
-// weight (11 significant bits); bf16 splits P into high and low parts, since
-// one bf16 keeps only 8.
+// workgroup) in each of KS key groups; 32 keys per iteration at head_dim 128
+// (64 at 64), i.e. 16 KiB of K and V per LDS buffer.  It needs no accumulator
+// registers beyond the architectural VGPRs and runs 4 waves per SIMD.  fp16
+// keeps one 16-bit P per weight (11 significant bits); bf16 splits P into high
+// and low parts, since one bf16 keeps only 8.
 template <class E, int D, int G>
 static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
     constexpr int NB = D == 128 ? 2 : 4;
     constexpr bool SPLIT = std::is_same<E, BF16>::value;
-    return launch_prefill_shape<E, D, G, 8, 1, NB, SPLIT, 1>(p, stream);
+    static_assert(8 * 16 == kPrefillRows, "the grid's tile height");
+    return launch_prefill_shape<E, D, G, 8, 1, NB, SPLIT, 2>(p, stream);
 }
 
 template <class E, int D>
