@@ -268,7 +268,8 @@ struct WaveAttn {
 // heads (16 tokens), with the wave's HG = NH * G query heads in columns
 // 0..HG-1 of 16 (the rest zero padding):
 //   S^T[16 tok][16]  = sum_h K_h[16][D] . Q_h^T[D][16]      (NH * D/32 MFMA 16x16x32)
-//   O^T[D][16]      += sum_h V_h^T[D][16 tok] . P_h^T[16][16] (NH * D/16 x 2 MFMA 16x16x16)
+//   O^T[D][16]      += sum_h V_h^T[D][16 tok] . P_h^T[16][16] (D/16 x 2 MFMA 16x16x32
+//                      with two heads, D/16 with one: two 4-token halves each)
 // Q_h^T holds only head h's columns, so both heads accumulate into one S^T
 // and P_h^T keeps only head h's columns of P^T.  Lane l = 16 g + j holds S^T
 // rows 4g..4g+3 of column j, which is exactly the B operand P^T, so the
@@ -410,17 +411,31 @@ struct MfmaAttn {
         }
         const op4_t zero = {};
         // V^T read transposed: lane (g, j) takes row 4g + j/4, bytes 32t + 8(j%4) of its head row.
+        // Each 16x16x32 product takes two 4-token halves: with two heads, head
+        // 0's V^T and P^T beside head 1's (a column's P is zero for the head it
+        // does not belong to); with one head, V^T twice beside P's high and
+        // low parts.
         const int trow = 4 * g + j / 4;
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            const bool mine = j >= h * G && j < (h + 1) * G;
-            const op4_t bh = mine ? phi : zero;
-            const op4_t bl = mine ? plo : zero;
+        if constexpr (NH == 2) {
+            const bool m0 = j < G, m1 = j >= G && j < 2 * G;
+            const op4_t bh0 = m0 ? phi : zero, bl0 = m0 ? plo : zero;
+            const op4_t bh1 = m1 ? phi : zero, bl1 = m1 ? plo : zero;
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                const op4_t a = OPS::read_tr(vl + lds_pos(trow, h, 2 * t + (j % 4) / 2) + 8 * (j % 2));
-                acc[t] = OPS::pv(a, bh, acc[t]);
-                acc[t] = OPS::pv(a, bl, acc[t]);
+                const uint32_t off = 2 * t + (j % 4) / 2;
+                const op4_t a0 = OPS::read_tr(vl + lds_pos(trow, 0, off) + 8 * (j % 2));
+                const op4_t a1 = OPS::read_tr(vl + lds_pos(trow, 1, off) + 8 * (j % 2));
+                acc[t] = OPS::pv2(a0, a1, bh0, bh1, acc[t]);
+                acc[t] = OPS::pv2(a0, a1, bl0, bl1, acc[t]);
+            }
+        } else {
+            static_assert(NH == 1, "one or two KV heads per wave");
+            const bool mine = j < G;
+            const op4_t bh = mine ? phi : zero, bl = mine ? plo : zero;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const op4_t a = OPS::read_tr(vl + lds_pos(trow, 0, 2 * t + (j % 4) / 2) + 8 * (j % 2));
+                acc[t] = OPS::pv2(a, a, bh, bl, acc[t]);
             }
         }
     }
