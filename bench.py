@@ -400,9 +400,9 @@ def run_prefill(w, steps, warmup):
 
 
 def cpu_baseline_prefill(w, budget_s=10.0):
-    """The oracle's prefill attention on sampled query rows (each sequence's
-    rows in turn, spread evenly) until budget_s is spent; flops per second of
-    the rows computed."""
+    """The oracle's prefill attention on query rows in a fixed random order
+    (whole passes over the step's rows repeated) until budget_s is spent;
+    flops per second of the rows computed."""
     import numpy as np
     from oracle import ref
     cores = len(os.sched_getaffinity(0))
@@ -414,10 +414,13 @@ def cpu_baseline_prefill(w, budget_s=10.0):
     order = np.random.default_rng(0).permutation(total)
     seq_of = np.searchsorted(w.cu_q, np.arange(total), side="right") - 1
     pos = w.start_pos[seq_of] + (np.arange(total) - w.cu_q[seq_of])
+    if total == 0:
+        return None
     done, flops, elapsed = 0, 0, 0.0
     batch = 64
-    while done < total and elapsed < budget_s:
-        ids = np.sort(order[done:done + batch])
+    while elapsed < budget_s:
+        start = done % total
+        ids = np.sort(order[start:start + batch])
         t0 = time.perf_counter()
         orc.attention_prefill(w.q, kc, vc, w.block_tables, w.cu_q, w.context_lens, w.scale, w.dtype_code,
                               row_ids=ids)
@@ -425,7 +428,8 @@ def cpu_baseline_prefill(w, budget_s=10.0):
         flops += int(np.sum(pos[ids] + 1)) * 4 * w.head_dim * w.n_q_heads
         done += len(ids)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": "%d of %d query rows (all heads), %.1f s" % (done, total, elapsed)}
+            "sample": "%d query rows (all heads): %.2f passes over the step's %d rows, %.1f s" % (
+                done, done / total, total, elapsed)}
 
 
 def main_prefill(a):
