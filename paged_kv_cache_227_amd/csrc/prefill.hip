@@ -121,6 +121,25 @@ struct PrefillShape {
     static_assert(KS == 1 || KS == 2, "one or two key groups");
 };
 
+// Maximum and sum over the four 16-lane rows' matching lanes (l, l^16, l^32,
+// l^48), inside the vector ALU: v_permlane16_swap of a value with itself
+// leaves lane l holding, in row order, its own and lane l^16's values (and
+// v_permlane32_swap likewise for l^32), so both lanes of a pair combine the
+// same two values in the same order.
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Headroom of the online softmax's reference maximum (log2 units): weights
 // reach at most 2^8, well inside fp16 and bf16 range.
 constexpr float kLazy = 8.f;
@@ -184,7 +203,6 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     const int jq = lane % 16;
     const int wr0 = r0 + w * SH::ROWS_W;  // this wave's first row
     const int wave_last_pos = wr0 < nrows ? ctx + (min(wr0 + SH::ROWS_W, nrows) - 1) / G : -1;
-    const int wave_first_pos = ctx + wr0 / G;
 
     // The softmax below needs a positive scale: a negative one moves into q's
     // sign bits (exact), and a zero one becomes the smallest normal float,
@@ -268,17 +286,18 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
                         tile_pos<RB>(c_row[k], c_col[k]), src[k]);
     };
 
-    auto compute = [&](int buf, int it) {
+    // One iteration of one wave; MASK builds the prefix-causal mask into the
+    // score products' initial value (0, or -inf for a key past the row's
+    // position), else every key of the iteration is visible to every row.
+    auto compute = [&](auto masked, int buf, int it) {
+        constexpr bool MASK = decltype(masked)::value;
         const int b0 = it * NB;
         if (b0 * kBlock <= wave_last_pos) {
             const char* kl = tiles(buf, 0);
             const char* vl = tiles(buf, 1);
             // scores: lane (gq, jq) holds keys (b0 + nb) * 16 + 4gq + r of row column jq
-            // The prefix-causal mask enters as the products' initial value (0,
-            // or -inf for a key past the row's position), built only in the
-            // iterations that hold such keys for some row of the wave.
             f32x4_t sacc[NQ][NB];
-            if ((b0 + NB) * kBlock - 1 <= wave_first_pos) {
+            if constexpr (!MASK) {
 #pragma unroll
                 for (int c = 0; c < NQ; ++c)
 #pragma unroll
@@ -314,8 +333,7 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[c][nb][r]);
-                mx = fmaxf(mx, shfl_xor(mx, 16));
-                mx = fmaxf(mx, shfl_xor(mx, 32));
+                mx = rows_max(mx);
                 const float mn = mx * scale_log2;  // the row's largest scaled score here
                 // The reference m[c] moves only when a row's scores pass it by
                 // more than kLazy (log2 units), so the weights stay below 2^kLazy
@@ -372,21 +390,25 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
         stash(0, pre);
     }
     __syncthreads();
-    for (int j = 0; j < half; ++j) {
+    auto step = [&](auto masked, int j) {
         const int it = kb + j;
         const bool more = it + 1 < ke;  // uniform over the group
         if (more) fetch(it + 1, pre);
-        if (it < ke) compute(j & 1, it);
+        if (it < ke) compute(masked, j & 1, it);
         if (more) stash((j + 1) & 1, pre);
         __syncthreads();
-    }
+    };
+    // Steps whose iterations (in both groups) hold only keys every row of the
+    // tile sees run without the mask; the rest, the causal diagonal, with it.
+    const int it_full = (ctx + r0 / G + 1) / (NB * kBlock);
+    const int j_full = KS == 1 ? min(it_full, half) : min(max(it_full - half, 0), half);
+    int j = 0;
+    for (; j < j_full; ++j) step(std::false_type{}, j);
+    for (; j < half; ++j) step(std::true_type{}, j);
 
     // Each lane summed its own 4 keys per block: add the other lane groups.
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-        l[c] += shfl_xor(l[c], 16);
-        l[c] += shfl_xor(l[c], 32);
-    }
+    for (int c = 0; c < NQ; ++c) l[c] = rows_sum(l[c]);
     if constexpr (KS == 2) {
         // Group 1 leaves its state in LDS (the tiles are no longer read: the
         // loop ended on a barrier); group 0 folds it into its own.  Lane-major
