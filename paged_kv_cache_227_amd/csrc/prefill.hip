@@ -35,7 +35,7 @@
 //                      blocks' 4-key lane slices make the 8 contraction slots),
 //     with P split into high and low 16-bit parts for bf16 so about 16 bits of
 //     each weight survive;
-//   * blocks wholly past a wave's last position are skipped by that wave;
+//   * iterations wholly past a wave's last position are skipped by that wave;
 //     tiles are started longest first (the last rows see the most keys).
 // Rows past L in a sequence's last block are loaded as zeros, so whatever
 // those slots hold never reaches the output.
@@ -312,18 +312,19 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
                         for (int r = 0; r < 4; ++r) sacc[c][nb][r] = 16 * nb + r <= lim ? 0.f : -INFINITY;
                 }
             }
+            // Every block of a computed iteration gets its products, those
+            // past the wave's rows included (their scores stay -inf from the
+            // mask): a branch around them would put the softmax's first reads
+            // of a product's result right after it, closer than its latency.
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                if ((b0 + nb) * kBlock <= wave_last_pos) {
-                    Vec16 ka[KK];
+                Vec16 ka[KK];
 #pragma unroll
-                    for (int kk = 0; kk < KK; ++kk)
-                        ka[kk] = lds_load16(kl + nb * SH::TILE, tile_pos<RB>(jq, 4 * kk + gq));
+                for (int kk = 0; kk < KK; ++kk) ka[kk] = lds_load16(kl + nb * SH::TILE, tile_pos<RB>(jq, 4 * kk + gq));
 #pragma unroll
-                    for (int c = 0; c < NQ; ++c)
+                for (int c = 0; c < NQ; ++c)
 #pragma unroll
-                        for (int kk = 0; kk < KK; ++kk) sacc[c][nb] = OPS::qk(ka[kk], qf[c][kk], sacc[c][nb]);
-                }
+                    for (int kk = 0; kk < KK; ++kk) sacc[c][nb] = OPS::qk(ka[kk], qf[c][kk], sacc[c][nb]);
             }
             op4_t ph[NQ][NB], pl[NQ][NB];
 #pragma unroll
