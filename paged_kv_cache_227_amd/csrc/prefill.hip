@@ -16,27 +16,29 @@
 // Attention: unlike decode, a chunk makes QK^T and PV real matrix products
 // (n x G query rows against every key), so the work runs on the matrix cores.
 // A query row is one (chunk token, head of the KV head's group) pair; rows of
-// one (sequence, KV head) are ordered token-major.  One workgroup holds
-// NW x 16 x NQ consecutive rows of one (sequence, KV head):
-//   * the K and V tiles of NB blocks at a time, up to the workgroup's last
-//     causal position, are loaded once per workgroup (the iteration's table
-//     entries first, then every 16-byte load in flight at once, one iteration
-//     ahead of the compute) and stored in LDS, double-buffered, 16-byte
-//     chunks XOR-swizzled by row;
-//   * each wave owns NQ groups of 16 rows; one softmax rescale per iteration
-//     covers its NB x 16 keys.  Per block and group:
+// one (sequence, KV head) are ordered token-major.  A workgroup holds one tile
+// of NW x 16 x NQ consecutive rows, in KS key groups of NW waves:
+//   * each key group takes its share of the tile's key iterations; an
+//     iteration's K and V tiles (NB blocks) are loaded once per group (the
+//     table entries first, then every 16-byte load in flight at once, one
+//     iteration ahead of the compute) and stored in LDS, double-buffered,
+//     16-byte chunks XOR-swizzled by row;
+//   * each wave owns NQ groups of 16 rows.  Per block and group:
 //       S^T = K Q^T   (v_mfma_f32_16x16x32, K from LDS as the A operand, the
 //                      group's q rows as B, held in registers),
-//     the prefix-causal mask (key position <= the row's position) by select,
-//     an online softmax per row in base-2 units (each row's state lives in one
-//     lane column), then, for each pair of blocks,
+//     the prefix-causal mask (key position <= the row's position) entering as
+//     the products' initial value (0 or -inf) in the steps that need it, an
+//     online softmax per row in base-2 units with a lazily moved reference
+//     maximum (each row's state lives in one lane column), then, for each
+//     pair of blocks,
 //       O^T += V^T P^T (v_mfma_f32_16x16x32, V^T read transposed from LDS,
 //                      P^T straight from S^T's accumulator layout; the two
 //                      blocks' 4-key lane slices make the 8 contraction slots),
 //     with P split into high and low 16-bit parts for bf16 so about 16 bits of
 //     each weight survive;
-//   * iterations wholly past a wave's last position are skipped by that wave;
-//     tiles are started longest first (the last rows see the most keys).
+//   * the key groups' softmax states meet in LDS at the end (the decode merge's
+//     rule), and group 0 writes the rows;
+//   * iterations wholly past a wave's last position are skipped by that wave.
 // Rows past L in a sequence's last block are loaded as zeros, so whatever
 // those slots hold never reaches the output.
 #include <math.h>
@@ -109,14 +111,10 @@ struct PrefillShape {
     static constexpr int NT_G = NW * kWave;     // threads of one key group
     static constexpr int TILE = kBlock * RB;    // bytes of one block's K (or V) rows of one head
     static constexpr int SPAN = NB * TILE;      // bytes of an iteration's K (or V) rows
-    static constexpr int NCH = 2 * NB * kBlock * CH;  // 16-byte chunks of an iteration's K + V
-    static constexpr int PER_T = NCH / NT_G;
-    static constexpr int LOOP_BYTES = KS * 2 * 2 * SPAN;  // [group][buffer][K, V] tiles
-    static constexpr int STATE = TT * 4 + 2;              // floats of one lane's row state (acc, m, l)
-    static constexpr int MERGE_BYTES = KS > 1 ? NW * NQ * STATE * kWave * 4 : 0;
-    static constexpr int LDS_BYTES = LOOP_BYTES > MERGE_BYTES ? LOOP_BYTES : MERGE_BYTES;
+    static constexpr int BUF_BYTES = KS * 2 * SPAN;      // one buffer: [group][K, V] tiles
+    static constexpr int STATE = TT * 4 + 2;             // floats of one lane's row state (acc, m, l)
+    static constexpr int MERGE_BYTES = KS > 1 ? NW * NQ * STATE * kWave * 4 : 16;
     static_assert(E::kBytes == 2 && D % 32 == 0 && CH == 4 * KK, "16-bit caches, head_dim a multiple of 32");
-    static_assert(NCH % NT_G == 0, "every thread moves the same number of chunks");
     static_assert(NB % 2 == 0, "PV takes blocks in pairs");
     static_assert(KS == 1 || KS == 2, "one or two key groups");
 };
@@ -138,6 +136,19 @@ __device__ __forceinline__ float rows_sum(float x) {
     x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle; with a
+// stride of 0 the size (word 2) is in bytes and reads at or past it return 0.
+constexpr int kBufferWord3 = 0x00020000;
+
+// One wave's buffer load of 64 16-byte chunks straight into LDS: lane i reads
+// `base + voff` (zeros at or past `bytes`) into `lds + 16 i`.  `base`, `bytes`
+// and `lds` must be uniform over the wave.
+__device__ __forceinline__ void lds_load_1k(const char* base, int bytes, char* lds, uint32_t voff) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
 // Headroom of the online softmax's reference maximum (log2 units): weights
@@ -166,7 +177,12 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     using op4_t = typename OPS::op4_t;
     using el_t = typename std::remove_reference<decltype(op4_t{}[0])>::type;
     constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT;
-    __shared__ __attribute__((aligned(16))) char smem[SH::LDS_BYTES];
+    // The two buffers are separate arrays, so the compiler can tell the LDS
+    // loads filling one from the reads of the other (and need not wait for
+    // them before reading); the key groups' states meet in a third.
+    __shared__ __attribute__((aligned(16))) char lds_a[SH::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_b[SH::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) float lds_state[SH::MERGE_BYTES / 4];
 
     // Grid (KV head, tile rank, sequence), KV head fastest: workgroups are
     // dealt to the XCDs round-robin in launch order, so 8 consecutive ones of
@@ -193,7 +209,6 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     const int tid = threadIdx.x;
     const int kg = wave_id_uniform() / NW;  // key group
     const int w = wave_id_uniform() % NW;   // row wave within the group
-    const int tid_g = tid % SH::NT_G;
     const int lane = tid % kWave;
     // iterations [kb, ke) belong to this wave's key group
     const int half = KS == 1 ? nit : (nit + 1) / 2;
@@ -238,58 +253,61 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
         for (int t = 0; t < TT; ++t) acc[c][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Cooperative loads: chunk e of an iteration is (cache e / (NB 16 CH), block,
-    // row, 16-byte column); consecutive threads read consecutive chunks of a row.
+    // K and V go from memory straight into LDS (buffer loads with an LDS
+    // destination).  One such instruction of a wave fills a contiguous 1 KiB
+    // of LDS, lane i bytes 16i .. 16i+15: RPR rows of one block of one cache.
+    // Lane i fetches the global chunk that the row's XOR swizzle puts in its
+    // slot.  The block's base address and the bytes of its rows inside the
+    // sequence make the buffer resource, so rows past the context and invalid
+    // table entries arrive as zeros (out-of-range buffer reads return 0).
     const uint32_t row_stride = (uint32_t)p.n_kv_heads * RB;
     const int64_t blk_bytes = (int64_t)row_stride * kBlock;
     const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
     const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
-    constexpr int PER_CACHE = NB * kBlock * CH;
-    // This thread's chunks: block, row and column within an iteration (fixed).
-    int c_nb[SH::PER_T], c_row[SH::PER_T], c_col[SH::PER_T];
+    constexpr int RPR = 1024 / RB;           // rows per load instruction
+    constexpr int RG = kBlock / RPR;         // load instructions per block and cache
+    constexpr int PER_W = 2 * NB * RG / NW;  // load instructions per wave and iteration
+    static_assert(RPR * RB == 1024 && (2 * NB * RG) % NW == 0, "whole 1 KiB slices, the same count per wave");
+    // slice g = w + k NW of an iteration: cache g / (NB RG), block (g / RG) % NB, rows RPR (g % RG) ..
+    uint32_t voff[PER_W];
 #pragma unroll
-    for (int k = 0; k < SH::PER_T; ++k) {
-        const int ee = (tid_g + k * SH::NT_G) % PER_CACHE;
-        c_nb[k] = ee / (kBlock * CH);
-        c_row[k] = (ee / CH) % kBlock;
-        c_col[k] = ee % CH;
+    for (int k = 0; k < PER_W; ++k) {
+        const int row = ((w + k * NW) % RG) * RPR + lane / CH;
+        voff[k] = (uint32_t)row * row_stride + (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
     }
-    Vec16 pre[SH::PER_T];  // the next iteration's chunks
-    auto fetch = [&](int it, Vec16(&dst)[SH::PER_T]) {
-        // the iteration's table entries first (uniform loads), then every chunk load in flight at once
-        int pbs[NB];
+    // LDS tiles of this key group in buffer BUF: [K, V][block][row][RB]
+    auto tiles = [&](auto bufc, int kv) {
+        return (decltype(bufc)::value ? lds_b : lds_a) + (kg * 2 + kv) * SH::SPAN;
+    };
+    // Table entries are read one step ahead of their loads: the step barrier's
+    // wait covers them, and no wait for them lands behind an LDS load.
+    auto entries = [&](int it, int (&pbs)[PER_W]) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int b = it * NB + nb;
-            const int pb = b < nblk ? table[b] : -1;
-            pbs[nb] = pb >= 0 && pb < p.num_blocks ? pb : -1;
-        }
-#pragma unroll
-        for (int k = 0; k < SH::PER_T; ++k) {
-            int pb = pbs[0];
-#pragma unroll
-            for (int nb = 1; nb < NB; ++nb) pb = c_nb[k] == nb ? pbs[nb] : pb;
-            const int b = it * NB + c_nb[k];
-            const bool ok = pb >= 0 && c_row[k] < L - b * kBlock;  // rows of the block inside the sequence
-            const char* base = tid_g + k * SH::NT_G < PER_CACHE ? kbase : vbase;
-            dst[k] = ok ? load16(base + (int64_t)pb * blk_bytes + (int64_t)c_row[k] * row_stride + c_col[k] * 16)
-                        : Vec16{{0u, 0u, 0u, 0u}};
+        for (int k = 0; k < PER_W; ++k) {
+            const int b = it * NB + ((w + k * NW) / RG) % NB;
+            pbs[k] = b < nblk ? table[b] : -1;
         }
     };
-    // LDS tiles of this key group: [buffer][K, V][block][row][RB]
-    auto tiles = [&](int buf, int kv) { return smem + ((kg * 2 + buf) * 2 + kv) * SH::SPAN; };
-    auto stash = [&](int buf, const Vec16(&src)[SH::PER_T]) {
+    auto issue = [&](int it, const int (&pbs)[PER_W], auto buf) {
 #pragma unroll
-        for (int k = 0; k < SH::PER_T; ++k)
-            lds_store16(tiles(buf, tid_g + k * SH::NT_G < PER_CACHE ? 0 : 1) + c_nb[k] * SH::TILE,
-                        tile_pos<RB>(c_row[k], c_col[k]), src[k]);
+        for (int k = 0; k < PER_W; ++k) {
+            const int g = w + k * NW;  // uniform over the wave
+            const int kv = g / (NB * RG), nb = (g / RG) % NB;
+            const int b = it * NB + nb;
+            const int pb = __builtin_amdgcn_readfirstlane(pbs[k]);
+            const bool ok = pb >= 0 && pb < p.num_blocks;
+            const int rows = min(max(L - b * kBlock, 0), kBlock);
+            // the size is uniform already; readfirstlane keeps the resource in scalar registers
+            lds_load_1k((kv ? vbase : kbase) + (ok ? (int64_t)pb * blk_bytes : 0), ok ? (int)(rows * row_stride) : 0,
+                        tiles(buf, kv) + nb * SH::TILE + (g % RG) * 1024, voff[k]);
+        }
     };
 
     // One iteration of one wave; MASK builds the prefix-causal mask into the
     // score products' initial value (0, or -inf for a key past the row's
     // position), else every key of the iteration is visible to every row.
-    auto compute = [&](auto masked, int buf, int it) {
+    auto compute = [&](auto masked, auto buf, int it) {
         constexpr bool MASK = decltype(masked)::value;
         const int b0 = it * NB;
         if (b0 * kBlock <= wave_last_pos) {
@@ -386,26 +404,43 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
 
     // Both groups step together (the barrier is the workgroup's); a group
     // whose range is shorter idles through its last step.
+    // Step j computes from buffer j % 2 while the next iteration's loads fill
+    // the other; they land before the step's barrier (vmcnt 0).
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    int pbs[PER_W];
     if (kb < ke) {
-        fetch(kb, pre);
-        stash(0, pre);
+        entries(kb, pbs);
+        issue(kb, pbs, B0{});
+        if (kb + 1 < ke) entries(kb + 1, pbs);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    auto step = [&](auto masked, int j) {
+    auto step = [&](auto masked, int j, auto buf) {
         const int it = kb + j;
-        const bool more = it + 1 < ke;  // uniform over the group
-        if (more) fetch(it + 1, pre);
-        if (it < ke) compute(masked, j & 1, it);
-        if (more) stash((j + 1) & 1, pre);
+        if (it + 1 < ke) {  // uniform over the group
+            issue(it + 1, pbs, std::integral_constant<int, 1 - decltype(buf)::value>{});
+            if (it + 2 < ke) entries(it + 2, pbs);
+        }
+        if (it < ke) compute(masked, buf, it);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
     // Steps whose iterations (in both groups) hold only keys every row of the
-    // tile sees run without the mask; the rest, the causal diagonal, with it.
+    // tile sees run without the mask (an even number of them, so that the
+    // buffers stay fixed per unrolled step); the rest, the causal diagonal,
+    // with it.
     const int it_full = (ctx + r0 / G + 1) / (NB * kBlock);
-    const int j_full = KS == 1 ? min(it_full, half) : min(max(it_full - half, 0), half);
+    const int j_full = (KS == 1 ? min(it_full, half) : min(max(it_full - half, 0), half)) & ~1;
     int j = 0;
-    for (; j < j_full; ++j) step(std::false_type{}, j);
-    for (; j < half; ++j) step(std::true_type{}, j);
+    for (; j < j_full; j += 2) {
+        step(std::false_type{}, j, B0{});
+        step(std::false_type{}, j + 1, B1{});
+    }
+    for (; j < half; j += 2) {
+        step(std::true_type{}, j, B0{});
+        if (j + 1 < half) step(std::true_type{}, j + 1, B1{});
+    }
 
     // Each lane summed its own 4 keys per block: add the other lane groups.
 #pragma unroll
@@ -414,7 +449,7 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
         // Group 1 leaves its state in LDS (the tiles are no longer read: the
         // loop ended on a barrier); group 0 folds it into its own.  Lane-major
         // layout, so each store and load is one conflict-free row of 64 words.
-        float* st = reinterpret_cast<float*>(smem);
+        float* st = lds_state;
         if (kg == 1) {
 #pragma unroll
             for (int c = 0; c < NQ; ++c) {
