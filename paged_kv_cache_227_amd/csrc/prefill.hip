@@ -113,7 +113,11 @@ struct PrefillShape {
     static constexpr int SPAN = NB * TILE;      // bytes of an iteration's K (or V) rows
     static constexpr int BUF_BYTES = KS * 2 * SPAN;      // one buffer: [group][K, V] tiles
     static constexpr int STATE = TT * 4 + 2;             // floats of one lane's row state (acc, m, l)
-    static constexpr int MERGE_BYTES = KS > 1 ? NW * NQ * STATE * kWave * 4 : 16;
+    // Group 1's states go to the two (by then idle) buffers, half each, when
+    // they fit there, else to an array of their own.
+    static constexpr int STATE_A = (STATE + 1) / 2;      // floats in the first buffer
+    static constexpr bool STATE_IN_BUFFERS = KS > 1 && NW * NQ * STATE_A * kWave * 4 <= BUF_BYTES;
+    static constexpr int MERGE_BYTES = KS > 1 && !STATE_IN_BUFFERS ? NW * NQ * STATE * kWave * 4 : 16;
     static_assert(E::kBytes == 2 && D % 32 == 0 && CH == 4 * KK, "16-bit caches, head_dim a multiple of 32");
     static_assert(NB % 2 == 0, "PV takes blocks in pairs");
     static_assert(KS == 1 || KS == 2, "one or two key groups");
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT;
     // The two buffers are separate arrays, so the compiler can tell the LDS
     // loads filling one from the reads of the other (and need not wait for
-    // them before reading); the key groups' states meet in a third.
+    // them before reading); the key groups' states meet in them or in a third.
     __shared__ __attribute__((aligned(16))) char lds_a[SH::BUF_BYTES];
     __shared__ __attribute__((aligned(16))) char lds_b[SH::BUF_BYTES];
     __shared__ __attribute__((aligned(16))) float lds_state[SH::MERGE_BYTES / 4];
@@ -449,26 +453,34 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
         // Group 1 leaves its state in LDS (the tiles are no longer read: the
         // loop ended on a barrier); group 0 folds it into its own.  Lane-major
         // layout, so each store and load is one conflict-free row of 64 words.
-        float* st = lds_state;
+        // State element e of row group c: acc[t][r] at e = 4t + r, then m, l.
+        auto slot = [&](int c, int e) -> float* {
+            if constexpr (SH::STATE_IN_BUFFERS) {
+                constexpr int SB = SH::STATE - SH::STATE_A;
+                return e < SH::STATE_A
+                           ? reinterpret_cast<float*>(lds_a) + ((w * NQ + c) * SH::STATE_A + e) * kWave + lane
+                           : reinterpret_cast<float*>(lds_b) + ((w * NQ + c) * SB + e - SH::STATE_A) * kWave + lane;
+            } else {
+                return lds_state + ((w * NQ + c) * SH::STATE + e) * kWave + lane;
+            }
+        };
         if (kg == 1) {
 #pragma unroll
             for (int c = 0; c < NQ; ++c) {
-                float* b = st + (w * NQ + c) * SH::STATE * kWave + lane;
 #pragma unroll
                 for (int t = 0; t < TT; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) b[(4 * t + r) * kWave] = acc[c][t][r];
-                b[4 * TT * kWave] = m[c];
-                b[(4 * TT + 1) * kWave] = l[c];
+                    for (int r = 0; r < 4; ++r) *slot(c, 4 * t + r) = acc[c][t][r];
+                *slot(c, 4 * TT) = m[c];
+                *slot(c, 4 * TT + 1) = l[c];
             }
         }
         __syncthreads();
         if (kg == 1) return;
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-            const float* b = st + (w * NQ + c) * SH::STATE * kWave + lane;
-            const float m1 = b[4 * TT * kWave];
-            const float l1 = b[(4 * TT + 1) * kWave];
+            const float m1 = *slot(c, 4 * TT);
+            const float l1 = *slot(c, 4 * TT + 1);
             const float mm = fmaxf(m[c], m1);
             const float mr = mm == -INFINITY ? 0.f : mm;
             const float a0 = __builtin_amdgcn_exp2f(m[c] - mr);
@@ -477,7 +489,7 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
 #pragma unroll
             for (int t = 0; t < TT; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[c][t][r] = acc[c][t][r] * a0 + b[(4 * t + r) * kWave] * a1;
+                for (int r = 0; r < 4; ++r) acc[c][t][r] = acc[c][t][r] * a0 + *slot(c, 4 * t + r) * a1;
         }
     }
 #pragma unroll
@@ -504,17 +516,16 @@ hipError_t launch_prefill_shape(const PrefillParams& p, hipStream_t stream) {
 }
 
 // Launch shape (measured on MI355X): 8 waves of 16 query rows (128 rows per
-// workgroup) in each of KS key groups; 32 keys per iteration at head_dim 128
-// (64 at 64), i.e. 16 KiB of K and V per LDS buffer.  It needs no accumulator
-// registers beyond the architectural VGPRs and runs 4 waves per SIMD.  fp16
-// keeps one 16-bit P per weight (11 significant bits); bf16 splits P into high
-// and low parts, since one bf16 keeps only 8.
+// workgroup) in each of 2 key groups; 4 blocks (64 keys) per iteration, i.e.
+// 32 KiB (head_dim 128) or 16 KiB (64) of K and V per group and LDS buffer.  It
+// needs no accumulator registers beyond the architectural VGPRs and runs 4
+// waves per SIMD.  fp16 keeps one 16-bit P per weight (11 significant bits);
+// bf16 splits P into high and low parts, since one bf16 keeps only 8.
 template <class E, int D, int G>
 static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
-    constexpr int NB = D == 128 ? 2 : 4;
     constexpr bool SPLIT = std::is_same<E, BF16>::value;
     static_assert(8 * 16 == kPrefillRows, "the grid's tile height");
-    return launch_prefill_shape<E, D, G, 8, 1, NB, SPLIT, 2>(p, stream);
+    return launch_prefill_shape<E, D, G, 8, 1, 4, SPLIT, 2>(p, stream);
 }
 
 template <class E, int D>
