@@ -8,8 +8,8 @@
 //     layout of a 16x16 product is the B layout of the next one;
 //   the order of the contracted index inside one product is free as long as
 //     A and B agree, so two 4-element halves (from two 16x16 C tiles) make the
-//     8 elements of a 16x16x32 operand (pv2), which on gfx950 does twice the
-//     work of a 16x16x16 in the same issue time;
+//     8 elements of a 16x16x32 operand (pv2): one instruction for the work of
+//     two 16x16x16 ones;
 //   ds_read_b64_tr_b16: within each 16-lane group, element r of lane j is
 //     element j % 4 of the 8-byte row (4r + j / 4) of the 4 x 16 block read.
 #pragma once

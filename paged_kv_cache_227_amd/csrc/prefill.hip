@@ -108,7 +108,6 @@ struct PrefillShape {
     static constexpr int TT = D / 16;           // 16-wide output tiles
     static constexpr int ROWS_W = 16 * NQ;      // query rows per wave
     static constexpr int ROWS = NW * ROWS_W;    // query rows per workgroup
-    static constexpr int NT_G = NW * kWave;     // threads of one key group
     static constexpr int TILE = kBlock * RB;    // bytes of one block's K (or V) rows of one head
     static constexpr int SPAN = NB * TILE;      // bytes of an iteration's K (or V) rows
     static constexpr int BUF_BYTES = KS * 2 * SPAN;      // one buffer: [group][K, V] tiles
