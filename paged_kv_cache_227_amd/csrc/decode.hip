@@ -387,8 +387,7 @@ struct MfmaAttn {
             if (valid < kBlock && 4 * g + r >= valid) sc[r] = -INFINITY;
         }
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx = rows_max(mx);
         const float mn = fmaxf(m, mx);
         const float ms = mn == -INFINITY ? 0.f : mn;
         if (__builtin_amdgcn_ballot_w64(mn > m)) {
@@ -441,8 +440,7 @@ struct MfmaAttn {
     }
 
     __device__ __forceinline__ void reduce() {
-        l += shfl_xor(l, 16);
-        l += shfl_xor(l, 32);
+        l = rows_sum(l);
     }
 
     __device__ __forceinline__ void store_out(char* out_rows) const {

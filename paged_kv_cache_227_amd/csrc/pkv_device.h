@@ -157,6 +157,25 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
     return __shfl_xor(x, mask, kWave);
 }
 
+// Maximum and sum over the four 16-lane rows' matching lanes (l, l^16, l^32,
+// l^48), inside the vector ALU: v_permlane16_swap of a value with itself
+// leaves lane l holding, in row order, its own and lane l^16's values (and
+// v_permlane32_swap likewise for l^32), so both lanes of a pair combine the
+// same two values in the same order.  (Lane mapping checked on gfx950.)
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, shfl_xor(x, m));

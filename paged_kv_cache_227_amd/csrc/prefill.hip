@@ -122,25 +122,6 @@ struct PrefillShape {
     static_assert(KS == 1 || KS == 2, "one or two key groups");
 };
 
-// Maximum and sum over the four 16-lane rows' matching lanes (l, l^16, l^32,
-// l^48), inside the vector ALU: v_permlane16_swap of a value with itself
-// leaves lane l holding, in row order, its own and lane l^16's values (and
-// v_permlane32_swap likewise for l^32), so both lanes of a pair combine the
-// same two values in the same order.
-__device__ __forceinline__ float rows_max(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float rows_sum(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Word 3 of a raw buffer resource: 32-bit data format, no swizzle; with a
 // stride of 0 the size (word 2) is in bytes and reads at or past it return 0.
 constexpr int kBufferWord3 = 0x00020000;
