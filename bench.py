@@ -146,7 +146,7 @@ def run_gpu(w, steps, warmup, extras, graph=False):
                merge_ms_mean=statistics.fmean(t_merge), append_ms_mean=statistics.fmean(t_app))
 
     if extras:
-        # a plain streaming read of 4 GiB: what a simple coalesced kernel reaches
+        # a streaming read of 4 GiB: the HBM read rate a plain streaming kernel reaches
         buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
         buf.fill_(1)
         sink = torch.empty(4096, dtype=torch.float32, device=dev)
@@ -738,6 +738,8 @@ def main():
         from paged_kv_cache_227_amd import workloads as W
         res["probe_read_gbs"] = round(g["probe_read_gbs"], 1)
         res["decode_kernel_gbs_after_flush"] = round(kv / (g["partition_ms_flushed_median"] * 1e-3) / 1e9, 1)
+        # the decode kernel against the streaming-read probe (the practical HBM read ceiling)
+        res["decode_kernel_vs_probe_read"] = round(res["roofline"]["achieved"] / g["probe_read_gbs"], 4)
         if a.config == "llama2_7b":
             import math
             lens = w.context_lens
