@@ -190,8 +190,8 @@ pkv_status paged_kv_append_tokens(const void* k_new, const void* v_new, void* k_
  *   max_q_len     host int: the longest chunk (sizes the grid); rows of a
  *                 longer chunk are not computed
  *
- * Supported: fp16 / bf16 caches, block_size 16, head_dim 64 or 128, group
- * 1, 2, 4 or 8, num_seqs <= 65535 and max_q_len x group <= 65535 x 128 query
+ * Supported: fp16 / bf16 caches, block_size 8, 16, 32 or 64, head_dim 64 or
+ * 128, group 1, 2, 4 or 8, num_seqs <= 65535 and max_q_len x group <= 65535 x 128 query
  * rows (PKV_ENOTSUP otherwise; fp32 prefill is not served).  A sequence whose
  * chunk is empty or longer than its context is skipped.
  * pkv_validate_prefill() checks cu_q, the lengths and the tables on the host.

@@ -22,11 +22,10 @@ namespace {
 thread_local std::string g_last_error;
 std::atomic<int32_t> g_part_tokens{0};
 
-constexpr int kGpuBlockSize = 16;  // prefill serves this block size only
-constexpr int kTileTokens = 16;    // the decode kernels stream 16-token tiles
+constexpr int kTileTokens = 16;  // the decode and prefill kernels stream 16-token tiles
 
-// Block sizes the decode kernels serve: powers of two from 8 to 64 tokens (a
-// 16-token tile then lies in one block, or in two when B = 8).
+// Block sizes the decode and prefill kernels serve: powers of two from 8 to 64
+// tokens (a 16-token tile then lies in one block, or in two when B = 8).
 int decode_block_shift(int32_t B) {
     switch (B) {
         case 8: return 3;
@@ -348,9 +347,8 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
         return fail(PKV_EINVAL, "max_blocks_per_seq * block_size overflows int32");
     if (num_seqs > 0 && max_q_len > 0 && (!q || !k_cache || !v_cache || !block_tables || !cu_q || !context_lens || !out))
         return fail(PKV_EINVAL, "a required pointer is NULL");
-    if (layout->block_size != kGpuBlockSize)
-        return fail(PKV_ENOTSUP, "prefill serves block_size %d only (got %d)", kGpuBlockSize,
-                    layout->block_size);
+    if (decode_block_shift(layout->block_size) < 0)
+        return fail(PKV_ENOTSUP, "prefill serves block sizes 8, 16, 32 and 64 (got %d)", layout->block_size);
     const int group = n_q_heads / layout->n_kv_heads;
     if (!pkv::prefill_supported(layout->dtype, layout->head_dim, group))
         return fail(PKV_ENOTSUP, "no prefill kernel for dtype %d, head_dim %d, group %d (16-bit caches only)",
@@ -374,6 +372,7 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
     p.max_blocks = max_blocks_per_seq;
     p.num_seqs = num_seqs;
     p.max_q_len = max_q_len;
+    p.block_shift = decode_block_shift(layout->block_size);
     p.scale_log2 = scale * 1.4426950408889634f;
     hipError_t e = pkv::launch_prefill(p, layout->dtype, layout->head_dim, group, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prefill launch");

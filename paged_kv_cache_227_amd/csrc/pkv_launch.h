@@ -50,8 +50,9 @@ struct PrefillParams {
     int32_t n_q_heads;
     int32_t max_blocks;
     int32_t num_seqs;
-    int32_t max_q_len;  // longest chunk (sizes the grid)
-    float scale_log2;   // scale * log2(e)
+    int32_t max_q_len;    // longest chunk (sizes the grid)
+    int32_t block_shift;  // log2 of the block size (8 .. 64 tokens)
+    float scale_log2;     // scale * log2(e)
 };
 
 struct SwapParams {

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     const int Hq = p.n_q_heads;
     const int q0 = p.cu_q[s];
     const int n = p.cu_q[s + 1] - q0;
-    const int L = min(max(p.context_lens[s], 0), p.max_blocks * kBlock);
+    const int L = min(max(p.context_lens[s], 0), p.max_blocks << p.block_shift);
     if (n <= 0 || n > L) return;  // an empty or impossible chunk
     const int nrows = n * G;
     const int ntiles = (nrows + SH::ROWS - 1) / SH::ROWS;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     const int r0 = tile * SH::ROWS;
     const int ctx = L - n;  // tokens before the chunk
     const int wg_last_pos = ctx + (min(r0 + SH::ROWS, nrows) - 1) / G;
-    const int nblk = wg_last_pos / kBlock + 1;
+    const int nblk = wg_last_pos / kBlock + 1;  // 16-token tiles the workgroup reads
     const int nit = (nblk + NB - 1) / NB;
 
     const int tid = threadIdx.x;
@@ -239,27 +239,43 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
 
     // K and V go from memory straight into LDS (buffer loads with an LDS
     // destination).  One such instruction of a wave fills a contiguous 1 KiB
-    // of LDS, lane i bytes 16i .. 16i+15: RPR rows of one block of one cache.
-    // Lane i fetches the global chunk that the row's XOR swizzle puts in its
-    // slot.  The block's base address and the bytes of its rows inside the
+    // of LDS, lane i bytes 16i .. 16i+15: RPR rows of one 16-token tile of one
+    // cache, which lie in one cache block whatever the block size (RPR divides
+    // 8).  Lane i fetches the global chunk that the row's XOR swizzle puts in
+    // its slot.  The block's base address and the bytes of its rows inside the
     // sequence make the buffer resource, so rows past the context and invalid
     // table entries arrive as zeros (out-of-range buffer reads return 0).
     const uint32_t row_stride = (uint32_t)p.n_kv_heads * RB;
-    const int64_t blk_bytes = (int64_t)row_stride * kBlock;
+    const int bshift = p.block_shift;
+    const int bsize = 1 << bshift;
+    const int64_t blk_bytes = (int64_t)row_stride << bshift;
     const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
     const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
     constexpr int RPR = 1024 / RB;           // rows per load instruction
-    constexpr int RG = kBlock / RPR;         // load instructions per block and cache
+    constexpr int RG = kBlock / RPR;         // load instructions per tile and cache
     constexpr int PER_W = 2 * NB * RG / NW;  // load instructions per wave and iteration
-    static_assert(RPR * RB == 1024 && (2 * NB * RG) % NW == 0, "whole 1 KiB slices, the same count per wave");
-    // slice g = w + k NW of an iteration: cache g / (NB RG), block (g / RG) % NB, rows RPR (g % RG) ..
+    constexpr int STEP = NB * kBlock;        // tokens per iteration
+    static_assert(RPR * RB == 1024 && 8 % RPR == 0 && STEP % 64 == 0 && (2 * NB * RG) % NW == 0,
+                  "whole 1 KiB slices inside one block of 8 to 64, the same count per wave");
+    // Slice g = w + k NW of an iteration: cache g / (NB RG), tile (g / RG) % NB,
+    // rows RPR (g % RG) ..  An iteration spans a whole number of blocks, so
+    // the slice's row offset inside its block is the same in every iteration
+    // and goes into the lane offsets; the load's resource starts at the block
+    // and covers its rows inside the sequence.
+    int tok0[PER_W];   // first token of slice k in iteration 0
+    int tokb0[PER_W];  // first token of its block
     uint32_t voff[PER_W];
 #pragma unroll
     for (int k = 0; k < PER_W; ++k) {
-        const int row = ((w + k * NW) % RG) * RPR + lane / CH;
-        voff[k] = (uint32_t)row * row_stride + (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
+        const int g = w + k * NW;
+        tok0[k] = ((g / RG) % NB) * kBlock + (g % RG) * RPR;
+        tokb0[k] = tok0[k] & -bsize;
+        const int row = (g % RG) * RPR + lane / CH;  // row in the tile
+        voff[k] = (uint32_t)(tok0[k] - tokb0[k] + lane / CH) * row_stride + (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
     }
+    // slices past the workgroup's last tile, or past the sequence's last table entry, load nothing
+    const int tok_lim = min(nblk * kBlock, (L + bsize - 1) & -bsize);
     // LDS tiles of this key group in buffer BUF: [K, V][block][row][RB]
     auto tiles = [&](auto bufc, int kv) {
         return (decltype(bufc)::value ? lds_b : lds_a) + (kg * 2 + kv) * SH::SPAN;
@@ -269,8 +285,8 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     auto entries = [&](int it, int (&pbs)[PER_W]) {
 #pragma unroll
         for (int k = 0; k < PER_W; ++k) {
-            const int b = it * NB + ((w + k * NW) / RG) % NB;
-            pbs[k] = b < nblk ? table[b] : -1;
+            const int tok = it * STEP + tok0[k];
+            pbs[k] = tok < tok_lim ? table[tok >> bshift] : -1;
         }
     };
     auto issue = [&](int it, const int (&pbs)[PER_W], auto buf) {
@@ -278,10 +294,9 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
         for (int k = 0; k < PER_W; ++k) {
             const int g = w + k * NW;  // uniform over the wave
             const int kv = g / (NB * RG), nb = (g / RG) % NB;
-            const int b = it * NB + nb;
             const int pb = __builtin_amdgcn_readfirstlane(pbs[k]);
             const bool ok = pb >= 0 && pb < p.num_blocks;
-            const int rows = min(max(L - b * kBlock, 0), kBlock);
+            const int rows = min(max(L - (it * STEP + tokb0[k]), 0), bsize);  // rows of the block in the sequence
             // the size is uniform already; readfirstlane keeps the resource in scalar registers
             lds_load_1k((kv ? vbase : kbase) + (ok ? (int64_t)pb * blk_bytes : 0), ok ? (int)(rows * row_stride) : 0,
                         tiles(buf, kv) + nb * SH::TILE + (g % RG) * 1024, voff[k]);

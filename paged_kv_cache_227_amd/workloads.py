@@ -426,7 +426,7 @@ class PrefillWorkload:
 
 def build_prefill(name: str, context: _Seq[int], chunk: _Seq[int], n_q_heads: int, n_kv_heads: int,
                   head_dim: int, dtype: str, seed: int, pool_factor: float = 1.0, data_mult: float = 1.0,
-                  notes: str = "") -> PrefillWorkload:
+                  notes: str = "", block_size: int = BLOCK_SIZE) -> PrefillWorkload:
     """Sequence s has context[s] tokens cached and a chunk of chunk[s] new ones.
     Tables, caches and scale come from ``build`` (same seeded streams); the
     chunk's q / k_new / v_new rows come from a stream of their own."""
@@ -434,7 +434,7 @@ def build_prefill(name: str, context: _Seq[int], chunk: _Seq[int], n_q_heads: in
     chunk = np.asarray(chunk, dtype=np.int64)
     lens = context + chunk
     w = build(name, lens, n_q_heads, n_kv_heads, head_dim, dtype, seed, pool_factor=pool_factor,
-              data_mult=data_mult, notes=notes)
+              data_mult=data_mult, notes=notes, block_size=block_size)
     c_q, c_kn, c_vn = np.random.SeedSequence([seed, 11]).spawn(3)
     total = int(chunk.sum())
     cu = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
@@ -447,28 +447,39 @@ def build_prefill(name: str, context: _Seq[int], chunk: _Seq[int], n_q_heads: in
         k_cache=w.k_cache, v_cache=w.v_cache, scale=w.scale, seed=seed, notes=notes)
 
 
-def prefill_llama2_7b(chunk: int = 512, seed: int = SEED_BASE + 7) -> PrefillWorkload:
+def _b_suffix(block_size: int) -> str:
+    return "" if block_size == BLOCK_SIZE else "_b%d" % block_size
+
+
+def prefill_llama2_7b(chunk: int = 512, seed: int = SEED_BASE + 7, block_size: int = BLOCK_SIZE) -> PrefillWorkload:
     """Chunked prefill of 2,048-token prompts on the Llama-2-7B layer (32/32
     heads, D=128, fp16; data N(0,1)/sqrt(128)), one step with four prompts at
     the four stages of a 512-token chunking: contexts 0, 512, 1024 and 1536
     tokens cached, each with its next 512-token chunk."""
     stages = 2048 // chunk
-    return build_prefill("prefill_llama2_7b", [i * chunk for i in range(stages)], [chunk] * stages, 32, 32, 128,
-                         "f16", seed, data_mult=1.0 / math.sqrt(128.0),
-                         notes="2048-token prompts in %d-token chunks, one prompt per stage" % chunk)
+    return build_prefill("prefill_llama2_7b" + _b_suffix(block_size), [i * chunk for i in range(stages)],
+                         [chunk] * stages, 32, 32, 128, "f16", seed, data_mult=1.0 / math.sqrt(128.0),
+                         notes="2048-token prompts in %d-token chunks, one prompt per stage" % chunk,
+                         block_size=block_size)
 
 
-def prefill_gqa_8b(chunk: int = 512, seed: int = SEED_BASE + 8) -> PrefillWorkload:
+def prefill_gqa_8b(chunk: int = 512, seed: int = SEED_BASE + 8, block_size: int = BLOCK_SIZE) -> PrefillWorkload:
     """The same chunking on the GQA 8B layer (32 q heads, 8 KV heads, D=128, bf16)."""
     stages = 2048 // chunk
-    return build_prefill("prefill_gqa_8b", [i * chunk for i in range(stages)], [chunk] * stages, 32, 8, 128,
-                         "bf16", seed, notes="2048-token prompts in %d-token chunks, one prompt per stage" % chunk)
+    return build_prefill("prefill_gqa_8b" + _b_suffix(block_size), [i * chunk for i in range(stages)],
+                         [chunk] * stages, 32, 8, 128, "bf16", seed,
+                         notes="2048-token prompts in %d-token chunks, one prompt per stage" % chunk,
+                         block_size=block_size)
 
 
 PREFILL_CONFIGS = {
     "prefill_llama2_7b": prefill_llama2_7b,
     "prefill_gqa_8b": prefill_gqa_8b,
 }
+# the same steps with the caches in blocks of 8, 32 or 64 tokens (prefill_<layer>_b<B>)
+for _base, _fn in list(PREFILL_CONFIGS.items()):
+    for _B in (8, 32, 64):
+        PREFILL_CONFIGS["%s_b%d" % (_base, _B)] = (lambda f=_fn, B=_B: f(block_size=B))
 
 
 # --------------------------------------------------------------------------

@@ -177,7 +177,8 @@ def test_prefill_rejects(L):
     assert call(lay=_layout(dtype=0, head_dim=128)) == _lib.PKV_ENOTSUP     # fp32 prefill is not served
     assert "16-bit" in _lib.last_error()
     assert call(lay=_layout(dtype=2, head_dim=96)) == _lib.PKV_ENOTSUP
-    assert call(lay=_layout(dtype=2, block_size=32)) == _lib.PKV_ENOTSUP
+    assert call(lay=_layout(dtype=2, block_size=12)) == _lib.PKV_ENOTSUP    # not a power of two in 8 .. 64
+    assert call(lay=_layout(dtype=2, block_size=128)) == _lib.PKV_ENOTSUP
     assert call(Hq=12) == _lib.PKV_ENOTSUP                                 # group of 3
     assert call(S=65536) == _lib.PKV_ENOTSUP                               # the grid's sequence dimension
     assert call(maxq=65535 * 128 // 4 + 1, Hq=16) == _lib.PKV_ENOTSUP     # more than 65535 tiles of 128 rows

@@ -203,3 +203,57 @@ def test_prefill_rising_scores(dtype):
     pos = np.concatenate([np.arange(int(w.cu_q[s + 1] - w.cu_q[s])) for s in range(w.num_seqs)])
     w.k_new = to_storage(k * (1.0 + pos / 16.0)[:, None, None], code)
     _check(w)
+
+
+BLOCK_CASES = [(B, dt, D, G) for B in (8, 32, 64) for dt, D, G in (("f16", 128, 1), ("bf16", 128, 4), ("bf16", 64, 8))]
+
+
+@pytest.mark.parametrize("B,dtype,D,G", BLOCK_CASES, ids=["b%d-%s-d%d-g%d" % c for c in BLOCK_CASES])
+def test_prefill_block_sizes(B, dtype, D, G):
+    """Cache blocks of 8, 32 and 64 tokens (16 is covered above): a 16-token
+    tile spans two blocks or part of one; contexts and chunks cross block
+    edges."""
+    w = W.build_prefill("block_%d" % B, [0, 5, 31, 64, 200], [33, 1, 40, 64, 129], 2 * G, 2, D, dtype,
+                        3600 + B + D + G, pool_factor=1.3, block_size=B)
+    _check(w)
+
+
+def _relayout(w, B, rng):
+    """The same workload with its caches laid out in blocks of B tokens (each
+    sequence's tokens gathered through its table, placed in shuffled blocks)."""
+    import copy
+    from pkv_testutil import sequential_fill
+    L = w.context_lens.astype(int)
+    need = [-(-int(n) // B) for n in L]
+    nb = sum(need) + 3
+    perm = rng.permutation(nb)
+    tables = np.full((w.num_seqs, max(need)), -1, np.int32)
+    caches = []
+    for src in (w.k_cache, w.v_cache):
+        dst = np.zeros((nb, B) + src.shape[2:], src.dtype)
+        off = 0
+        for s_, n in enumerate(need):
+            t = perm[off:off + n]
+            off += n
+            rows = np.stack([src[w.block_tables[s_][i // w.block_size], i % w.block_size] for i in range(L[s_])])
+            sequential_fill(dst, t, rows)
+            tables[s_, :n] = t
+        caches.append(dst)
+    w2 = copy.copy(w)
+    w2.block_size, w2.num_blocks, w2.block_tables = B, nb, tables
+    w2.k_cache, w2.v_cache = caches
+    return w2
+
+
+def test_prefill_same_tokens_any_block_size_bitwise():
+    """The same tokens laid out in blocks of 8, 16, 32 and 64: the kernel sees
+    the same 16-token tiles, so the outputs are identical bits (and the caches
+    after the append hold the same tokens)."""
+    rng = np.random.default_rng(3700)
+    base = W.build_prefill("same_tokens", [0, 100, 300], [200, 57, 130], 16, 4, 128, "bf16", 3700)
+    outs = []
+    for B in (8, 16, 32, 64):
+        _, _, got = gpu_prefill(_poisoned(_relayout(base, B, rng)))
+        outs.append(got)
+        say("  B=%d done" % B)
+    assert all(np.array_equal(outs[0], o) for o in outs[1:]), "outputs differ between block sizes"
