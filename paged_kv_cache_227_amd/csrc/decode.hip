@@ -116,6 +116,13 @@ struct WaveAttn {
             for (int k = 0; k < CPL; ++k) qv[gi][k] = load16(q_rows + (hd * G + gi) * RB + (c + k * R) * 16);
     }
 
+    __device__ __forceinline__ void settle_q() const {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) settle(qv[gi][k]);
+    }
+
     __device__ __forceinline__ void reset() {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
@@ -339,6 +346,13 @@ struct MfmaAttn {
             }
     }
 
+    __device__ __forceinline__ void settle_q() const {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) settle(qb[h][kk]);
+    }
+
     __device__ __forceinline__ void reset() {
         m = -INFINITY;
         l = 0.f;
@@ -480,6 +494,20 @@ struct TileAddr {
     bool ok;
 };
 
+// Loads issued past the end of a wave's tiles read rows 0-7 of block 0 twice
+// (lo = 0, hi = -8 rows): inside the cache at every block size.
+constexpr int kDummyRows = 8;
+
+// A table entry is read with a scalar load: the table is constant while the
+// kernel runs and the wave's index is uniform, so the read goes through the
+// constant address space.  A vector load would be counted together with the
+// K/V loads in flight, and waiting for its value would wait for all of them.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+__device__ __forceinline__ int table_entry(const int32_t* table, int i) {
+    return ((const_i32*)table)[__builtin_amdgcn_readfirstlane(i)];
+}
+
 __device__ __forceinline__ TileAddr tile_addr(const int32_t* table, int t, int ntab, int shift, int num_blocks,
                                               uint32_t row_stride) {
     const int tok0 = t * kBlock;
@@ -488,8 +516,8 @@ __device__ __forceinline__ TileAddr tile_addr(const int32_t* table, int t, int n
     const int bi0 = tok0 >> shift;
     const int bi1 = (tok0 + 8) >> shift;
     const bool second = bi1 != bi0 && bi1 < ntab;
-    int pb0 = __builtin_amdgcn_readfirstlane(table[bi0]);
-    int pb1 = second ? __builtin_amdgcn_readfirstlane(table[bi1]) : pb0;
+    int pb0 = table_entry(table, bi0);
+    int pb1 = second ? table_entry(table, bi1) : pb0;
     TileAddr a;
     a.ok = pb0 >= 0 && pb0 < num_blocks && pb1 >= 0 && pb1 < num_blocks;
     if (!a.ok) pb0 = pb1 = 0;
@@ -599,12 +627,19 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     a.init(lane, row_stride, dyn_lds + wave_id_uniform() * A::kLdsBytes);
     bool oks[NS];
     const int bmask = (1 << p.block_shift) - 1;
-    auto issue = [&](int slot, const Cur& q) {
-        const int ntab = (Ls[q.s] + bmask) >> p.block_shift;
-        const TileAddr ta = tile_addr(p.block_tables + (int64_t)q.s * p.max_blocks, q.b, ntab, p.block_shift,
-                                      p.num_blocks, row_stride);
-        a.issue(slot, kcache + (int64_t)q.kvh * A::NH * A::RB, vcache + (int64_t)q.kvh * A::NH * A::RB, ta.lo,
-                ta.hi);
+    // Every pass issues its loads, also past the wave's last tile (then of the
+    // first rows of block 0, never computed): loads are counted in issue order,
+    // and a load issued on one path only would make the wait for the tile
+    // being computed also wait for the tiles issued after it.
+    auto issue = [&](int slot, const Cur& q, bool real) {
+        TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
+        if (real) {
+            const int ntab = (Ls[q.s] + bmask) >> p.block_shift;
+            ta = tile_addr(p.block_tables + (int64_t)q.s * p.max_blocks, q.b, ntab, p.block_shift, p.num_blocks,
+                           row_stride);
+        }
+        const int64_t hoff = real ? (int64_t)q.kvh * A::NH * A::RB : 0;
+        a.issue(slot, kcache + hoff, vcache + hoff, ta.lo, ta.hi);
         oks[slot] = ta.ok;
     };
 
@@ -615,11 +650,11 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     cur.nb = __builtin_amdgcn_readfirstlane(cur.nb);
     Cur iss = cur;
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (t0 + d < t1) {
-            issue(d, iss);
-            advance(iss);
-        }
+    for (int d = 0; d < DEPTH; ++d) {
+        const bool real = t0 + d < t1;
+        issue(d, iss, real);
+        if (real) advance(iss);
+    }
 
     int as = cur.s, akvh = cur.kvh;  // the segment being accumulated
     a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
@@ -641,16 +676,16 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             const int tt = t + u;
-            if (tt + DEPTH < t1) {
-                issue((u + DEPTH) % NS, iss);
-                advance(iss);
-            }
+            const bool real = tt + DEPTH < t1;
+            issue((u + DEPTH) % NS, iss, real);
+            if (real) advance(iss);
             if (tt < t1) {
                 if (cur.s != as || cur.kvh != akvh) {
                     flush();
                     as = cur.s;
                     akvh = cur.kvh;
                     a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
+                    a.settle_q();  // here, not at the next product, where it would also wait for the next tiles
                     a.reset();
                 }
                 const int valid = !oks[u] ? 0 : (cur.b == cur.nb - 1 ? Ls[cur.s] - cur.b * kBlock : kBlock);
@@ -801,21 +836,23 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     a.reset();
     bool oks[NS];
     const int ntab = (L + (1 << p.block_shift) - 1) >> p.block_shift;
-    auto issue = [&](int slot, int bi) {
-        const TileAddr ta = tile_addr(table, bi, ntab, p.block_shift, p.num_blocks, row_stride);
+    // As in the flat schedule, every pass issues its loads (past the
+    // partition's end, of the first rows of block 0, never computed).
+    auto issue = [&](int slot, int bi, bool real) {
+        TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
+        if (real) ta = tile_addr(table, bi, ntab, p.block_shift, p.num_blocks, row_stride);
         a.issue(slot, kbase, vbase, ta.lo, ta.hi);
         oks[slot] = ta.ok;
     };
 
     // Block b_begin + k goes through register slot k % NS, DEPTH blocks ahead.
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        if (b_begin + d < b_end) issue(d, b_begin + d);
+    for (int d = 0; d < DEPTH; ++d) issue(d, b_begin + d, b_begin + d < b_end);
     for (int bi = b_begin; bi < b_end; bi += NS) {
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             const int b = bi + u;
-            if (b + DEPTH < b_end) issue((u + DEPTH) % NS, b + DEPTH);
+            issue((u + DEPTH) % NS, b + DEPTH, b + DEPTH < b_end);
             if (b < b_end) {
                 const int valid = !oks[u] ? 0 : (b == nblk - 1 ? tail_rows : kBlock);
                 a.process(u, valid, p.scale_log2);

@@ -53,6 +53,14 @@ __device__ __forceinline__ Vec16 load16_policy(const void* p) {
         return load16(p);
 }
 
+// The wave waits here until v has arrived: an empty asm statement reads v's
+// registers.  Loads are counted in issue order, so a load on a rarely taken
+// branch would otherwise be waited for where the branches join, together with
+// every load issued before it.
+__device__ __forceinline__ void settle(const Vec16& v) {
+    asm volatile("" ::"v"(v.w[0]), "v"(v.w[1]), "v"(v.w[2]), "v"(v.w[3]));
+}
+
 __device__ __forceinline__ void store16(void* p, const Vec16& v) {
     *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
 }
