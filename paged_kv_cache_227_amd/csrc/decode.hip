@@ -233,24 +233,43 @@ struct WaveAttn {
         }
     }
 
-    // After reduce, row group 0 writes the normalised rows of the HG query
-    // heads ([HG][D] at out_rows) ...
-    __device__ __forceinline__ void store_out(char* out_rows) const {
+    // A segment's state after reduce, as this lane holds it.  The flat
+    // schedule keeps one finished segment's Result in registers and writes it
+    // after the tile loop when it is small (kHold).
+    struct Result {
+        float acc[G][EPL];
+        float m[G], l[G];
+    };
+    static constexpr bool kHold = G * (EPL + 2) <= 40;
+
+    __device__ __forceinline__ void take(Result& r) const {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) r.acc[gi][e] = acc[gi][e];
+            r.m[gi] = m[gi];
+            r.l[gi] = l[gi];
+        }
+    }
+
+    // Row group 0 writes the normalised rows of the HG query heads ([HG][D]
+    // at out_rows) ...
+    __device__ __forceinline__ void store_out(const Result& r, char* out_rows) const {
         if (rg != 0) return;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
-            const float inv = 1.f / l[gi];
+            const float inv = 1.f / r.l[gi];
             const int row = hd * G + gi;
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    E::store(out_rows + (row * D + (c + k * R) * VEC + e) * E::kBytes, acc[gi][k * VEC + e] * inv);
+                    E::store(out_rows + (row * D + (c + k * R) * VEC + e) * E::kBytes, r.acc[gi][k * VEC + e] * inv);
         }
     }
 
     // ... or the partial record: acc [HG][D] fp32 and (m, l) [HG][2] fp32.
-    __device__ __forceinline__ void store_partial(float* rec_acc, float* rec_ml) const {
+    __device__ __forceinline__ void store_partial(const Result& r, float* rec_acc, float* rec_ml) const {
         if (rg != 0) return;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
@@ -260,11 +279,11 @@ struct WaveAttn {
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4)
                     *reinterpret_cast<float4*>(rec_acc + row * D + (c + k * R) * VEC + e) =
-                        make_float4(acc[gi][k * VEC + e], acc[gi][k * VEC + e + 1], acc[gi][k * VEC + e + 2],
-                                    acc[gi][k * VEC + e + 3]);
+                        make_float4(r.acc[gi][k * VEC + e], r.acc[gi][k * VEC + e + 1], r.acc[gi][k * VEC + e + 2],
+                                    r.acc[gi][k * VEC + e + 3]);
             if (c == 0) {
-                rec_ml[row * 2] = m[gi];
-                rec_ml[row * 2 + 1] = l[gi];
+                rec_ml[row * 2] = r.m[gi];
+                rec_ml[row * 2 + 1] = r.l[gi];
             }
         }
     }
@@ -457,24 +476,38 @@ struct MfmaAttn {
         l = rows_sum(l);
     }
 
-    __device__ __forceinline__ void store_out(char* out_rows) const {
+    // A segment's state after reduce (see WaveAttn::Result).
+    struct Result {
+        f32x4_t acc[TT];
+        float m, l;
+    };
+    static constexpr bool kHold = HG <= 4;  // more query heads leave no registers to spare
+
+    __device__ __forceinline__ void take(Result& r) const {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) r.acc[t] = acc[t];
+        r.m = m;
+        r.l = l;
+    }
+
+    __device__ __forceinline__ void store_out(const Result& r, char* out_rows) const {
         if (j >= HG) return;
-        const float inv = 1.f / l;
+        const float inv = 1.f / r.l;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) E::store(out_rows + (j * D + 16 * t + 4 * g + r) * 2, acc[t][r] * inv);
+            for (int i = 0; i < 4; ++i) E::store(out_rows + (j * D + 16 * t + 4 * g + i) * 2, r.acc[t][i] * inv);
     }
 
-    __device__ __forceinline__ void store_partial(float* rec_acc, float* rec_ml) const {
+    __device__ __forceinline__ void store_partial(const Result& r, float* rec_acc, float* rec_ml) const {
         if (j >= HG) return;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
             *reinterpret_cast<float4*>(rec_acc + j * D + 16 * t + 4 * g) =
-                make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+                make_float4(r.acc[t][0], r.acc[t][1], r.acc[t][2], r.acc[t][3]);
         if (g == 0) {
-            rec_ml[j * 2] = m;
-            rec_ml[j * 2 + 1] = l;
+            rec_ml[j * 2] = r.m;
+            rec_ml[j * 2 + 1] = r.l;
         }
     }
 };
@@ -648,6 +681,11 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     cur.kvh = __builtin_amdgcn_readfirstlane(cur.kvh);
     cur.b = __builtin_amdgcn_readfirstlane(cur.b);
     cur.nb = __builtin_amdgcn_readfirstlane(cur.nb);
+    // q before the first tiles: the wait for a tile then also covers q.
+    int as = cur.s, akvh = cur.kvh;  // the segment being accumulated
+    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
+    a.reset();
+
     Cur iss = cur;
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
@@ -656,19 +694,37 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         if (real) advance(iss);
     }
 
-    int as = cur.s, akvh = cur.kvh;  // the segment being accumulated
-    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
-    a.reset();
-
+    // A finished segment is written as normalised output rows when this wave
+    // held the whole pair, else as the partial record of (pair, wave).
+    auto emit = [&](const typename A::Result& r, bool whole, int64_t dst) {
+        if (whole) a.store_out(r, static_cast<char*>(p.out) + dst * D * E::kBytes);
+        else a.store_partial(r, p.ws_acc + dst * A::HG * D, p.ws_ml + dst * A::HG * 2);
+    };
+    // Stores are counted together with the loads in flight, and the registers
+    // that format them may still await a prefetched tile, so a store inside
+    // the tile loop makes the next wait also wait for the tiles issued before
+    // it.  With a small Result the wave keeps one finished segment in
+    // registers and writes it after its last tile; only a third segment
+    // writes the held one inside the loop.
+    typename A::Result held;
+    bool held_whole = false, have_held = false;
+    int64_t held_dst = 0;
     auto flush = [&]() {
         a.reduce();
         const int nb = (Ls[as] + kBlock - 1) / kBlock;
         const int p0 = pre[as] + akvh * nb;  // the pair's tiles are [p0, p0 + nb)
-        if (p0 / per == (p0 + nb - 1) / per) {
-            a.store_out(static_cast<char*>(p.out) + ((int64_t)as * Hq + akvh * A::HG) * D * E::kBytes);
+        const bool whole = p0 / per == (p0 + nb - 1) / per;
+        const int64_t dst = whole ? (int64_t)as * Hq + akvh * A::HG : (int64_t)as * NG + akvh + w;
+        if constexpr (A::kHold) {
+            if (have_held) emit(held, held_whole, held_dst);
+            a.take(held);
+            held_whole = whole;
+            held_dst = dst;
+            have_held = true;
         } else {
-            const int64_t rec = (int64_t)as * NG + akvh + w;
-            a.store_partial(p.ws_acc + rec * A::HG * D, p.ws_ml + rec * A::HG * 2);
+            typename A::Result r;
+            a.take(r);
+            emit(r, whole, dst);
         }
     };
 
@@ -695,6 +751,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         }
     }
     flush();
+    if constexpr (A::kHold) emit(held, held_whole, held_dst);
 }
 
 // Log-sum-exp combination, by one wave, of n partial records: record x has its
@@ -860,11 +917,13 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
         }
     }
     a.reduce();
+    typename A::Result r;
+    a.take(r);
     if (n_parts == 1) {
-        a.store_out(out_rows);
+        a.store_out(r, out_rows);
     } else {  // record [sequence][head group][partition] of [HG][D] acc and [HG][2] (m, l)
         const int64_t rec = ((int64_t)s * NG + hg) * p.n_parts_max + part;
-        a.store_partial(p.ws_acc + rec * HG * D, p.ws_ml + rec * HG * 2);
+        a.store_partial(r, p.ws_acc + rec * HG * D, p.ws_ml + rec * HG * 2);
     }
 }
 
