@@ -756,19 +756,42 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
 
 // Log-sum-exp combination, by one wave, of n partial records: record x has its
 // (m, l) at ml[(first + x * stride) * 2] and its acc row at acc[(first + x * stride) * D].
-// The records' (m, l) are read by all lanes at once; the weighted sum over the
-// acc rows keeps several rows' loads in flight.
+// A pair usually has a few records, so the (m, l) of records 0..63 (one per
+// lane) and the acc rows of records 0..3 are loaded together, before anything
+// waits: one memory round trip serves the common case.  Further acc rows are
+// read UNROLL at a time.
 template <class E, int D>
 __device__ __forceinline__ void merge_records(const float* ml, const float* acc, int64_t first, int stride, int n,
                                               char* out_row) {
     constexpr int PER = (D + kWave - 1) / kWave;
     constexpr int UNROLL = 4;
     const int lane = threadIdx.x % kWave;
-    float M = -INFINITY;
-    for (int x = lane; x < n; x += kWave) M = fmaxf(M, ml[(first + (int64_t)x * stride) * 2]);
+    auto load_rows = [&](int x0, int i, int cnt, float (&a)[UNROLL][PER]) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const bool ok = i + u < cnt;
+            const int64_t r = first + (int64_t)(x0 + (ok ? i + u : 0)) * stride;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int d = lane + k * kWave;
+                a[u][k] = (ok && d < D) ? acc[r * D + d] : 0.f;
+            }
+        }
+    };
+    float a0[UNROLL][PER];
+    load_rows(0, 0, min(kWave, n), a0);
+    float m0 = -INFINITY, l0 = 0.f;  // record `lane` (the first 64)
+    if (lane < n) {
+        const int64_t r = first + (int64_t)lane * stride;
+        m0 = ml[r * 2];
+        l0 = ml[r * 2 + 1];
+    }
+    float M = m0;
+    for (int x = lane + kWave; x < n; x += kWave) M = fmaxf(M, ml[(first + (int64_t)x * stride) * 2]);
     M = wave_max(M);
-    float den = 0.f;
-    for (int x = lane; x < n; x += kWave) {
+    const float w0 = lane < n ? __builtin_amdgcn_exp2f(m0 - M) : 0.f;
+    float den = w0 * l0;
+    for (int x = lane + kWave; x < n; x += kWave) {
         const int64_t r = first + (int64_t)x * stride;
         den += __builtin_amdgcn_exp2f(ml[r * 2] - M) * ml[r * 2 + 1];
     }
@@ -780,21 +803,20 @@ __device__ __forceinline__ void merge_records(const float* ml, const float* acc,
     for (int x0 = 0; x0 < n; x0 += kWave) {
         // weights of records x0 .. x0+63, one per lane, then broadcast
         const int xl = x0 + lane;
-        const float fl = xl < n ? __builtin_amdgcn_exp2f(ml[(first + (int64_t)xl * stride) * 2] - M) : 0.f;
+        const float fl = x0 == 0 ? w0 : (xl < n ? __builtin_amdgcn_exp2f(ml[(first + (int64_t)xl * stride) * 2] - M) : 0.f);
         const int cnt = min(kWave, n - x0);
         for (int i = 0; i < cnt; i += UNROLL) {
             float a[UNROLL][PER], f[UNROLL];
+            if (x0 == 0 && i == 0) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const bool ok = i + u < cnt;
-                f[u] = __shfl(fl, i + u, kWave);
-                const int64_t r = first + (int64_t)(x0 + (ok ? i + u : 0)) * stride;
+                for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-                for (int k = 0; k < PER; ++k) {
-                    const int d = lane + k * kWave;
-                    a[u][k] = (ok && d < D) ? acc[r * D + d] : 0.f;
-                }
+                    for (int k = 0; k < PER; ++k) a[u][k] = a0[u][k];
+            } else {
+                load_rows(x0, i, cnt, a);
             }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) f[u] = __shfl(fl, i + u, kWave);
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
