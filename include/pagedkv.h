@@ -314,6 +314,40 @@ pkv_status paged_attention_merge(const pkv_layout* layout, int32_t max_blocks_pe
                                  size_t ws_bytes, void* stream);
 
 /*
+ * paged_kv_append_attention_decode_ws -- paged_kv_append followed by
+ * paged_attention_decode_ws, as one call with the same result: the same
+ * caches afterwards (each new row bit-copied to its slot) and the same
+ * output bits.  The new token's K/V enter the attention exactly as the
+ * append would have stored them ("How a serving engine actually works",
+ * paperfordummies.in, "The one formula"; the appended token is attended in
+ * the same step -- henryhe.ai, "What's deliberately still missing").
+ *
+ *   k_new, v_new, positions   as for paged_kv_append
+ *   the rest                  as for paged_attention_decode_ws
+ *
+ * Under the flat schedule this runs two kernels, not three: the decode pass
+ * reads the row at positions[s] from k_new / v_new instead of the cache, and
+ * the merge pass, after every read of the step, writes the rows to their
+ * slots.  Under fixed partitions it is the two calls.  The caches are written
+ * during the call (k_cache, v_cache are not const).  Errors as for the two
+ * calls; a NULL k_new, v_new or positions is PKV_EINVAL.
+ */
+pkv_status paged_kv_append_attention_decode_ws(const void* k_new, const void* v_new, const int32_t* positions,
+                                               const void* q, void* k_cache, void* v_cache,
+                                               const pkv_layout* layout, const int32_t* block_tables,
+                                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                               int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                                               int32_t part_tokens, void* workspace, size_t ws_bytes,
+                                               void* stream);
+
+/* The same with the library's workspace and partition choice (as paged_attention_decode). */
+pkv_status paged_kv_append_attention_decode(const void* k_new, const void* v_new, const int32_t* positions,
+                                            const void* q, void* k_cache, void* v_cache, const pkv_layout* layout,
+                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                            float scale, void* out, void* stream);
+
+/*
  * Process-wide partition length used when a call passes 0 (and by
  * paged_attention_decode): a positive multiple of 16 (and, at call time, of
  * the block size), or 0 to

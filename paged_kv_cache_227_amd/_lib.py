@@ -42,6 +42,10 @@ SIGNATURES = {
     "paged_attention_partitions": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _I32, _I32, _F32, _P,
                                                   _I32, _P, _SZ, _P]),
     "paged_attention_merge": (ctypes.c_int, [_LP, _I32, _P, _I32, _I32, _P, _I32, _P, _SZ, _P]),
+    "paged_kv_append_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _LP, _P, _I32, _P, _I32, _I32,
+                                                        _F32, _P, _P]),
+    "paged_kv_append_attention_decode_ws": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _LP, _P, _I32, _P, _I32, _I32,
+                                                           _F32, _P, _I32, _P, _SZ, _P]),
     "pkv_set_partition_tokens": (ctypes.c_int, [_I32]),
     "pkv_partition_tokens_for": (_I32, [_I32, _I32, _I32, _LP]),
     "pkv_validate": (ctypes.c_int, [_LP, _P, _I32, _P, _P, _I32]),
@@ -313,6 +317,32 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         _i32(block_tables, "block_tables"), block_tables.shape[1], _i32(context_lens, "context_lens"),
         S, Hq, float(scale), _dev(out, "out"), part_tokens, _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), st), "paged_attention_decode_ws")
+
+
+def paged_kv_append_attention_decode(k_new, v_new, positions, q, k_cache, v_cache, block_tables, context_lens,
+                                     scale, out, part_tokens: int = 0, workspace=None, stream=None) -> None:
+    """paged_kv_append(k_new, v_new, ...) then paged_attention_decode(q, ...), as
+    one call with the same caches and output bits afterwards (two kernels
+    under the flat schedule)."""
+    L, S, Hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out)
+    want = (S, L.n_kv_heads, L.head_dim)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+        raise ValueError("k_new / v_new must be %r" % (want,))
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("k_new / v_new must have the cache dtype")
+    _check_tables(block_tables, positions, S, "positions")
+    st = _stream(stream, q.device)
+    head = (_dev(k_new, "k_new"), _dev(v_new, "v_new"), _i32(positions, "positions"), _dev(q, "q"),
+            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L), _i32(block_tables, "block_tables"),
+            block_tables.shape[1], _i32(context_lens, "context_lens"), S, Hq, float(scale), _dev(out, "out"))
+    if workspace is None and part_tokens == 0:
+        _check(lib().paged_kv_append_attention_decode(*head, st), "paged_kv_append_attention_decode")
+        return
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, block_tables, part_tokens)
+    _check(lib().paged_kv_append_attention_decode_ws(*head, part_tokens, _dev(workspace, "workspace"),
+                                                     workspace.numel() * workspace.element_size(), st),
+           "paged_kv_append_attention_decode_ws")
 
 
 def paged_attention_partitions(q, k_cache, v_cache, block_tables, context_lens, scale, out, part_tokens,

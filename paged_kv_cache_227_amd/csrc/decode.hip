@@ -135,15 +135,20 @@ struct WaveAttn {
 
     // Loads of one tile: row r of head g at kbase/vbase + (r < 8 ? lo : hi) + r * row_stride.
     // A load instruction covers RPS consecutive rows, all in the same half.
-    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi) {
+    // Tile row `prow` (if 0..15) is read from the rows kn, vn ([NH][D] of the
+    // token being appended) instead of the cache.
+    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi,
+                                          int prow, const char* kn, const char* vn) {
         static_assert(8 % RPS == 0, "a load instruction stays within one half of the tile");
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int64_t boff = j * RPS < 8 ? lo : hi;
+            const bool fresh = j * RPS + rg == prow;
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
-                kb[slot][j][k] = load16_policy<TU::STREAM>(kbase + boff + lane_off[j][k]);
-                vb[slot][j][k] = load16_policy<TU::STREAM>(vbase + boff + lane_off[j][k]);
+                const uint32_t col = hd * RB + (c + k * R) * 16;
+                kb[slot][j][k] = load16_policy<TU::STREAM>(fresh ? kn + col : kbase + boff + lane_off[j][k]);
+                vb[slot][j][k] = load16_policy<TU::STREAM>(fresh ? vn + col : vbase + boff + lane_off[j][k]);
             }
         }
     }
@@ -379,13 +384,18 @@ struct MfmaAttn {
         for (int t = 0; t < TT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi) {
+    // Tile row `prow` (if 0..15) is read from the rows kn, vn ([NH][D] of the
+    // token being appended) instead of the cache.
+    __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi,
+                                          int prow, const char* kn, const char* vn) {
         static_assert(8 % RPI == 0, "a load instruction stays within one half of the tile");
+        const uint32_t col = lhead * RB + lchunk * 16;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int64_t off = (i * RPI < 8 ? lo : hi) + ld_base + (int64_t)i * RPI * row_stride_;
-            kt[slot][i] = load16_policy<TU::STREAM>(kbase + off);
-            vt[slot][i] = load16_policy<TU::STREAM>(vbase + off);
+            const bool fresh = i * RPI + lrow == prow;
+            kt[slot][i] = load16_policy<TU::STREAM>(fresh ? kn + col : kbase + off);
+            vt[slot][i] = load16_policy<TU::STREAM>(fresh ? vn + col : vbase + off);
         }
     }
 
@@ -619,6 +629,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     const uint32_t row_stride = (uint32_t)Hkv * A::RB;
     const char* kcache = static_cast<const char*>(p.k_cache);
     const char* vcache = static_cast<const char*>(p.v_cache);
+    const bool fused = p.positions != nullptr;
 
     // Cursor over the tile stream: sequence, head group, block, blocks of the sequence.
     struct Cur {
@@ -672,7 +683,20 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
                            row_stride);
         }
         const int64_t hoff = real ? (int64_t)q.kvh * A::NH * A::RB : 0;
-        a.issue(slot, kcache + hoff, vcache + hoff, ta.lo, ta.hi);
+        // With an append in the same call, the tile holding the new token's
+        // position reads that row from k_new / v_new.
+        int prow = -1;
+        const char *kn = kcache, *vn = vcache;
+        if (fused && real) {
+            const int r = table_entry(p.positions, q.s) - q.b * kBlock;
+            if (r >= 0 && r < kBlock) {
+                prow = r;
+                const int64_t roff = ((int64_t)q.s * Hkv + q.kvh * A::NH) * A::RB;
+                kn = static_cast<const char*>(p.k_new) + roff;
+                vn = static_cast<const char*>(p.v_new) + roff;
+            }
+        }
+        a.issue(slot, kcache + hoff, vcache + hoff, ta.lo, ta.hi, prow, kn, vn);
         oks[slot] = ta.ok;
     };
 
@@ -831,6 +855,25 @@ __device__ __forceinline__ void merge_records(const float* ml, const float* acc,
     }
 }
 
+// The append of a fused call, made once every read of the step is done: the
+// new token's K and V rows of KV head kvh go to their slot.  Like the append
+// kernel, a position or table entry out of range skips the sequence.
+template <class E, int D>
+__device__ __forceinline__ void append_head_row(const DecodeParams& p, int s, int kvh, int lane) {
+    constexpr int RB = D * E::kBytes;  // a multiple of 16 bytes, at most 64 x 16
+    const int pos = p.positions[s];
+    if (pos < 0 || (pos >> p.block_shift) >= p.max_blocks) return;
+    const int blk = p.block_tables[(int64_t)s * p.max_blocks + (pos >> p.block_shift)];
+    if (blk < 0 || blk >= p.num_blocks) return;
+    const int64_t slot = ((int64_t)blk << p.block_shift) + (pos & ((1 << p.block_shift) - 1));
+    const int64_t dst = (slot * p.n_kv_heads + kvh) * RB + lane * 16;
+    const int64_t src = ((int64_t)s * p.n_kv_heads + kvh) * RB + lane * 16;
+    if (lane < RB / 16) {
+        store16(static_cast<char*>(p.k_cache_w) + dst, load16(static_cast<const char*>(p.k_new) + src));
+        store16(static_cast<char*>(p.v_cache_w) + dst, load16(static_cast<const char*>(p.v_new) + src));
+    }
+}
+
 // One wave per (sequence, query head): combine the records of pairs that were
 // split between waves, and write zeros for empty sequences.
 template <class E, int D>
@@ -841,6 +884,8 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
     if (pair >= p.num_seqs * p.n_q_heads) return;
     const int s = pair / p.n_q_heads;
     const int h = pair % p.n_q_heads;
+    const int Gq = p.n_q_heads / p.n_kv_heads;
+    if (p.positions != nullptr && h % Gq == 0) append_head_row<E, D>(p, s, h / Gq, lane);
     const int HG = p.n_q_heads / p.n_kv_heads * p.heads_per_wave;  // query heads per record
     const int NG = p.n_kv_heads / p.heads_per_wave;
     const int hg = h / HG;
@@ -920,7 +965,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     auto issue = [&](int slot, int bi, bool real) {
         TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
         if (real) ta = tile_addr(table, bi, ntab, p.block_shift, p.num_blocks, row_stride);
-        a.issue(slot, kbase, vbase, ta.lo, ta.hi);
+        a.issue(slot, kbase, vbase, ta.lo, ta.hi, -1, kbase, vbase);
         oks[slot] = ta.ok;
     };
 

@@ -531,6 +531,70 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
                                      stream);
 }
 
+pkv_status paged_kv_append_attention_decode_ws(const void* k_new, const void* v_new, const int32_t* positions,
+                                               const void* q, void* k_cache, void* v_cache,
+                                               const pkv_layout* layout, const int32_t* block_tables,
+                                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                               int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                                               int32_t part_tokens, void* workspace, size_t ws_bytes,
+                                               void* stream) {
+    pkv_status st = check_decode(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq, context_lens,
+                                 num_seqs, n_q_heads, scale, out);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return ok();
+    if (!k_new || !v_new || !positions) return fail(PKV_EINVAL, "a required pointer is NULL");
+    int32_t P = 0;
+    st = resolve_partition(part_tokens, num_seqs, max_blocks_per_seq, layout, &P);
+    if (st != PKV_OK) return st;
+    if (P > 0) {  // fixed partitions: the two calls
+        st = paged_kv_append(k_new, v_new, k_cache, v_cache, layout, block_tables, max_blocks_per_seq, positions,
+                             num_seqs, stream);
+        if (st != PKV_OK) return st;
+        return paged_attention_decode_ws(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
+                                         context_lens, num_seqs, n_q_heads, scale, out, P, workspace, ws_bytes,
+                                         stream);
+    }
+    const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, 0);
+    st = check_workspace(pl, workspace, ws_bytes);
+    if (st != PKV_OK) return st;
+    pkv::DecodeParams p = make_params(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq, context_lens,
+                                      num_seqs, n_q_heads, scale, out, pl, workspace);
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.positions = positions;
+    p.k_cache_w = k_cache;
+    p.v_cache_w = v_cache;
+    const int group = n_q_heads / layout->n_kv_heads;
+    hipError_t e = pkv::launch_decode_partitions(p, layout->dtype, layout->head_dim, group,
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "partition launch");
+    e = pkv::launch_decode_merge(p, layout->dtype, layout->head_dim, group, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return ok();
+}
+
+pkv_status paged_kv_append_attention_decode(const void* k_new, const void* v_new, const int32_t* positions,
+                                            const void* q, void* k_cache, void* v_cache, const pkv_layout* layout,
+                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                            float scale, void* out, void* stream) {
+    pkv_status st = check_decode(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq, context_lens,
+                                 num_seqs, n_q_heads, scale, out);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return ok();
+    if (!k_new || !v_new || !positions) return fail(PKV_EINVAL, "a required pointer is NULL");
+    int32_t P = 0;
+    st = resolve_partition(0, num_seqs, max_blocks_per_seq, layout, &P);
+    if (st != PKV_OK) return st;
+    const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
+    void* ws = nullptr;
+    st = library_workspace(pl.ws_bytes, &ws);
+    if (st != PKV_OK) return st;
+    return paged_kv_append_attention_decode_ws(k_new, v_new, positions, q, k_cache, v_cache, layout, block_tables,
+                                               max_blocks_per_seq, context_lens, num_seqs, n_q_heads, scale, out, P,
+                                               ws, pl.ws_bytes, stream);
+}
+
 pkv_status pkv_set_partition_tokens(int32_t tokens) {
     if (tokens < 0 || tokens % kTileTokens != 0)
         return fail(PKV_EINVAL, "partition length %d is not 0 or a positive multiple of %d", tokens,

@@ -114,6 +114,15 @@ struct DecodeParams {
     int32_t heads_per_wave;  // adjacent KV heads one wave streams together (see decode_heads_per_wave)
     int32_t block_shift;     // log2 of the cache block size (8, 16, 32 or 64 tokens)
     float scale_log2;  // scale * log2(e): scores are kept in base-2 units
+    // A fused append (flat schedule only; positions == nullptr otherwise): the
+    // decode pass reads each sequence's new row from k_new / v_new ([num_seqs]
+    // [n_kv_heads][head_dim]) at positions[s], and the merge pass writes it to
+    // its slot in k_cache_w / v_cache_w (the same caches).
+    const void* k_new;
+    const void* v_new;
+    const int32_t* positions;
+    void* k_cache_w;
+    void* v_cache_w;
 };
 
 // Each returns hipSuccess or the launch error.  dtype: 0 f32, 1 f16, 2 bf16.

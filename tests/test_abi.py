@@ -95,6 +95,24 @@ def test_decode_ws_checks_workspace(L):
     assert L.paged_attention_decode_ws(*args, ctypes.c_void_p(0x1000), need, None) == _lib.PKV_EINVAL
 
 
+def test_fused_rejects(L):
+    lay = _layout()
+
+    def call(k_new=FAKE, v_new=FAKE, pos=FAKE, S=4, Hq=4, ws=None, nbytes=0):
+        return L.paged_kv_append_attention_decode_ws(k_new, v_new, pos, FAKE, FAKE, FAKE, ctypes.byref(lay), FAKE,
+                                                     3, FAKE, S, Hq, 0.125, FAKE, 0, ws, nbytes, None)
+    assert call(k_new=None) == _lib.PKV_EINVAL
+    assert call(v_new=None) == _lib.PKV_EINVAL
+    assert call(pos=None) == _lib.PKV_EINVAL
+    assert call(Hq=6) == _lib.PKV_EINVAL                  # not a multiple of n_kv_heads
+    assert call(S=0) == _lib.PKV_OK                       # empty batch
+    assert call() == _lib.PKV_EINVAL                      # the flat schedule's workspace is missing
+    assert "workspace" in _lib.last_error()
+    args = [FAKE, FAKE, FAKE, ctypes.byref(lay), FAKE, 3, FAKE, 4, 4, 0.125, FAKE, None]
+    assert L.paged_kv_append_attention_decode(None, FAKE, FAKE, *args) == _lib.PKV_EINVAL
+    assert L.paged_kv_append_attention_decode(FAKE, FAKE, None, *args) == _lib.PKV_EINVAL
+
+
 def test_partition_setting(L):
     lay = _layout()
     assert L.pkv_set_partition_tokens(17) == _lib.PKV_EINVAL
