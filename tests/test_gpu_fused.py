@@ -125,3 +125,25 @@ def test_fused_llama2_7b_full():
 def test_fused_gqa_8b_sampled():
     w = W.gqa_8b()
     check(poisoned(w), oracle_ids=[0, 101, 255])
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_fused_random_shapes(seed):
+    """Seeded random batches: sizes, lengths (empty and one-token sequences
+    among them), heads, dtype, head_dim and block size drawn per case, so that
+    waves start and end segments at every kind of boundary."""
+    rng = np.random.default_rng(6000 + seed)
+    dtype = ["f32", "f16", "bf16"][seed % 3]
+    head_dim = [64, 128][(seed // 3) % 2]
+    group = [1, 2, 4, 8][seed % 4] if dtype != "f32" else [1, 2][seed % 2]
+    hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    B = int(rng.choice([8, 16, 32, 64]))
+    S = int(rng.integers(1, 120))
+    lens = rng.integers(1, 1200, size=S)
+    lens[rng.random(S) < 0.1] = 1
+    w = W.small(S, lens, hkv * group, hkv, head_dim, dtype, seed=6100 + seed, block_size=B)
+    lens0 = np.array(w.context_lens)
+    lens0[rng.random(S) < 0.05] = 0  # empty sequences: zeros out, the append still lands
+    w.context_lens = lens0.astype(np.int32)
+    ids = sorted(set(int(i) for i in rng.integers(0, S, size=min(S, 6))))
+    check(poisoned(w), oracle_ids=ids)
