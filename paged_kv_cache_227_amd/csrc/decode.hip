@@ -417,12 +417,17 @@ struct MfmaAttn {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        // two accumulators, so the score products form two chains half as long
+        f32x4_t sacc0 = {0.f, 0.f, 0.f, 0.f}, sacc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                sacc = OPS::qk(lds_load16(kl, lds_pos(j, h, 4 * kk + g)), qb[h][kk], sacc);
+            for (int kk = 0; kk < KK; ++kk) {
+                const Vec16 ka = lds_load16(kl, lds_pos(j, h, 4 * kk + g));
+                if ((h * KK + kk) % 2 == 0) sacc0 = OPS::qk(ka, qb[h][kk], sacc0);
+                else sacc1 = OPS::qk(ka, qb[h][kk], sacc1);
+            }
+        const f32x4_t sacc = sacc0 + sacc1;
         float sc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
