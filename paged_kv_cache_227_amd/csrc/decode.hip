@@ -245,7 +245,7 @@ struct WaveAttn {
         float acc[G][EPL];
         float m[G], l[G];
     };
-    static constexpr bool kHold = G * (EPL + 2) <= 40;
+    static constexpr bool kHold = G * (EPL + 2) <= 18;  // one query head per KV head: 10-18 registers
 
     __device__ __forceinline__ void take(Result& r) const {
 #pragma unroll
@@ -1117,7 +1117,9 @@ struct DefaultTune {
     static constexpr int kR = kCH < 16 ? kCH : 16;
     static constexpr int kNH = E::kBytes == 2 && !kMfma ? 2 : 1;
     using mfma_flat = typename std::conditional<(G >= 8), Tune<1, 8, 1, true, true, 1>, Tune<8, 8, 2, true, true, 1>>::type;
-    using valu = typename std::conditional<kNH == 2, Tune<8, kR, 1, true, false, 2>, Tune<4, 8, 1, true, false, 1>>::type;
+    // fp32 with G >= 4 spreads a head row over more lanes: fewer accumulators per lane
+    static constexpr int kRf = E::kBytes == 4 && G >= 4 ? kR : 8;
+    using valu = typename std::conditional<kNH == 2, Tune<8, kR, 1, true, false, 2>, Tune<4, kRf, 1, true, false, 1>>::type;
     using type = typename std::conditional<kMfma, mfma_flat, valu>::type;
     using parts = typename std::conditional<kMfma, Tune<1, 8, 2, true, true, 1>, valu>::type;
     using NH1 = Tune<4, 8, 1, true, kMfma, 1>;
