@@ -1122,7 +1122,7 @@ struct DefaultTune {
     using valu = typename std::conditional<kNH == 2, Tune<8, kR, 1, true, false, 2>, Tune<4, kRf, 1, true, false, 1>>::type;
     using type = typename std::conditional<kMfma, mfma_flat, valu>::type;
     using parts = typename std::conditional<kMfma, Tune<1, 8, 2, true, true, 1>, valu>::type;
-    using NH1 = Tune<4, 8, 1, true, kMfma, 1>;
+    using NH1 = Tune<4, kMfma ? 8 : kRf, 1, true, kMfma, 1>;
 };
 
 template <class E, int D, int G>
