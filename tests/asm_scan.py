@@ -13,6 +13,7 @@ between and whether the path took a branch.
 
 It reads only assembly built here from this repository's sources.
 """
+import functools
 import os
 import re
 import subprocess
@@ -33,7 +34,13 @@ def _vregs(op):
 
 
 def device_asm(src, flags, hipcc="/opt/rocm/bin/hipcc"):
-    """The device assembly of one source file, compiled with the library's flags."""
+    """The device assembly of one source file, compiled with the library's flags
+    (compiled once per test session and source)."""
+    return _device_asm(src, tuple(flags), hipcc, os.path.getmtime(src))
+
+
+@functools.lru_cache(maxsize=None)
+def _device_asm(src, flags, hipcc, _mtime):
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
         cmd = [hipcc] + [f for f in flags if f != "-fPIC"] + ["--cuda-device-only", "-S", src, "-o", out]
