@@ -1,193 +1,222 @@
-"""Host-side block manager: the free list, reference counts and per-sequence
-block tables that the GPU path consumes.
+"""Host-side bookkeeping for the paged cache: which physical blocks are idle,
+how many block tables point at each block, and each sequence's table.  The GPU
+path only ever sees the resulting tables; this module never touches device
+memory.
 
-Semantics follow the two allocators on the pages:
+The rules it keeps are the ones the pages state:
 
-* "How a serving engine actually works" (paperfordummies.in), section
-  "The code": a FIFO free list (allocate takes the front, a freed block goes to
-  the back), a refcount per block, ``share`` as a refcount bump, the guard that
-  only the last owner really frees, copy-on-write, and ``OutOfBlocks`` when the
-  pool is empty.  The ``Sequence`` class there (a table plus a length that grows
-  a block when the current one is full, ``fork``, ``release``) is mirrored here.
-* "Paged Attention and the Block Manager" (snowch.github.io ch08), section
-  "The build": ``ValueError`` for a non-positive pool or block size,
-  ``blocks_needed`` and ``allocate(n)`` returning a list, ``n_free``.
-* "Paged-KV + Continuous Batching From Scratch" (henryhe.ai), section 2: the
-  allocator hard-fails on a double free.
+* "How a serving engine actually works" (paperfordummies.in), "The code":
+  blocks are reused first-freed-first-reused; sharing a block only counts one
+  more holder; a block goes back to the pool when its last holder lets go;
+  writing into a block that others also hold first moves the writer to a
+  private block; an empty pool is an error (``OutOfBlocks``).
+* "Paged Attention and the Block Manager" (snowch.github.io ch08), "The build":
+  a pool of no blocks, or of empty blocks, is a ``ValueError``; a request for
+  n blocks is served whole or not at all.
+* "Paged-KV + Continuous Batching From Scratch" (henryhe.ai), section 2: giving
+  back a block that nobody holds is a hard failure (``DoubleFree``).
 
-Unlike the pages' counter simulation, ``copy_on_write`` here reports the block
-whose rows the caller must copy (the simulation allocates without copying any
-data); copying the rows is the caller's job.  ``Sequence`` queues each such copy
-as (source block, private block, rows already written); ``take_copies`` hands
-the queue to the caller, who runs them (``paged_kv_copy_blocks``) before the
-append that triggered them.
+Design.  The pool is two structures: ``_holders``, one count per physical
+block (zero means idle), and ``_idle``, a deque of the idle block ids in the
+order they became idle.  Every operation is a few O(1) steps on them.  A
+sequence is a list of block ids plus its token count; the slot of its token i
+is ``table[i // B] * B + i % B``.
 
-This module does bookkeeping only; it never touches device memory.
+Where the pages' simulation only counts a copy-on-write, here the writer's
+``Sequence`` also queues the data move it implies (source block, private
+block, rows already written) for the caller to run on the device
+(``paged_kv_copy_blocks``) before the append that caused it.
 """
 from __future__ import annotations
 
+from collections import deque
 from typing import Iterable, List, Optional, Tuple
 
 
 class OutOfBlocks(RuntimeError):
-    """No free physical block is left in the pool."""
+    """The pool has fewer idle blocks than a request needs."""
 
 
 class DoubleFree(RuntimeError):
-    """A block was released more times than it was referenced."""
+    """An operation named a block that no table holds."""
 
 
 class BlockAllocator:
-    """A pool of ``n_blocks`` fixed-size KV blocks with reference counts."""
+    """``n_blocks`` physical blocks of ``block_size`` token slots each.
+
+    ``free_order`` fixes the order in which the idle blocks are first handed
+    out (a permutation of the block ids); by default it is 0, 1, 2, ...
+    ``copies`` counts the private blocks handed out by ``copy_on_write``.
+    """
 
     def __init__(self, n_blocks: int, block_size: int,
                  free_order: Optional[Iterable[int]] = None) -> None:
-        if n_blocks < 1 or block_size < 1:
-            raise ValueError("n_blocks and block_size must both be positive")
-        self.n_blocks = int(n_blocks)
-        self.block_size = int(block_size)
-        if free_order is None:
-            self._free: List[int] = list(range(self.n_blocks))
-        else:
-            self._free = [int(b) for b in free_order]
-            if sorted(self._free) != list(range(self.n_blocks)):
-                raise ValueError("free_order must be a permutation of range(n_blocks)")
-        self._ref: dict = {}
-        self.copies = 0  # copy-on-write events
+        n_blocks, block_size = int(n_blocks), int(block_size)
+        if n_blocks <= 0 or block_size <= 0:
+            raise ValueError("a pool needs at least one block of at least one slot "
+                             "(got %d blocks of %d)" % (n_blocks, block_size))
+        ids = list(range(n_blocks)) if free_order is None else [int(b) for b in free_order]
+        if len(ids) != n_blocks or set(ids) != set(range(n_blocks)):
+            raise ValueError("free_order must list every block id 0..%d exactly once" % (n_blocks - 1))
+        self.n_blocks = n_blocks
+        self.block_size = block_size
+        self._holders = [0] * n_blocks
+        self._idle = deque(ids)
+        self.copies = 0
 
-    # -- queries ---------------------------------------------------------
+    # ---- state ------------------------------------------------------------
     @property
     def n_free(self) -> int:
-        return len(self._free)
+        return len(self._idle)
 
     @property
     def free_list(self) -> List[int]:
-        return list(self._free)
+        """Idle block ids, next to be handed out first."""
+        return list(self._idle)
 
     def refcount(self, b: int) -> int:
-        return self._ref.get(b, 0)
+        return self._holders[b] if 0 <= b < self.n_blocks else 0
 
     def blocks_needed(self, n_tokens: int) -> int:
-        """Blocks that hold ``n_tokens`` tokens: the ceiling of n_tokens / block_size."""
-        return -(-int(n_tokens) // self.block_size)
+        """Blocks a table needs for ``n_tokens`` tokens (n_tokens / B rounded up)."""
+        n_tokens = int(n_tokens)
+        return (n_tokens + self.block_size - 1) // self.block_size
 
-    # -- allocation ------------------------------------------------------
-    def allocate_one(self) -> int:
-        if not self._free:
-            raise OutOfBlocks("no free physical blocks")
-        b = self._free.pop(0)
-        self._ref[b] = 1
-        return b
+    def is_whole(self) -> bool:
+        """Every block idle and listed once: nothing leaked, nothing listed twice."""
+        return not any(self._holders) and sorted(self._idle) == list(range(self.n_blocks))
 
+    def _check_held(self, b: int, op: str) -> None:
+        if not (0 <= b < self.n_blocks) or self._holders[b] == 0:
+            raise DoubleFree("%s: block %d has no holder" % (op, b))
+
+    # ---- operations -------------------------------------------------------
     def allocate(self, n: int) -> List[int]:
-        """``n`` blocks, all or none."""
+        """Hand out the ``n`` longest-idle blocks, each with one holder; if fewer
+        than ``n`` are idle, raise ``OutOfBlocks`` and change nothing."""
+        n = int(n)
         if n < 0:
-            raise ValueError("cannot allocate a negative number of blocks")
-        if n > len(self._free):
-            raise OutOfBlocks("no free physical blocks")
-        return [self.allocate_one() for _ in range(n)]
+            raise ValueError("block count %d is negative" % n)
+        if n > len(self._idle):
+            raise OutOfBlocks("pool exhausted: %d block(s) wanted, %d idle" % (n, len(self._idle)))
+        out = []
+        for _ in range(n):
+            b = self._idle.popleft()
+            self._holders[b] = 1
+            out.append(b)
+        return out
+
+    def allocate_one(self) -> int:
+        return self.allocate(1)[0]
 
     def share(self, b: int) -> int:
-        """Another sequence now points at block ``b``; nothing is copied."""
-        if b not in self._ref:
-            raise DoubleFree("share of block %d, which is not allocated" % b)
-        self._ref[b] += 1
+        """Count one more holder of ``b`` (a forked table pointing at it)."""
+        self._check_held(b, "share")
+        self._holders[b] += 1
         return b
 
     def free_block(self, b: int) -> bool:
-        """Drop one reference; return True when the block went back to the pool."""
-        if b not in self._ref:
-            raise DoubleFree("block %d released more often than referenced" % b)
-        self._ref[b] -= 1
-        if self._ref[b] == 0:
-            del self._ref[b]
-            self._free.append(b)
-            return True
-        return False
+        """One holder lets go of ``b``; True if that made it idle again."""
+        self._check_held(b, "release")
+        left = self._holders[b] - 1
+        self._holders[b] = left
+        if left:
+            return False
+        self._idle.append(b)
+        return True
 
     def copy_on_write(self, b: int) -> int:
-        """Block to write into instead of ``b``: ``b`` itself if this is its sole
-        owner, otherwise a fresh private block (the caller copies ``b``'s rows)."""
-        if b not in self._ref:
-            raise DoubleFree("write into block %d, which is not allocated" % b)
-        if self._ref[b] == 1:
+        """The block a holder of ``b`` may write into: ``b`` when it is the only
+        holder, else a new private block, the writer giving up its hold on ``b``.
+        Moving the rows already written into the private block is the caller's
+        job."""
+        self._check_held(b, "write")
+        if self._holders[b] == 1:
             return b
-        new = self.allocate_one()
-        self._ref[b] -= 1
+        private = self.allocate_one()  # may raise before b's count changes
+        self.free_block(b)             # others still hold b: it stays live
         self.copies += 1
-        return new
-
-    def is_whole(self) -> bool:
-        """True when every block is free again (no leak)."""
-        return not self._ref and sorted(self._free) == list(range(self.n_blocks))
+        return private
 
 
 class Sequence:
-    """A block table plus a length."""
+    """One request's block table and the number of tokens it has written.
+
+    ``pending_copies`` queues (source, private, rows) moves that copy-on-write
+    made necessary; ``last_cow`` is the latest (source, private) pair.
+    """
 
     def __init__(self, name: str, alloc: BlockAllocator) -> None:
         self.name = name
         self.alloc = alloc
         self.table: List[int] = []
         self.n_tokens = 0
-        self.last_cow: Optional[tuple] = None  # (src, dst) of the latest private copy
-        self.pending_copies: List[Tuple[int, int, int]] = []  # (src, dst, rows) not yet run
+        self.last_cow: Optional[Tuple[int, int]] = None
+        self.pending_copies: List[Tuple[int, int, int]] = []
+
+    def _own_next_slot(self) -> None:
+        """Make the slot of token ``n_tokens`` exist and be this table's alone."""
+        written = self.n_tokens % self.alloc.block_size
+        if written == 0:
+            # every block in the table is full (or there is none): open one
+            self.table.append(self.alloc.allocate_one())
+            return
+        shared = self.table[-1]
+        private = self.alloc.copy_on_write(shared)
+        if private != shared:
+            self.table[-1] = private
+            self.last_cow = (shared, private)
+            self.pending_copies.append((shared, private, written))
 
     def append_tokens(self, n: int) -> None:
-        """Grow by ``n`` tokens: a new block when the current one is full, a
-        private copy when writing inside a block someone else also holds."""
-        for _ in range(n):
-            offset = self.n_tokens % self.alloc.block_size
-            if offset == 0:
-                self.table.append(self.alloc.allocate_one())
-            else:
-                last = len(self.table) - 1
-                old = self.table[last]
-                new = self.alloc.copy_on_write(old)
-                if new != old:
-                    self.last_cow = (old, new)
-                    # rows 0 .. offset-1 hold this sequence's tokens already
-                    self.pending_copies.append((old, new, offset))
-                self.table[last] = new
+        """Reserve slots for ``n`` more tokens, one at a time, so an
+        ``OutOfBlocks`` leaves the tokens reserved so far in place."""
+        for _ in range(int(n)):
+            self._own_next_slot()
             self.n_tokens += 1
 
     def take_copies(self) -> List[Tuple[int, int, int]]:
-        """The queued (src, dst, rows) block copies, oldest first; clears the queue."""
-        out, self.pending_copies = self.pending_copies, []
-        return out
+        """Hand over the queued block moves, oldest first, and empty the queue."""
+        queued = self.pending_copies
+        self.pending_copies = []
+        return queued
 
     def fork(self, name: str) -> "Sequence":
-        """Same tokens, shared blocks (parallel sampling, shared prompts)."""
-        child = Sequence(name, self.alloc)
-        child.table = [self.alloc.share(b) for b in self.table]
-        child.n_tokens = self.n_tokens
-        return child
+        """A new sequence with the same tokens, holding the same blocks."""
+        twin = Sequence(name, self.alloc)
+        for b in self.table:
+            self.alloc.share(b)
+        twin.table = list(self.table)
+        twin.n_tokens = self.n_tokens
+        return twin
 
-    def preempt_swap(self) -> List[int]:
-        """Preemption by swapping, all or nothing: the blocks whose contents the
-        caller copies to host memory (table order), after which every one is
-        released.  The tokens stay (``n_tokens`` is kept); only the cache leaves."""
-        blocks = list(self.table)
-        for b in blocks:
-            self.alloc.free_block(b)
+    def _let_go(self) -> List[int]:
+        dropped = self.table
         self.table = []
-        return blocks
-
-    def resume_swapped(self, n_blocks: int) -> List[int]:
-        """Fresh blocks for a swapped-out sequence, all or none; host slot i goes
-        into the i-th returned block.  Blocks it once shared come back private."""
-        if n_blocks != self.alloc.blocks_needed(self.n_tokens):
-            raise ValueError("a swapped-out sequence of %d tokens needs %d blocks, not %d"
-                             % (self.n_tokens, self.alloc.blocks_needed(self.n_tokens), n_blocks))
-        self.table = self.alloc.allocate(n_blocks)
-        return list(self.table)
+        for b in dropped:
+            self.alloc.free_block(b)
+        return dropped
 
     def release(self) -> None:
-        for b in self.table:
-            self.alloc.free_block(b)
-        self.table = []
+        """Finished: give every block back and forget the tokens."""
+        self._let_go()
         self.n_tokens = 0
 
+    def preempt_swap(self) -> List[int]:
+        """Preemption by swapping: returns the table (in order) whose blocks the
+        caller copies to host memory, then gives every block back.  The token
+        count stays, so the sequence can resume where it stopped."""
+        return list(self._let_go())
+
+    def resume_swapped(self, n_blocks: int) -> List[int]:
+        """New private blocks for a swapped-out sequence, all or none; host
+        slot i is copied into the i-th one returned."""
+        want = self.alloc.blocks_needed(self.n_tokens)
+        if int(n_blocks) != want:
+            raise ValueError("%d tokens fill %d blocks; %d were asked for" % (self.n_tokens, want, n_blocks))
+        self.table = self.alloc.allocate(want)
+        return list(self.table)
+
     def internal_waste(self) -> int:
-        """Slots held but not written: at most block_size - 1."""
+        """Reserved but unwritten slots in the table (below block_size)."""
         return len(self.table) * self.alloc.block_size - self.n_tokens
