@@ -11,6 +11,29 @@ from pkv_testutil import poison_unused
 # Tolerances on max |gpu - oracle| over every output element (values as float).
 TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
 
+# A second bound, scaled to each output row: for every (sequence, query head),
+# max_d |gpu - oracle| <= ROW_REL * max_d |oracle|.  The absolute bound above
+# is the acceptance bar, but where the data are small (N(0,1)/sqrt(128), whose
+# outputs are about 0.33/sqrt(L) at most) it would pass an all-zero row; this
+# one fails a zeroed row, a dropped block or a swapped head.  Rounding a row to
+# fp16 / bf16 costs at most 2^-11 / 2^-8 of its largest element, so the
+# legitimate error stays well under 1e-2 of it.
+ROW_REL = 1e-2
+
+
+def row_check(g, ref_out):
+    """(max abs error, worst row ratio) of a [S][H][D] output against the
+    oracle's; the ratio is max|g - ref| / (ROW_REL * max|ref|) per row, so
+    a value above 1 breaks the row bound.  An all-zero oracle row must be
+    matched exactly (ratio inf otherwise, 0 if equal)."""
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(ref_out, dtype=np.float64)
+    diff = np.abs(g - r).max(axis=-1)
+    scale = ROW_REL * np.abs(r).max(axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(scale > 0, diff / np.where(scale > 0, scale, 1.0), np.where(diff > 0, np.inf, 0.0))
+    return float(diff.max()), float(ratio.max())
+
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -79,11 +102,16 @@ def oracle_step(w, seq_ids=None, part_tokens=0):
 
 
 def max_err(gpu_out, ref_out, seq_ids=None):
+    """max |gpu - oracle| over the chosen sequences; asserts that the output is
+    finite and that every row meets the row-scaled bound (ROW_REL)."""
     g = to_np_f64(gpu_out)
     if seq_ids is not None:
         g, ref_out = g[seq_ids], ref_out[seq_ids]
     assert np.all(np.isfinite(g)), "GPU output holds NaN/inf"
-    return float(np.max(np.abs(g - ref_out)))
+    err, ratio = row_check(g, ref_out)
+    say("  row-scaled error: worst row at %.3g of its bound" % ratio)
+    assert ratio <= 1.0, "a row differs from the oracle by more than %g of its largest value" % ROW_REL
+    return err
 
 
 def dev_storage(a, dtype, device="cuda"):

@@ -151,6 +151,20 @@ def test_long_context_sampled():
     _sampled_check(w, 1, part_tokens=w.part_tokens)
 
 
+def test_long_context_default_schedule_sampled():
+    """The long-context configuration through paged_attention_decode with the
+    library's own choice of schedule (the flat one at this size: a 131k-token
+    sequence is split between many waves and merged): the longest sequence,
+    the shortest and one more, all 64 query heads, against the oracle."""
+    import paged_kv_cache_227_amd as P
+    from paged_kv_cache_227_amd._lib import Layout
+    w = W.long_context()
+    L = Layout(w.num_blocks, w.block_size, w.n_kv_heads, w.head_dim, w.dtype_code)
+    assert P.partition_tokens_for(w.num_seqs, w.n_q_heads, w.block_tables.shape[1], L) == 0, \
+        "the default schedule for this batch is no longer the flat one"
+    _sampled_check(w, 1, part_tokens=0)
+
+
 # ---- the flat schedule's edge cases ---------------------------------------------------------
 
 def test_flat_many_short_sequences():
