@@ -55,9 +55,9 @@
  *     pkv_validate() reports them.
  *   - Supported by the GPU path: dtype f32 / f16 / bf16, head_dim 64 or 128,
  *     n_q_heads / n_kv_heads in {1, 2, 4, 8}; block_size 8, 16, 32 or 64 for
- *     decode (the block size is "the one tuning knob" of "How a serving engine
- *     actually works", section "The one formula"), 16 for prefill, any for the
- *     appends and block copies.
+ *     decode and prefill (the block size is "the one tuning knob" of "How a
+ *     serving engine actually works", section "The one formula"), any for the
+ *     appends, block copies and swaps.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -82,7 +82,7 @@ typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
 /* Shape of one layer's cache pair (host struct, read during the call only). */
 typedef struct {
     int32_t num_blocks; /* physical blocks in the pool */
-    int32_t block_size; /* tokens per block (B); 16 on the GPU path */
+    int32_t block_size; /* tokens per block (B): 8, 16, 32 or 64 for attention, any for copies */
     int32_t n_kv_heads;
     int32_t head_dim;
     int32_t dtype; /* pkv_dtype */
@@ -259,7 +259,11 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
 /*
  * Bytes of split-K workspace paged_attention_decode_ws needs for these sizes
  * with partition length part_tokens (0 = the library's choice).  Returns 0 for
- * invalid sizes.
+ * invalid sizes.  The size is a function of the table width, not of the
+ * lengths in a batch: fixed partitions need one record per partition of the
+ * longest context a table row can describe (max_blocks_per_seq * block_size
+ * tokens), and the flat schedule's records depend on the batch and grid sizes
+ * only.  So one workspace sized here serves every batch of these dimensions.
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t n_q_heads,
                                       int32_t max_blocks_per_seq, const pkv_layout* layout,
@@ -349,11 +353,12 @@ pkv_status paged_kv_append_attention_decode(const void* k_new, const void* v_new
 
 /*
  * Process-wide partition length used when a call passes 0 (and by
- * paged_attention_decode): a positive multiple of 16 (and, at call time, of
- * the block size), or 0 to
- * restore the library's choice (the flat schedule; batches of more than 8000
- * sequences, or with more than 2^30 tiles, use 512-token partitions).
- * Returns PKV_EINVAL otherwise.
+ * paged_attention_decode): a positive multiple of 16, or 0 to restore the
+ * library's choice (the flat schedule; batches of more than 8000 sequences,
+ * or with more than 2^30 tiles, use 512-token partitions).  Returns
+ * PKV_EINVAL otherwise.  A call whose block size is larger than this length,
+ * or does not divide it, uses the next multiple of the block size (a length
+ * of 16 with 64-token blocks partitions by 64).
  */
 pkv_status pkv_set_partition_tokens(int32_t tokens);
 

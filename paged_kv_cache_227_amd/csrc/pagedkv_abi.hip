@@ -87,8 +87,13 @@ bool flat_fits(int32_t num_seqs, int32_t max_blocks, const pkv_layout* L) {
 pkv_status resolve_partition(int32_t requested, int32_t num_seqs, int32_t max_blocks, const pkv_layout* L,
                              int32_t* out) {
     int32_t P = requested;
-    if (P == 0) P = g_part_tokens.load();
     const int32_t unit = std::max<int32_t>(L->block_size, kTileTokens);
+    if (P == 0) {
+        // the process-wide setting is a multiple of 16; it is rounded up to
+        // whole blocks of this layout
+        P = g_part_tokens.load();
+        P = (P + unit - 1) / unit * unit;
+    }
     if (P < 0 || P % unit != 0)
         return fail(PKV_EINVAL, "partition length %d is not a positive multiple of %d (the block size and 16)", P,
                     unit);
@@ -113,10 +118,12 @@ Plan make_plan(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks, const pk
     Plan pl{};
     pl.part_tokens = P;
     if (P == 0) {
-        // records of NH * G query heads, (num_seqs * Hkv / NH + waves) of them: at
-        // most (num_seqs * Hkv + waves * kMaxHeadsPerWave) * G head rows
-        const size_t G = (size_t)n_q_heads / L->n_kv_heads;
-        const size_t recs = (size_t)num_seqs * L->n_kv_heads + (size_t)pkv::kMaxFlatWorkers * pkv::kMaxHeadsPerWave;
+        // records of NH * G query heads (NH KV heads per wave), indexed by
+        // (sequence, head group) + wave: fewer than num_seqs * Hkv / NH + waves
+        // of them, so (num_seqs * Hkv + waves * NH) * G head rows at most
+        const int G = n_q_heads / L->n_kv_heads;
+        const size_t NH = (size_t)pkv::decode_heads_per_wave(L->dtype, L->head_dim, G, L->n_kv_heads);
+        const size_t recs = (size_t)num_seqs * L->n_kv_heads + (size_t)pkv::kMaxFlatWorkers * NH;
         pl.n_parts_max = 1;
         pl.hdr_bytes = round_up((size_t)(num_seqs + 3) * sizeof(int32_t));
         pl.acc_bytes = round_up(recs * G * L->head_dim * sizeof(float));

@@ -123,6 +123,19 @@ def test_partition_setting(L):
     assert L.pkv_partition_tokens_for(4, 4, 100, ctypes.byref(lay)) % 16 == 0
 
 
+@pytest.mark.parametrize("setting,B,want", [(16, 64, 64), (48, 32, 64), (48, 16, 48), (32, 8, 32), (128, 64, 128)])
+def test_partition_setting_rounds_to_blocks(L, setting, B, want):
+    """The process-wide length is a multiple of 16; a layout with larger blocks
+    partitions by the next multiple of its block size instead of failing."""
+    lay = _layout(block_size=B)
+    assert L.pkv_set_partition_tokens(setting) == _lib.PKV_OK
+    try:
+        assert L.pkv_partition_tokens_for(4, 4, 100, ctypes.byref(lay)) == want
+        assert L.paged_attention_workspace_size(4, 4, 100, ctypes.byref(lay), 0) > 0
+    finally:
+        assert L.pkv_set_partition_tokens(0) == _lib.PKV_OK
+
+
 def test_validate(L):
     lay = _layout(num_blocks=8, block_size=4)
     bt = np.array([[5, 2, 9, -1], [0, 1, 3, -1]], np.int32)
