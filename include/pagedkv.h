@@ -257,6 +257,28 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
                                   void* stream);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory during the call: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, schedule and output bits as paged_attention_decode; the split-K
+ * workspace is a fixed array of PKV_NOALLOC_SCRATCH_BYTES in the library's
+ * device code, one per GPU, held from the library's first use on that GPU
+ * until the process ends.  The call makes no hipMalloc / hipFree.
+ *
+ * A batch whose workspace (paged_attention_workspace_size(..., 0)) exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES is rejected with PKV_EINVAL.  Every call on one GPU
+ * uses that GPU's one array: calls that may overlap on one GPU (different
+ * streams, or other threads) race and must be ordered by the caller.  The
+ * array keeps the last call's contents; nothing in it needs clearing.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pkv_status paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const pkv_layout* layout, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t n_q_heads, float scale, void* out,
+                                          void* stream);
+
+/*
  * Bytes of split-K workspace paged_attention_decode_ws needs for these sizes
  * with partition length part_tokens (0 = the library's choice).  Returns 0 for
  * invalid sizes.  The size is a function of the table width, not of the

@@ -4,7 +4,8 @@ The compute path is the HIP library libpagedkv.so (C ABI in include/pagedkv.h);
 this package binds it (``_lib``), and holds the host block manager
 (``blocks``) and the seeded input generator (``workloads``).
 """
-from ._lib import (PagedKVCache, alloc_workspace, last_error, layout_of, paged_attention_decode,
+from ._lib import (NOALLOC_SCRATCH_BYTES, PagedKVCache, alloc_workspace, last_error, layout_of,
+                   paged_attention_decode, paged_attention_decode_noalloc,
                    paged_attention_merge, paged_attention_partitions, paged_kv_append,
                    paged_kv_append_attention_decode,
                    paged_kv_copy_blocks, validate_copies, paged_kv_append_tokens,
@@ -12,7 +13,8 @@ from ._lib import (PagedKVCache, alloc_workspace, last_error, layout_of, paged_a
                    partition_tokens_for, probe_copy, probe_read, set_partition_tokens, validate,
                    version, workspace_size)
 
-__all__ = ["PagedKVCache", "alloc_workspace", "last_error", "layout_of", "paged_attention_decode",
+__all__ = ["NOALLOC_SCRATCH_BYTES", "PagedKVCache", "alloc_workspace", "last_error", "layout_of",
+           "paged_attention_decode", "paged_attention_decode_noalloc",
            "paged_attention_merge", "paged_attention_partitions", "paged_kv_append",
            "paged_kv_append_attention_decode", "paged_kv_copy_blocks",
            "validate_copies", "paged_kv_append_tokens", "paged_attention_prefill", "validate_prefill",

@@ -21,6 +21,8 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_EHIP, PKV_EOOB = 0, 1, 2, 3, 4
+# PKV_NOALLOC_SCRATCH_BYTES of include/pagedkv.h: the no-allocation decode's workspace
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 
 
@@ -36,6 +38,7 @@ _LP = ctypes.POINTER(Layout)
 SIGNATURES = {
     "paged_kv_append": (ctypes.c_int, [_P, _P, _P, _P, _LP, _P, _I32, _P, _I32, _P]),
     "paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _I32, _I32, _F32, _P, _P]),
+    "paged_attention_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _I32, _I32, _F32, _P, _P]),
     "paged_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _LP, _I32]),
     "paged_attention_decode_ws": (ctypes.c_int, [_P, _P, _P, _LP, _P, _I32, _P, _I32, _I32, _F32, _P,
                                                  _I32, _P, _SZ, _P]),
@@ -317,6 +320,19 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         _i32(block_tables, "block_tables"), block_tables.shape[1], _i32(context_lens, "context_lens"),
         S, Hq, float(scale), _dev(out, "out"), part_tokens, _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), st), "paged_attention_decode_ws")
+
+
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                   stream=None) -> None:
+    """paged_attention_decode whose split-K workspace is the library's fixed
+    per-device array (NOALLOC_SCRATCH_BYTES): the call allocates nothing.
+    Batches needing a larger workspace raise ValueError; calls that may overlap
+    on one GPU must be ordered by the caller."""
+    L, S, Hq = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out)
+    _check(lib().paged_attention_decode_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(L),
+        _i32(block_tables, "block_tables"), block_tables.shape[1], _i32(context_lens, "context_lens"),
+        S, Hq, float(scale), _dev(out, "out"), _stream(stream, q.device)), "paged_attention_decode_noalloc")
 
 
 def paged_kv_append_attention_decode(k_new, v_new, positions, q, k_cache, v_cache, block_tables, context_lens,

@@ -249,6 +249,34 @@ pkv_status library_workspace(size_t need, void** out) {
     return PKV_OK;
 }
 
+// Split-K workspace for callers that cannot allocate (paged_attention_decode_noalloc):
+// one fixed array per device, created with the code object and held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the host
+// the name stands for a host-side shadow, not the device array): it passes the
+// device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::vector<void*> g_scratch_ptr;  // per device; nullptr until looked up
+
+pkv_status device_scratch(void** out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -536,6 +564,32 @@ pkv_status paged_attention_decode(const void* q, const void* k_cache, const void
     return paged_attention_decode_ws(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
                                      context_lens, num_seqs, n_q_heads, scale, out, P, ws, pl.ws_bytes,
                                      stream);
+}
+
+pkv_status paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const pkv_layout* layout, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t n_q_heads, float scale, void* out, void* stream) {
+    pkv_status st = check_decode(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq,
+                                 context_lens, num_seqs, n_q_heads, scale, out);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return ok();
+    int32_t P = 0;
+    st = resolve_partition(0, num_seqs, max_blocks_per_seq, layout, &P);
+    if (st != PKV_OK) return st;
+    const Plan pl = make_plan(num_seqs, n_q_heads, max_blocks_per_seq, layout, P);
+    if (pl.ws_bytes > kScratchBytes)
+        return fail(PKV_EINVAL,
+                    "this batch needs %zu bytes of split-K workspace; the no-allocation call holds %zu "
+                    "(use paged_attention_decode_ws with a workspace of that size)",
+                    pl.ws_bytes, kScratchBytes);
+    void* ws = nullptr;
+    st = device_scratch(&ws);
+    if (st != PKV_OK) return st;
+    // Nothing in the workspace needs to start at zero: the partition pass writes
+    // the schedule header and every record before the merge pass reads them.
+    return paged_attention_decode_ws(q, k_cache, v_cache, layout, block_tables, max_blocks_per_seq, context_lens,
+                                     num_seqs, n_q_heads, scale, out, P, ws, kScratchBytes, stream);
 }
 
 pkv_status paged_kv_append_attention_decode_ws(const void* k_new, const void* v_new, const int32_t* positions,
