@@ -17,10 +17,13 @@ Printed (one JSON line): KV-read GB/s over the whole step (value), tokens/s,
 the partition kernel's roofline (algorithmic KV bytes per launch / its mean
 duration from HIP events, against the 8 TB/s HBM peak), the oracle on the host
 cores as a CPU baseline, and context figures (merge and append times, a
-streaming-read probe, shuffled vs in-order block tables).
+streaming-read probe, shuffled vs in-order block tables).  The default run
+also measures the other decode configurations (GQA-8B, the copied and the
+shared prefix, long context at 512-token partitions and under the library's
+own schedule), each kernel after a cache flush, in a "configs" object.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
-                    [--no-cpu-baseline] [--no-extras]
+                    [--no-cpu-baseline] [--no-extras] [--side-iters N]
     python bench.py --summarize-pmc DIR     # condense rocprofv3 --pmc output
 """
 import argparse
@@ -74,6 +77,16 @@ def load_traffic(config, n_bytes, sources=None):
 def make_workload(name):
     from paged_kv_cache_227_amd import workloads as W
     return W.CONFIGS[name]()
+
+
+def with_schedule(w, schedule):
+    """The workload as given ("workload": its own partition length, if it fixes
+    one), or under the library's default schedule ("default"), then named
+    <workload>_default_schedule for its traffic and profile files."""
+    if schedule == "default" and w.part_tokens:
+        w.part_tokens = 0
+        w.name = w.name + "_default_schedule"
+    return w
 
 
 def run_gpu(w, steps, warmup, extras, graph=False):
@@ -215,6 +228,112 @@ def time_partitions_only(w, iters=30):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters
+
+
+# The other decode configurations, each on its own layer, measured in the same
+# run: (key, workload, partition length: None = the library's choice, label).
+# "graded" rows count against the HBM peak; the shared-prefix layout reads its
+# 64 prompt blocks 128 times, from cache after the first, so its rate is an
+# effective one (logical K/V bytes / time) and is not graded against HBM.
+SIDE_CONFIGS = [
+    ("gqa_8b", "gqa_8b", None, "graded"),
+    ("prefix_copied", "prefix_copied", None, "graded"),
+    ("prefix_shared", "prefix_shared", None, "effective"),
+    ("long_context", "long_context", 512, "graded"),
+    ("long_context_default_schedule", "long_context", None, "graded"),
+]
+
+
+def profile_for(key, kernel):
+    """The committed rocprofv3 kernel-trace summary of this kernel on this workload, if any."""
+    path = os.path.join("profiles", "%s_%s.md" % (kernel, key))
+    return path if os.path.exists(os.path.join(ROOT, path)) else None
+
+
+def measure_side_configs(iters, flush_bytes=2 << 30):
+    """Decode kernel of each SIDE_CONFIGS workload: `iters` launches, each after
+    a copy of flush_bytes (8x the 256 MB last-level cache) so that no K/V byte
+    is left in cache from the launch before, with HIP events around the
+    partition pass; plus the fused step (append + decode + merge) timed over
+    `iters` back-to-back calls."""
+    import torch
+    import paged_kv_cache_227_amd as P
+    from paged_kv_cache_227_amd import workloads as W
+    dev = torch.device("cuda:0")
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    src, dst = buf[:flush_bytes // 2], buf[flush_bytes // 2:]
+    out_rows = {}
+    cache = {}
+    for key, name, part_req, label in SIDE_CONFIGS:
+        t_gen = time.perf_counter()
+        if name not in cache:
+            cache.clear()
+            cache[name] = make_workload(name)
+        w = cache[name]
+        T = W.to_torch(w, dev)
+        q, kc, vc, bt, lens = T["q"], T["k_cache"], T["v_cache"], T["block_tables"], T["context_lens"]
+        out = torch.empty_like(q)
+        layout = P.layout_of(kc)
+        part = part_req if part_req is not None else P.partition_tokens_for(w.num_seqs, w.n_q_heads,
+                                                                          w.max_blocks_per_seq, layout)
+        ws = P.alloc_workspace(q, kc, bt, part)
+        t_gen = time.perf_counter() - t_gen
+
+        def fused():
+            P.paged_kv_append_attention_decode(T["k_new"], T["v_new"], T["positions"], q, kc, vc, bt, lens,
+                                               w.scale, out, part_tokens=part, workspace=ws)
+        for _ in range(3):
+            fused()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            fused()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / iters
+        t_k, t_m = [], []
+        for _ in range(iters):
+            P.probe_copy(src, dst)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            P.paged_attention_partitions(q, kc, vc, bt, lens, w.scale, out, part, ws)
+            e[1].record()
+            P.paged_attention_merge(kc, bt, lens, out, part, ws)
+            e[2].record()
+            torch.cuda.synchronize()
+            t_k.append(e[0].elapsed_time(e[1]))
+            t_m.append(e[1].elapsed_time(e[2]))
+        kv = w.kv_read_bytes()
+        kms = statistics.fmean(t_k)
+        gbs = kv / (kms * 1e-3) / 1e9
+        kernel = "decode_flat_kernel" if part == 0 else "decode_partition_kernel"
+        row = {"label": label, "workload": name, "kernel": kernel, "partition_tokens": part, "dtype": w.dtype,
+               "num_seqs": w.num_seqs, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+               "kv_read_bytes": kv, "mean_launch_ms": round(kms, 5),
+               "median_launch_ms": round(statistics.median(t_k), 5), "merge_ms_mean": round(statistics.fmean(t_m), 5),
+               "fused_step_ms": round(ms_step, 5), "fused_step_gbs": round(kv / (ms_step * 1e-3) / 1e9, 1),
+               "timing": "HIP events around each of %d launches, each after a %d GiB cache flush" % (
+                   iters, flush_bytes >> 30)}
+        if label == "graded":
+            row["kernel_gbs"] = round(gbs, 1)
+            row["frac"] = round(gbs / HBM_PEAK_GBS, 4)
+            t = load_traffic(key, kv)
+            row["traffic"] = None if t is None else round(t["hbm_bytes_per_launch"])
+            row["hbm_read_over_algorithmic"] = None if t is None else round(t["read_over_algorithmic"], 4)
+        else:
+            row["kernel_gbs_effective"] = round(gbs, 1)
+            row["unique_kv_bytes"] = int(w.used_blocks()) * w.block_size * w.n_kv_heads * 2 * w.head_dim * (
+                4 if w.dtype == "f32" else 2)
+        row["profile"] = profile_for(key, kernel)
+        out_rows[key] = row
+        log("config %s: %s, kernel %.4f ms (%.0f GB/s%s), fused step %.4f ms (setup %.1f s)" % (
+            key, kernel, kms, gbs, "" if label == "graded" else ", effective", ms_step, t_gen))
+        del T, q, kc, vc, bt, lens, out, ws
+        torch.cuda.empty_cache()
+    del buf, src, dst
+    cache.clear()
+    torch.cuda.empty_cache()
+    return out_rows
 
 
 def cpu_baseline(w, budget_s=15.0, min_s=10.0):
@@ -672,6 +791,11 @@ def main():
                     help="write profiles/traffic_<config>.json from two rocprofv3 --pmc runs of this bench "
                          "made with --copy-probe-bytes (pass the same size)")
     ap.add_argument("--graph", action="store_true", help="also time the step as a replayed HIP graph")
+    ap.add_argument("--schedule", default="workload", choices=["workload", "default"],
+                    help="decode: the workload's own partition length (long_context: 512 tokens), or the "
+                         "library's default schedule")
+    ap.add_argument("--side-iters", type=int, default=20,
+                    help="flushed launches per configuration in the 'configs' object of the default run")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="after the steps, run the plain copy kernel once over this many bytes "
                          "(a launch of known traffic for calibrating hardware counters)")
@@ -694,9 +818,9 @@ def main():
                               a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=a.config),
                               "copy_blocks_kernel", COPY_KERNEL_SOURCES)
         else:
-            w = make_workload(a.config)
-            t = write_traffic(a.write_traffic[0], a.write_traffic[1], a.config, w.kv_read_bytes(),
-                              a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=a.config),
+            w = with_schedule(make_workload(a.config), a.schedule)
+            t = write_traffic(a.write_traffic[0], a.write_traffic[1], w.name, w.kv_read_bytes(),
+                              a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=w.name),
                               "decode_partition_kernel" if w.part_tokens else "decode_flat_kernel")
         print(json.dumps(t, indent=1))
         return 0
@@ -716,7 +840,7 @@ def main():
         return main_swap(a)
 
     t = time.perf_counter()
-    w = make_workload(a.config)
+    w = with_schedule(make_workload(a.config), a.schedule)
     log("workload %s: %d sequences, %d tokens, KV bytes %.3f GB (generated in %.1f s)"
         % (w.name, w.num_seqs, int(w.context_lens.sum()), w.kv_read_bytes() / 1e9, time.perf_counter() - t))
     kv = w.kv_read_bytes()
@@ -769,6 +893,9 @@ def main():
         res["copy_probe_bytes"] = a.copy_probe_bytes // 16 * 16
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
+    if not a.no_extras and a.config == "llama2_7b":
+        del w
+        res["configs"] = measure_side_configs(a.side_iters)
     print(json.dumps(res), flush=True)
     return 0
 

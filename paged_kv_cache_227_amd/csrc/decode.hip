@@ -57,8 +57,10 @@ namespace pkv {
 
 // Launch shape: NW waves per workgroup, R lanes per K/V row, DEPTH tiles in
 // flight ahead of the one being computed, streaming (nontemporal) loads; the
-// flat schedule's grid holds at most CAP workgroups per CU (0: as many as fit).
-template <int NW_, int R_, int DEPTH_, bool STREAM_, bool MFMA_ = false, int NH_ = 1, int CAP_ = 0>
+// flat schedule's grid holds at most CAP workgroups per CU (0: as many as fit);
+// teams of up to TEAM waves of a workgroup walk the same blocks in lockstep,
+// each wave its own head group (TEAM divides NW; 1: every wave on its own).
+template <int NW_, int R_, int DEPTH_, bool STREAM_, bool MFMA_ = false, int NH_ = 1, int CAP_ = 0, int TEAM_ = 1>
 struct Tune {
     static constexpr int NW = NW_;
     static constexpr int R = R_;
@@ -67,7 +69,25 @@ struct Tune {
     static constexpr bool MFMA = MFMA_;  // matrix-core engine (16-bit caches, G >= 4)
     static constexpr int NH = NH_;       // adjacent KV heads per wave (VALU engine)
     static constexpr int CAP = CAP_;     // flat grid: workgroups per CU at most (0: occupancy)
+    static constexpr int TEAM = TEAM_;   // largest team (a power of two dividing NW)
+    static_assert(TEAM >= 1 && (TEAM & (TEAM - 1)) == 0 && NW % TEAM == 0, "team size");
 };
+
+// The team size for ng head groups: the largest power of two up to TU::TEAM
+// that divides ng (so every team is whole).
+template <class TU>
+static int team_size(int ng) {
+    int ts = TU::TEAM;
+    while (ts > 1 && ng % ts != 0) ts /= 2;
+    return ts;
+}
+
+// a ? x : y for addresses, as a select of the two values (no branch around the
+// load that uses it).
+__device__ __forceinline__ const char* pick(bool a, const char* x, const char* y) {
+    const uint64_t ux = reinterpret_cast<uint64_t>(x), uy = reinterpret_cast<uint64_t>(y);
+    return reinterpret_cast<const char*>(a ? ux : uy);
+}
 
 // One wave's share of the attention for NH adjacent KV heads (a head group)
 // and the G query heads of each.  The NH head rows of one token are adjacent
@@ -125,6 +145,24 @@ struct WaveAttn {
             for (int k = 0; k < CPL; ++k) settle(qv[gi][k]);
     }
 
+    // The flat schedule loads the q rows of a segment's pair into the slot of
+    // the segment's first tile, right before that tile's K/V loads, so the
+    // wait for the tile covers them; take_q makes them current.
+    Vec16 qs[NS][G][CPL];
+    __device__ __forceinline__ void load_q_slot(int slot, const char* q_rows) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int k = 0; k < CPL; ++k)
+                qs[slot][gi][k] = load16(q_rows + (hd * G + gi) * RB + (c + k * R) * 16);
+    }
+    __device__ __forceinline__ void take_q(int slot) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) qv[gi][k] = qs[slot][gi][k];
+    }
+
     __device__ __forceinline__ void reset() {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
@@ -139,18 +177,20 @@ struct WaveAttn {
     // A load instruction covers RPS consecutive rows, all in the same half.
     // Tile row `prow` (if 0..15) is read from the rows kn, vn ([NH][D] of the
     // token being appended) instead of the cache.
+    // FRESH = false: no row comes from kn / vn (prow is ignored).
+    template <bool FRESH>
     __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi,
                                           int prow, const char* kn, const char* vn) {
         static_assert(8 % RPS == 0, "a load instruction stays within one half of the tile");
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int64_t boff = j * RPS < 8 ? lo : hi;
-            const bool fresh = j * RPS + rg == prow;
+            const bool fresh = FRESH && j * RPS + rg == prow;
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
                 const uint32_t col = hd * RB + (c + k * R) * 16;
-                kb[slot][j][k] = load16_policy<TU::STREAM>(fresh ? kn + col : kbase + boff + lane_off[j][k]);
-                vb[slot][j][k] = load16_policy<TU::STREAM>(fresh ? vn + col : vbase + boff + lane_off[j][k]);
+                kb[slot][j][k] = load16_policy<TU::STREAM>(pick(fresh, kn + col, kbase + boff + lane_off[j][k]));
+                vb[slot][j][k] = load16_policy<TU::STREAM>(pick(fresh, vn + col, vbase + boff + lane_off[j][k]));
             }
         }
     }
@@ -379,6 +419,24 @@ struct MfmaAttn {
             for (int kk = 0; kk < KK; ++kk) settle(qb[h][kk]);
     }
 
+    // As in WaveAttn: a segment's q rows ride in the slot of its first tile.
+    Vec16 qs[NS][NH][KK];
+    __device__ __forceinline__ void load_q_slot(int slot, const char* q_rows) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const Vec16 z = {{0u, 0u, 0u, 0u}};
+                qs[slot][h][kk] = (j >= h * G && j < (h + 1) * G) ? load16(q_rows + j * RB + (4 * kk + g) * 16) : z;
+            }
+    }
+    __device__ __forceinline__ void take_q(int slot) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) qb[h][kk] = qs[slot][h][kk];
+    }
+
     __device__ __forceinline__ void reset() {
         m = -INFINITY;
         l = 0.f;
@@ -388,6 +446,7 @@ struct MfmaAttn {
 
     // Tile row `prow` (if 0..15) is read from the rows kn, vn ([NH][D] of the
     // token being appended) instead of the cache.
+    template <bool FRESH>
     __device__ __forceinline__ void issue(int slot, const char* kbase, const char* vbase, int64_t lo, int64_t hi,
                                           int prow, const char* kn, const char* vn) {
         static_assert(8 % RPI == 0, "a load instruction stays within one half of the tile");
@@ -395,9 +454,9 @@ struct MfmaAttn {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int64_t off = (i * RPI < 8 ? lo : hi) + ld_base + (int64_t)i * RPI * row_stride_;
-            const bool fresh = i * RPI + lrow == prow;
-            kt[slot][i] = load16_policy<TU::STREAM>(fresh ? kn + col : kbase + off);
-            vt[slot][i] = load16_policy<TU::STREAM>(fresh ? vn + col : vbase + off);
+            const bool fresh = FRESH && i * RPI + lrow == prow;
+            kt[slot][i] = load16_policy<TU::STREAM>(pick(fresh, kn + col, kbase + off));
+            vt[slot][i] = load16_policy<TU::STREAM>(pick(fresh, vn + col, vbase + off));
         }
     }
 
@@ -558,16 +617,33 @@ __device__ __forceinline__ int table_entry(const int32_t* table, int i) {
     return ((const_i32*)table)[__builtin_amdgcn_readfirstlane(i)];
 }
 
-__device__ __forceinline__ TileAddr tile_addr(const int32_t* table, int t, int ntab, int shift, int num_blocks,
-                                              uint32_t row_stride) {
+// The table entries tile t needs: the block of rows 0-7 and, when B = 8 and
+// the second block belongs to the sequence, the block of rows 8-15.
+struct TileEnt {
+    int pb0, pb1;
+};
+
+__device__ __forceinline__ TileEnt tile_entries(const int32_t* table, int t, int ntab, int shift) {
+    const int tok0 = t * kBlock;
+    const int bi0 = tok0 >> shift;
+    const int bi1 = (tok0 + 8) >> shift;
+    const bool second = bi1 != bi0 && bi1 < ntab;
+    TileEnt e;
+    e.pb0 = table_entry(table, bi0);
+    e.pb1 = table_entry(table, second ? bi1 : bi0);  // no branch: neither read waits here
+    return e;
+}
+
+__device__ __forceinline__ TileAddr tile_addr_of(TileEnt e, int t, int ntab, int shift, int num_blocks,
+                                                 uint32_t row_stride) {
     const int tok0 = t * kBlock;
     const int bmask = (1 << shift) - 1;
     const int64_t blk_bytes = (int64_t)row_stride << shift;
     const int bi0 = tok0 >> shift;
     const int bi1 = (tok0 + 8) >> shift;
     const bool second = bi1 != bi0 && bi1 < ntab;
-    int pb0 = table_entry(table, bi0);
-    int pb1 = second ? table_entry(table, bi1) : pb0;
+    int pb0 = e.pb0;
+    int pb1 = e.pb1;
     TileAddr a;
     a.ok = pb0 >= 0 && pb0 < num_blocks && pb1 >= 0 && pb1 < num_blocks;
     if (!a.ok) pb0 = pb1 = 0;
@@ -578,18 +654,25 @@ __device__ __forceinline__ TileAddr tile_addr(const int32_t* table, int t, int n
     return a;
 }
 
+__device__ __forceinline__ TileAddr tile_addr(const int32_t* table, int t, int ntab, int shift, int num_blocks,
+                                              uint32_t row_stride) {
+    return tile_addr_of(tile_entries(table, t, ntab, shift), t, ntab, shift, num_blocks, row_stride);
+}
+
 // ============================================================================
 // Flat schedule: a persistent grid deals equal ranges of the tile stream.
 // ============================================================================
 
-template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
+template <class E, int D, int G, class TU, bool FUSED, class A = Engine<E, D, G, TU>>
 __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParams p) {
     constexpr int NS = A::NS;
     constexpr int DEPTH = TU::DEPTH;
     extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
     const int S = p.num_seqs;
     const int Hkv = p.n_kv_heads;
-    const int NG = Hkv / A::NH;  // head groups: the tile stream's middle index
+    const int NG = Hkv / A::NH;  // head groups
+    const int TS = p.team;       // waves per team (divides NG and NW)
+    const int NGB = NG / TS;     // blocks of TS head groups: the tile stream's middle index
     const int Hq = p.n_q_heads;
     // [NW engine areas][Ls: clamped context length per sequence][pre: tile prefix]
     int32_t* Ls = reinterpret_cast<int32_t*>(dyn_lds + TU::NW * A::kLdsBytes);
@@ -604,7 +687,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         int carry = 0;
         for (int base = 0; base < S; base += kWave) {
             const int i = base + lane;
-            int v = i < S ? ((Ls[i] + kBlock - 1) / kBlock) * NG : 0;
+            int v = i < S ? ((Ls[i] + kBlock - 1) / kBlock) * NGB : 0;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 const int y = __shfl_up(v, off, kWave);
@@ -617,8 +700,8 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     }
     __syncthreads();
     const int T = pre[S];
-    const int Wt = gridDim.x * TU::NW;
-    const int per = max((T + Wt - 1) / Wt, p.min_tiles_per_worker);
+    const int NT = gridDim.x * (TU::NW / TS);  // teams in the grid
+    const int per = max((T + NT - 1) / NT, p.min_tiles_per_worker);
     if (blockIdx.x == 0) {  // the schedule, for the merge pass
         if (threadIdx.x == 0) {
             p.ws_hdr[0] = per;
@@ -627,8 +710,13 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         for (int i = threadIdx.x; i <= S; i += blockDim.x) p.ws_hdr[2 + i] = pre[i];
     }
 
+    // Team `team` takes tiles [team * per, (team + 1) * per) of the stream; its
+    // wave tj streams head group hb * TS + tj of each tile (sequence, hb, block),
+    // so the team's waves read the same blocks at the same time.
     const int w = blockIdx.x * TU::NW + wave_id_uniform();
-    const int t0 = w * per;
+    const int team = w / TS;
+    const int tj = w - team * TS;
+    const int t0 = team * per;
     const int t1 = min(t0 + per, T);
     if (t0 >= T) return;
 
@@ -636,11 +724,19 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     const uint32_t row_stride = (uint32_t)Hkv * A::RB;
     const char* kcache = static_cast<const char*>(p.k_cache);
     const char* vcache = static_cast<const char*>(p.v_cache);
-    const bool fused = p.positions != nullptr;
+    // FUSED: an append in the same call (positions != nullptr).
 
-    // Cursor over the tile stream: sequence, head group, block, blocks of the sequence.
+    // Cursor over the tile stream, kept in scalar registers: sequence, block
+    // of TS head groups, block, blocks and length of the sequence.
     struct Cur {
-        int s, kvh, b, nb;  // kvh: the head group
+        int s, kvh, b, nb, L;
+    };
+    auto uniform = [](Cur& q) {
+        q.s = __builtin_amdgcn_readfirstlane(q.s);
+        q.kvh = __builtin_amdgcn_readfirstlane(q.kvh);
+        q.b = __builtin_amdgcn_readfirstlane(q.b);
+        q.nb = __builtin_amdgcn_readfirstlane(q.nb);
+        q.L = __builtin_amdgcn_readfirstlane(q.L);
     };
     auto locate = [&](int t) {
         int lo = 0, hi = S;  // largest s with pre[s] <= t (then t < pre[s + 1])
@@ -651,78 +747,96 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         }
         Cur q;
         q.s = lo;
-        q.nb = (Ls[lo] + kBlock - 1) / kBlock;
+        q.L = Ls[lo];
+        q.nb = (q.L + kBlock - 1) / kBlock;
         const int r = t - pre[lo];
         q.kvh = r / q.nb;
         q.b = r - q.kvh * q.nb;
+        uniform(q);
         return q;
     };
+    // Only a move to the next sequence reads LDS.
     auto advance = [&](Cur& q) {
         if (++q.b == q.nb) {
             q.b = 0;
-            if (++q.kvh == NG) {
+            if (++q.kvh == NGB) {
                 q.kvh = 0;
                 do {
                     ++q.s;
                 } while (q.s < S && Ls[q.s] == 0);
-                q.nb = q.s < S ? (Ls[q.s] + kBlock - 1) / kBlock : 1;
+                q.L = q.s < S ? Ls[q.s] : 0;
+                q.nb = q.s < S ? (q.L + kBlock - 1) / kBlock : 1;
             }
         }
-        q.s = __builtin_amdgcn_readfirstlane(q.s);
-        q.kvh = __builtin_amdgcn_readfirstlane(q.kvh);
-        q.b = __builtin_amdgcn_readfirstlane(q.b);
-        q.nb = __builtin_amdgcn_readfirstlane(q.nb);
+        uniform(q);
     };
 
     A a;
     a.init(lane, row_stride, dyn_lds + wave_id_uniform() * A::kLdsBytes);
     bool oks[NS];
     const int bmask = (1 << p.block_shift) - 1;
+    // The scalar reads a tile's issue needs (table entries, and the new
+    // token's position when an append is fused) are made one issue ahead, so
+    // their latency passes while the tile before is computed.
+    struct Ahead {
+        TileEnt e;
+        int pos;
+    };
+    auto fetch = [&](const Cur& q, bool real) {
+        Ahead f = {{0, 0}, -1};
+        if (real) {
+            const int ntab = (q.L + bmask) >> p.block_shift;
+            f.e = tile_entries(p.block_tables + (int64_t)q.s * p.max_blocks, q.b, ntab, p.block_shift);
+            if constexpr (FUSED) f.pos = table_entry(p.positions, q.s);
+        }
+        return f;
+    };
     // Every pass issues its loads, also past the wave's last tile (then of the
     // first rows of block 0, never computed): loads are counted in issue order,
     // and a load issued on one path only would make the wait for the tile
     // being computed also wait for the tiles issued after it.
-    auto issue = [&](int slot, const Cur& q, bool real) {
+    int qs_s = -1, qs_k = -1;  // pair of the last tile issued
+    auto issue = [&](int slot, const Cur& q, const Ahead& f, bool real) {
+        if (real && (q.s != qs_s || q.kvh != qs_k)) {  // the first tile of a segment carries its q rows
+            qs_s = q.s;
+            qs_k = q.kvh;
+            a.load_q_slot(slot, static_cast<const char*>(p.q) + ((int64_t)q.s * Hq + (q.kvh * TS + tj) * A::HG) * A::RB);
+        }
         TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
         if (real) {
-            const int ntab = (Ls[q.s] + bmask) >> p.block_shift;
-            ta = tile_addr(p.block_tables + (int64_t)q.s * p.max_blocks, q.b, ntab, p.block_shift, p.num_blocks,
-                           row_stride);
+            const int ntab = (q.L + bmask) >> p.block_shift;
+            ta = tile_addr_of(f.e, q.b, ntab, p.block_shift, p.num_blocks, row_stride);
         }
-        const int64_t hoff = real ? (int64_t)q.kvh * A::NH * A::RB : 0;
+        const int64_t hoff = real ? (int64_t)(q.kvh * TS + tj) * A::NH * A::RB : 0;
         // With an append in the same call, the tile holding the new token's
         // position reads that row from k_new / v_new.
         int prow = -1;
         const char *kn = kcache, *vn = vcache;
-        if (fused && real) {
-            const int r = table_entry(p.positions, q.s) - q.b * kBlock;
-            if (r >= 0 && r < kBlock) {
+        if constexpr (FUSED) {
+            const int r = f.pos - q.b * kBlock;
+            if (real && r >= 0 && r < kBlock) {
                 prow = r;
-                const int64_t roff = ((int64_t)q.s * Hkv + q.kvh * A::NH) * A::RB;
+                const int64_t roff = ((int64_t)q.s * Hkv + (q.kvh * TS + tj) * A::NH) * A::RB;
                 kn = static_cast<const char*>(p.k_new) + roff;
                 vn = static_cast<const char*>(p.v_new) + roff;
             }
         }
-        a.issue(slot, kcache + hoff, vcache + hoff, ta.lo, ta.hi, prow, kn, vn);
+        a.template issue<FUSED>(slot, kcache + hoff, vcache + hoff, ta.lo, ta.hi, prow, kn, vn);
         oks[slot] = ta.ok;
     };
 
     Cur cur = locate(t0);
-    cur.s = __builtin_amdgcn_readfirstlane(cur.s);
-    cur.kvh = __builtin_amdgcn_readfirstlane(cur.kvh);
-    cur.b = __builtin_amdgcn_readfirstlane(cur.b);
-    cur.nb = __builtin_amdgcn_readfirstlane(cur.nb);
-    // q before the first tiles: the wait for a tile then also covers q.
-    int as = cur.s, akvh = cur.kvh;  // the segment being accumulated
-    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
+    int as = -1, akvh = -1, aL = 0;  // the segment being accumulated (none yet)
     a.reset();
 
     Cur iss = cur;
+    Ahead ahead = fetch(iss, t0 < t1);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
         const bool real = t0 + d < t1;
-        issue(d, iss, real);
+        issue(d, iss, ahead, real);
         if (real) advance(iss);
+        ahead = fetch(iss, t0 + d + 1 < t1);
     }
 
     // A finished segment is written as normalised output rows when this wave
@@ -742,10 +856,13 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     int64_t held_dst = 0;
     auto flush = [&]() {
         a.reduce();
-        const int nb = (Ls[as] + kBlock - 1) / kBlock;
+        const int nb = (aL + kBlock - 1) / kBlock;
         const int p0 = pre[as] + akvh * nb;  // the pair's tiles are [p0, p0 + nb)
         const bool whole = p0 / per == (p0 + nb - 1) / per;
-        const int64_t dst = whole ? (int64_t)as * Hq + akvh * A::HG : (int64_t)as * NG + akvh + w;
+        // split pairs: record (pair + team) * TS + tj, unique because pair + team
+        // grows by at least one from one segment of a wave to the next
+        const int64_t dst = whole ? (int64_t)as * Hq + (akvh * TS + tj) * A::HG
+                                  : ((int64_t)as * NGB + akvh + team) * TS + tj;
         if constexpr (A::kHold) {
             if (have_held) emit(held, held_whole, held_dst);
             a.take(held);
@@ -764,18 +881,19 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         for (int u = 0; u < NS; ++u) {
             const int tt = t + u;
             const bool real = tt + DEPTH < t1;
-            issue((u + DEPTH) % NS, iss, real);
+            issue((u + DEPTH) % NS, iss, ahead, real);
             if (real) advance(iss);
+            ahead = fetch(iss, tt + DEPTH + 1 < t1);
             if (tt < t1) {
                 if (cur.s != as || cur.kvh != akvh) {
-                    flush();
+                    if (as >= 0) flush();
                     as = cur.s;
                     akvh = cur.kvh;
-                    a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + akvh * A::HG) * A::RB);
-                    a.settle_q();  // here, not at the next product, where it would also wait for the next tiles
+                    aL = cur.L;
+                    a.take_q(u);
                     a.reset();
                 }
-                const int valid = !oks[u] ? 0 : (cur.b == cur.nb - 1 ? Ls[cur.s] - cur.b * kBlock : kBlock);
+                const int valid = !oks[u] ? 0 : (cur.b == cur.nb - 1 ? cur.L - cur.b * kBlock : kBlock);
                 a.process(u, valid, p.scale_log2);
                 advance(cur);
             }
@@ -895,7 +1013,11 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
     if (p.positions != nullptr && h % Gq == 0) append_head_row<E, D>(p, s, h / Gq, lane);
     const int HG = p.n_q_heads / p.n_kv_heads * p.heads_per_wave;  // query heads per record
     const int NG = p.n_kv_heads / p.heads_per_wave;
+    const int TS = p.team;
+    const int NGB = NG / TS;
     const int hg = h / HG;
+    const int hb = hg / TS;
+    const int tj = hg - hb * TS;
     const int gi = h % HG;
     char* out_row = static_cast<char*>(p.out) + (int64_t)pair * D * E::kBytes;
     const int L = min(max(p.context_lens[s], 0), (p.max_blocks << p.block_shift));
@@ -907,18 +1029,20 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
     }
     const int per = p.ws_hdr[0];
     const int nb = (L + kBlock - 1) / kBlock;
-    const int p0 = p.ws_hdr[2 + s] + hg * nb;
-    const int w0 = p0 / per;
+    const int p0 = p.ws_hdr[2 + s] + hb * nb;
+    const int w0 = p0 / per;  // teams w0 .. w1 hold the pair's tiles
     const int w1 = (p0 + nb - 1) / per;
     if (w0 == w1) return;  // one wave held the whole pair and wrote it
-    const int64_t base = (int64_t)s * NG + hg;  // record of wave w is base + w
-    merge_records<E, D>(p.ws_ml, p.ws_acc, (base + w0) * HG + gi, HG, w1 - w0 + 1, out_row);
+    const int64_t base = (int64_t)s * NGB + hb;  // record of team w is (base + w) * TS + tj
+    merge_records<E, D>(p.ws_ml, p.ws_acc, ((base + w0) * TS + tj) * HG + gi, TS * HG, w1 - w0 + 1, out_row);
 }
 
 // ============================================================================
 // Fixed partitions: one wave per (P-token partition, head group, sequence).
-// A workgroup holds NW consecutive partitions of one sequence and head group;
-// its waves share nothing.  Grid: x = sequence * chunks + chunk, y = head group.
+// A workgroup holds NW / TS consecutive partitions of one sequence, each for a
+// team of TS adjacent head groups (TS = 1: NW partitions of one head group);
+// the team's waves read the same blocks in lockstep and share nothing else.
+// Grid: x = sequence * chunks + chunk, y = block of TS head groups.
 // ============================================================================
 
 template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
@@ -929,12 +1053,15 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     constexpr int HG = A::HG;
     __shared__ __attribute__((aligned(16))) char sm_eng[NW * (A::kLdsBytes > 0 ? A::kLdsBytes : 16)];
 
-    const int chunks = (p.n_parts_max + NW - 1) / NW;
+    const int TS = p.team;
+    const int PW = NW / TS;  // partitions per workgroup
+    const int chunks = (p.n_parts_max + PW - 1) / PW;
     const int s = blockIdx.x / chunks;
     const int w = wave_id_uniform();
-    const int part = (blockIdx.x - s * chunks) * NW + w;
-    const int hg = blockIdx.y;  // head group: KV heads hg*NH .. +NH-1
-    const int NG = gridDim.y;
+    const int pi = w / TS;
+    const int part = (blockIdx.x - s * chunks) * PW + pi;
+    const int hg = blockIdx.y * TS + (w - pi * TS);  // head group: KV heads hg*NH .. +NH-1
+    const int NG = gridDim.y * TS;
     const int Hq = p.n_q_heads;
     const int lane = threadIdx.x % kWave;
     char* out_rows = static_cast<char*>(p.out) + ((int64_t)s * Hq + hg * HG) * D * E::kBytes;
@@ -972,7 +1099,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     auto issue = [&](int slot, int bi, bool real) {
         TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
         if (real) ta = tile_addr(table, bi, ntab, p.block_shift, p.num_blocks, row_stride);
-        a.issue(slot, kbase, vbase, ta.lo, ta.hi, -1, kbase, vbase);
+        a.template issue<false>(slot, kbase, vbase, ta.lo, ta.hi, -1, kbase, vbase);
         oks[slot] = ta.ok;
     };
 
@@ -1118,14 +1245,17 @@ struct DefaultTune {
     static constexpr int kCH = D * E::kBytes / 16;
     static constexpr int kR = kCH < 16 ? kCH : 16;
     static constexpr int kNH = E::kBytes == 2 && !kMfma ? 2 : 1;
-    using mfma_flat = typename std::conditional<(G >= 8), Tune<1, 8, 1, true, true, 1>, Tune<8, 8, 2, true, true, 1>>::type;
+    // matrix-core engine: teams of up to 8 waves (one workgroup) stream the
+    // KV heads of the same blocks together
+    using mfma_flat = typename std::conditional<(G >= 8), Tune<8, 8, 1, true, true, 1, 0, 8>,
+                                                Tune<8, 8, 1, true, true, 1, 0, 8>>::type;
     // fp32 with G >= 4 spreads a head row over more lanes: fewer accumulators per lane
     static constexpr int kRf = E::kBytes == 4 && G >= 4 ? kR : 8;
     // 16-bit, two KV heads a wave: one 4-wave workgroup per CU (one wave per
     // SIMD) streams 2-3 % faster than the two waves per SIMD that fit
     using valu = typename std::conditional<kNH == 2, Tune<4, kR, 1, true, false, 2, 1>, Tune<4, kRf, 1, true, false, 1>>::type;
     using type = typename std::conditional<kMfma, mfma_flat, valu>::type;
-    using parts = typename std::conditional<kMfma, Tune<1, 8, 2, true, true, 1>, valu>::type;
+    using parts = typename std::conditional<kMfma, Tune<8, 8, 2, true, true, 1, 0, 8>, valu>::type;
     using NH1 = Tune<4, kMfma ? 8 : kRf, 1, true, kMfma, 1>;
 };
 
@@ -1135,13 +1265,24 @@ static int heads_per_wave_t(int n_kv_heads) {
     return n_kv_heads % nh == 0 ? nh : 1;
 }
 
+// Team size of the flat schedule's launch for this shape (the merge pass needs it).
+template <class E, int D, int G>
+static int flat_team_t(int n_kv_heads) {
+    using TU = typename DefaultTune<E, D, G>::type;
+    using TU1 = typename DefaultTune<E, D, G>::NH1;
+    return heads_per_wave_t<E, D, G>(n_kv_heads) == TU::NH ? team_size<TU>(n_kv_heads / TU::NH)
+                                                            : team_size<TU1>(n_kv_heads);
+}
+
 template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
 hipError_t launch_parts_tuned(const DecodeParams& pin, hipStream_t stream) {
     DecodeParams p = pin;
     p.heads_per_wave = A::NH;
-    const int64_t chunks = (p.n_parts_max + TU::NW - 1) / TU::NW;
+    const int ng = p.n_kv_heads / A::NH;
+    p.team = team_size<TU>(ng);
+    const int64_t chunks = (p.n_parts_max + TU::NW / p.team - 1) / (TU::NW / p.team);
     if (chunks * p.num_seqs > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(chunks * p.num_seqs), p.n_kv_heads / A::NH);
+    const dim3 grid((unsigned)(chunks * p.num_seqs), ng / p.team);
     hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU, A>), grid, dim3(TU::NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
@@ -1152,7 +1293,13 @@ template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
 hipError_t launch_flat_tuned(const DecodeParams& pin, hipStream_t stream) {
     DecodeParams p = pin;
     p.heads_per_wave = A::NH;
-    auto kern = decode_flat_kernel<E, D, G, TU, A>;
+    p.team = team_size<TU>(p.n_kv_heads / A::NH);
+    // The grid is sized from the kernel without the fused append, and the fused
+    // kernel gets the same grid: the tiles are then dealt alike and both give
+    // the same bits.  (Its waves do not wait on one another, so a grid larger
+    // than what is resident would only run in turns.)
+    auto kern_plain = decode_flat_kernel<E, D, G, TU, false, A>;
+    auto kern = p.positions != nullptr ? decode_flat_kernel<E, D, G, TU, true, A> : kern_plain;
     const size_t lds = (size_t)TU::NW * A::kLdsBytes + (size_t)(2 * p.num_seqs + 1) * sizeof(int32_t);
     static thread_local int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
     static thread_local size_t cached_lds = 0;
@@ -1163,7 +1310,7 @@ hipError_t launch_flat_tuned(const DecodeParams& pin, hipStream_t stream) {
         int cus = 0, per_cu = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, TU::NW * kWave, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern_plain, TU::NW * kWave, lds);
         if (e != hipSuccess) return e;
         cached_dev = dev;
         cached_lds = lds;
@@ -1225,6 +1372,22 @@ static int heads_per_wave_e(int head_dim, int group, int n_kv_heads) {
                           : heads_per_wave_d<E, 128>(group, n_kv_heads);
 }
 
+template <class E, int D>
+static int flat_team_d(int group, int n_kv_heads) {
+    switch (group) {
+        case 1: return flat_team_t<E, D, 1>(n_kv_heads);
+        case 2: return flat_team_t<E, D, 2>(n_kv_heads);
+        case 4: return flat_team_t<E, D, 4>(n_kv_heads);
+        case 8: return flat_team_t<E, D, 8>(n_kv_heads);
+        default: return 1;
+    }
+}
+
+template <class E>
+static int flat_team_e(int head_dim, int group, int n_kv_heads) {
+    return head_dim == 64 ? flat_team_d<E, 64>(group, n_kv_heads) : flat_team_d<E, 128>(group, n_kv_heads);
+}
+
 int decode_heads_per_wave(int dtype, int head_dim, int group, int n_kv_heads) {
     switch (dtype) {
         case 0: return heads_per_wave_e<F32>(head_dim, group, n_kv_heads);
@@ -1254,6 +1417,7 @@ template <class E>
 static hipError_t launch_merge_e(const DecodeParams& pin, int head_dim, int group, hipStream_t stream) {
     DecodeParams p = pin;
     p.heads_per_wave = heads_per_wave_e<E>(head_dim, group, p.n_kv_heads);
+    p.team = flat_team_e<E>(head_dim, group, p.n_kv_heads);
     const int pairs = p.num_seqs * p.n_q_heads;
     const dim3 grid_flat((pairs + 3) / 4);  // one wave per pair
     const dim3 grid_parts(pairs);           // one workgroup per pair

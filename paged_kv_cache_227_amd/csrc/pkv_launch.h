@@ -112,6 +112,7 @@ struct DecodeParams {
     int32_t n_parts_max;
     int32_t min_tiles_per_worker;
     int32_t heads_per_wave;  // adjacent KV heads one wave streams together (see decode_heads_per_wave)
+    int32_t team;            // waves walking the same blocks, one head group each (set by the launchers)
     int32_t block_shift;     // log2 of the cache block size (8, 16, 32 or 64 tokens)
     float scale_log2;  // scale * log2(e): scores are kept in base-2 units
     // A fused append (flat schedule only; positions == nullptr otherwise): the

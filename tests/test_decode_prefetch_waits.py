@@ -7,8 +7,8 @@ one branch only, or a store among the loads made the wait for the tile being
 computed also wait for every tile issued after it: in the kernels below no
 wait then left more than half a tile's loads outstanding.  With the tiles kept
 in flight, the steady-state wait leaves at least one whole tile's loads
-(16: K and V of 16 rows at 512 bytes a row over 64 lanes, or two tiles of 8
-for the matrix-core engine) outstanding.
+(16: K and V of 16 rows at 512 bytes a row over 64 lanes; 8 for the
+matrix-core engine's 256-byte rows) outstanding.
 """
 import os
 import re
@@ -24,11 +24,15 @@ sys.path.insert(0, ROOT)
 # (kernel name fragment, loads a wait must leave outstanding in the steady state)
 CASES = {
     "flat, f16, head_dim 128, one query head per KV head (vector engine, two heads a wave)":
-        (r"decode_flat_kernelINS_3F16ELi128ELi1ENS_4TuneILi4ELi16ELi1ELb1ELb0ELi2ELi1E", 16),
+        (r"decode_flat_kernelINS_3F16ELi128ELi1ENS_4TuneILi4ELi16ELi1ELb1ELb0ELi2ELi1ELi1EEELb0E", 16),
+    "flat with the append fused, f16, head_dim 128, one query head per KV head (vector engine)":
+        (r"decode_flat_kernelINS_3F16ELi128ELi1ENS_4TuneILi4ELi16ELi1ELb1ELb0ELi2ELi1ELi1EEELb1E", 16),
     "flat, bf16, head_dim 128, four query heads per KV head (matrix-core engine)":
-        (r"decode_flat_kernelINS_4BF16ELi128ELi4ENS_4TuneILi8ELi8ELi2ELb1ELb1ELi1E", 16),
+        (r"decode_flat_kernelINS_4BF16ELi128ELi4ENS_4TuneILi8ELi8ELi1ELb1ELb1ELi1ELi0ELi8EEELb0E", 8),
+    "flat, bf16, head_dim 128, eight query heads per KV head (matrix-core engine)":
+        (r"decode_flat_kernelINS_4BF16ELi128ELi8ENS_4TuneILi8ELi8ELi1ELb1ELb1ELi1ELi0ELi8EEELb0E", 8),
     "fixed partitions, bf16, head_dim 128, eight query heads per KV head (matrix-core engine)":
-        (r"decode_partition_kernelINS_4BF16ELi128ELi8ENS_4TuneILi1ELi8ELi2ELb1ELb1ELi1E", 8),
+        (r"decode_partition_kernelINS_4BF16ELi128ELi8ENS_4TuneILi8ELi8ELi2ELb1ELb1ELi1ELi0ELi8E", 8),
 }
 
 
