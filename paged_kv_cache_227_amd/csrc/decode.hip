@@ -60,7 +60,8 @@ namespace pkv {
 // flat schedule's grid holds at most CAP workgroups per CU (0: as many as fit);
 // teams of up to TEAM waves of a workgroup walk the same blocks in lockstep,
 // each wave its own head group (TEAM divides NW; 1: every wave on its own).
-template <int NW_, int R_, int DEPTH_, bool STREAM_, bool MFMA_ = false, int NH_ = 1, int CAP_ = 0, int TEAM_ = 1>
+template <int NW_, int R_, int DEPTH_, bool STREAM_, bool MFMA_ = false, int NH_ = 1, int CAP_ = 0, int TEAM_ = 1,
+          int KS_ = 1>
 struct Tune {
     static constexpr int NW = NW_;
     static constexpr int R = R_;
@@ -70,7 +71,8 @@ struct Tune {
     static constexpr int NH = NH_;       // adjacent KV heads per wave (VALU engine)
     static constexpr int CAP = CAP_;     // flat grid: workgroups per CU at most (0: occupancy)
     static constexpr int TEAM = TEAM_;   // largest team (a power of two dividing NW)
-    static_assert(TEAM >= 1 && (TEAM & (TEAM - 1)) == 0 && NW % TEAM == 0, "team size");
+    static constexpr int KS = KS_;       // fixed partitions: waves that split one partition's tiles
+    static_assert(TEAM >= 1 && (TEAM & (TEAM - 1)) == 0 && NW % (TEAM * KS) == 0, "team size");
 };
 
 // The team size for ng head groups: the largest power of two up to TU::TEAM
@@ -289,6 +291,21 @@ struct WaveAttn {
     };
     static constexpr bool kHold = G * (EPL + 2) <= 18;  // one query head per KV head: 10-18 registers
 
+    // r = the combination of the states r and o of the same rows (log-sum-exp
+    // rule; o may be empty: m = -inf, l = 0).
+    __device__ static __forceinline__ void combine(Result& r, const Result& o) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const float M = fmaxf(r.m[gi], o.m[gi]);
+            const float f0 = r.m[gi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(r.m[gi] - M);
+            const float f1 = o.m[gi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o.m[gi] - M);
+            r.l[gi] = f0 * r.l[gi] + f1 * o.l[gi];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) r.acc[gi][e] = f0 * r.acc[gi][e] + f1 * o.acc[gi][e];
+            r.m[gi] = M;
+        }
+    }
+
     __device__ __forceinline__ void take(Result& r) const {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
@@ -310,8 +327,11 @@ struct WaveAttn {
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    E::store(out_rows + (row * D + (c + k * R) * VEC + e) * E::kBytes, r.acc[gi][k * VEC + e] * inv);
+                for (int e = 0; e < VEC; e += 4) {
+                    const float* x = &r.acc[gi][k * VEC + e];
+                    store4<E>(out_rows + (row * D + (c + k * R) * VEC + e) * E::kBytes, x[0] * inv, x[1] * inv,
+                              x[2] * inv, x[3] * inv);
+                }
         }
     }
 
@@ -332,6 +352,24 @@ struct WaveAttn {
                 rec_ml[row * 2] = r.m[gi];
                 rec_ml[row * 2 + 1] = r.l[gi];
             }
+        }
+    }
+
+    // A state to and from LDS in the record's own order: acc [HG][D], then
+    // (m, l) [HG][2].  Every lane reads back what it holds after reduce.
+    __device__ __forceinline__ void stage(const Result& r, float* slot) const {
+        store_partial(r, slot, slot + HG * D);
+    }
+    __device__ __forceinline__ void unstage(const float* slot, Result& r) const {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const int row = hd * G + gi;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) r.acc[gi][k * VEC + e] = slot[row * D + (c + k * R) * VEC + e];
+            r.m[gi] = slot[HG * D + row * 2];
+            r.l[gi] = slot[HG * D + row * 2 + 1];
         }
     }
 };
@@ -559,6 +597,17 @@ struct MfmaAttn {
     };
     static constexpr bool kHold = HG <= 4;  // more query heads leave no registers to spare
 
+    // r = the combination of r and o (see WaveAttn::combine).
+    __device__ static __forceinline__ void combine(Result& r, const Result& o) {
+        const float M = fmaxf(r.m, o.m);
+        const float f0 = r.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(r.m - M);
+        const float f1 = o.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o.m - M);
+        r.l = f0 * r.l + f1 * o.l;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) r.acc[t] = f0 * r.acc[t] + f1 * o.acc[t];
+        r.m = M;
+    }
+
     __device__ __forceinline__ void take(Result& r) const {
 #pragma unroll
         for (int t = 0; t < TT; ++t) r.acc[t] = acc[t];
@@ -571,8 +620,8 @@ struct MfmaAttn {
         const float inv = 1.f / r.l;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) E::store(out_rows + (j * D + 16 * t + 4 * g + i) * 2, r.acc[t][i] * inv);
+            store4<E>(out_rows + (j * D + 16 * t + 4 * g) * 2, r.acc[t][0] * inv, r.acc[t][1] * inv,
+                      r.acc[t][2] * inv, r.acc[t][3] * inv);
     }
 
     __device__ __forceinline__ void store_partial(const Result& r, float* rec_acc, float* rec_ml) const {
@@ -585,6 +634,27 @@ struct MfmaAttn {
             rec_ml[j * 2] = r.m;
             rec_ml[j * 2 + 1] = r.l;
         }
+    }
+
+    // See WaveAttn::stage; columns past HG (padding) read back as empty states.
+    __device__ __forceinline__ void stage(const Result& r, float* slot) const {
+        store_partial(r, slot, slot + HG * D);
+    }
+    __device__ __forceinline__ void unstage(const float* slot, Result& r) const {
+        if (j >= HG) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) r.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            r.m = -INFINITY;
+            r.l = 0.f;
+            return;
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const float4 v = *reinterpret_cast<const float4*>(slot + j * D + 16 * t + 4 * g);
+            r.acc[t] = f32x4_t{v.x, v.y, v.z, v.w};
+        }
+        r.m = slot[HG * D + j * 2];
+        r.l = slot[HG * D + j * 2 + 1];
     }
 };
 
@@ -1038,30 +1108,44 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
 }
 
 // ============================================================================
-// Fixed partitions: one wave per (P-token partition, head group, sequence).
-// A workgroup holds NW / TS consecutive partitions of one sequence, each for a
-// team of TS adjacent head groups (TS = 1: NW partitions of one head group);
-// the team's waves read the same blocks in lockstep and share nothing else.
-// Grid: x = sequence * chunks + chunk, y = block of TS head groups.
+// Fixed partitions: the P-token partitions of every sequence are computed
+// alone (so a sequence's result does not depend on the rest of the batch),
+// each by KS waves that split its tiles, one key group each, for each of its
+// head groups.  A workgroup holds NW waves: KS key groups of NW / KS waves,
+// each group NW / KS / TS consecutive partitions x a team of TS adjacent head
+// groups; the team's waves read the same blocks in lockstep.  The key groups'
+// states meet in LDS and the first writes the partition's record (or the
+// output, for a sequence with one partition).  Grid: x = (sequence * chunks +
+// chunk) * (head groups / TS) + block of TS head groups.
 // ============================================================================
 
 template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
 __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(DecodeParams p) {
     constexpr int NW = TU::NW;
+    constexpr int KS = TU::KS;
+    constexpr int NWK = NW / KS;  // waves per key group
     constexpr int NS = A::NS;
     constexpr int DEPTH = TU::DEPTH;
     constexpr int HG = A::HG;
+    using Result = typename A::Result;
+    constexpr int NF = sizeof(Result) / 4;  // floats of one lane's state
     __shared__ __attribute__((aligned(16))) char sm_eng[NW * (A::kLdsBytes > 0 ? A::kLdsBytes : 16)];
+    __shared__ float sm_x[KS > 1 ? (KS - 1) * NWK * NF * kWave : 1];
 
     const int TS = p.team;
-    const int PW = NW / TS;  // partitions per workgroup
+    const int PW = NWK / TS;  // partitions per key group
+    const int NG = p.n_kv_heads / A::NH;
+    const int NGB = NG / TS;
     const int chunks = (p.n_parts_max + PW - 1) / PW;
-    const int s = blockIdx.x / chunks;
+    const int hb = blockIdx.x % NGB;
+    const int sc = blockIdx.x / NGB;
+    const int s = sc / chunks;
     const int w = wave_id_uniform();
-    const int pi = w / TS;
-    const int part = (blockIdx.x - s * chunks) * PW + pi;
-    const int hg = blockIdx.y * TS + (w - pi * TS);  // head group: KV heads hg*NH .. +NH-1
-    const int NG = gridDim.y * TS;
+    const int kg = w / NWK;  // key group
+    const int wl = w - kg * NWK;
+    const int pi = wl / TS;
+    const int part = (sc - s * chunks) * PW + pi;
+    const int hg = hb * TS + (wl - pi * TS);  // head group: KV heads hg*NH .. +NH-1
     const int Hq = p.n_q_heads;
     const int lane = threadIdx.x % kWave;
     char* out_rows = static_cast<char*>(p.out) + ((int64_t)s * Hq + hg * HG) * D * E::kBytes;
@@ -1070,17 +1154,15 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     const int L = min(max(p.context_lens[s], 0), (p.max_blocks << p.block_shift));
     const int P = p.part_tokens;
     const int n_parts = (L + P - 1) / P;
-
-    if (part >= n_parts) {
-        if (L == 0 && part == 0)  // nothing to attend: zero rows
-            for (int i = lane; i < HG * D; i += kWave) E::store(out_rows + i * E::kBytes, 0.f);
-        return;
-    }
+    const bool live = part < n_parts;  // uniform over the wave (not over the workgroup when PW > 1)
+    if (L == 0 && part == 0 && kg == 0)  // nothing to attend: zero rows
+        for (int i = lane; i < HG * D; i += kWave) E::store(out_rows + i * E::kBytes, 0.f);
 
     const int nblk = (L + kBlock - 1) / kBlock;
     const int PB = P / kBlock;
-    const int b_begin = part * PB;
-    const int b_end = min(b_begin + PB, nblk);
+    const int HB = (PB + KS - 1) / KS;  // tiles per key group
+    const int kb0 = part * PB + kg * HB;
+    const int kb1 = live ? min(min(kb0 + HB, part * PB + PB), nblk) : kb0;  // this wave's tiles [kb0, kb1)
     const int tail_rows = L - (nblk - 1) * kBlock;  // valid rows of the last block, 1..16
 
     const uint32_t row_stride = (uint32_t)p.n_kv_heads * A::RB;
@@ -1094,32 +1176,66 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     a.reset();
     bool oks[NS];
     const int ntab = (L + (1 << p.block_shift) - 1) >> p.block_shift;
-    // As in the flat schedule, every pass issues its loads (past the
-    // partition's end, of the first rows of block 0, never computed).
-    auto issue = [&](int slot, int bi, bool real) {
+    // As in the flat schedule: each tile's table entries are read one issue
+    // ahead, and every pass issues its loads (past the range's end, of the
+    // first rows of block 0, never computed).
+    auto fetch = [&](int bi, bool real) {
+        TileEnt e = {0, 0};
+        if (real) e = tile_entries(table, bi, ntab, p.block_shift);
+        return e;
+    };
+    auto issue = [&](int slot, int bi, TileEnt e, bool real) {
         TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
-        if (real) ta = tile_addr(table, bi, ntab, p.block_shift, p.num_blocks, row_stride);
+        if (real) ta = tile_addr_of(e, bi, ntab, p.block_shift, p.num_blocks, row_stride);
         a.template issue<false>(slot, kbase, vbase, ta.lo, ta.hi, -1, kbase, vbase);
         oks[slot] = ta.ok;
     };
 
-    // Block b_begin + k goes through register slot k % NS, DEPTH blocks ahead.
+    // Block kb0 + k goes through register slot k % NS, DEPTH blocks ahead.
+    TileEnt ahead = fetch(kb0, kb0 < kb1);
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) issue(d, b_begin + d, b_begin + d < b_end);
-    for (int bi = b_begin; bi < b_end; bi += NS) {
+    for (int d = 0; d < DEPTH; ++d) {
+        issue(d, kb0 + d, ahead, kb0 + d < kb1);
+        ahead = fetch(kb0 + d + 1, kb0 + d + 1 < kb1);
+    }
+    for (int bi = kb0; bi < kb1; bi += NS) {
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             const int b = bi + u;
-            issue((u + DEPTH) % NS, b + DEPTH, b + DEPTH < b_end);
-            if (b < b_end) {
+            issue((u + DEPTH) % NS, b + DEPTH, ahead, b + DEPTH < kb1);
+            ahead = fetch(b + DEPTH + 1, b + DEPTH + 1 < kb1);
+            if (b < kb1) {
                 const int valid = !oks[u] ? 0 : (b == nblk - 1 ? tail_rows : kBlock);
                 a.process(u, valid, p.scale_log2);
             }
         }
     }
     a.reduce();
-    typename A::Result r;
+    Result r;
     a.take(r);
+    if constexpr (KS > 1) {
+        // key groups 1.. hand their states to group 0 through LDS, lane by lane
+        if (kg > 0) {
+            float f[NF];
+            __builtin_memcpy(f, &r, sizeof(Result));
+            float* x = sm_x + ((kg - 1) * NWK + wl) * NF * kWave;
+#pragma unroll
+            for (int i = 0; i < NF; ++i) x[i * kWave + lane] = f[i];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int k = 1; k < KS; ++k) {
+            const float* x = sm_x + ((k - 1) * NWK + wl) * NF * kWave;
+            float f[NF];
+#pragma unroll
+            for (int i = 0; i < NF; ++i) f[i] = x[i * kWave + lane];
+            Result o;
+            __builtin_memcpy(&o, f, sizeof(Result));
+            A::combine(r, o);
+        }
+    }
+    if (!live) return;
     if (n_parts == 1) {
         a.store_out(r, out_rows);
     } else {  // record [sequence][head group][partition] of [HG][D] acc and [HG][2] (m, l)
@@ -1128,12 +1244,308 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     }
 }
 
-// Fixed partitions: one 256-thread workgroup per (sequence, query head) whose
+// A staged state of HG query heads in LDS: acc [HG][D], (m, l) [HG][2], and
+// three words naming its destination.
+template <int D, int HG>
+struct PartSlot {
+    static constexpr int kFloats = HG * D + 2 * HG + 4;  // + 1 padding keeps slots 16-byte aligned
+};
+constexpr int kPartStaged = 4;
+
+// Fixed partitions, persistent: the same units of work as
+// decode_partition_kernel -- (sequence, partition, block of TS head groups),
+// each split between KS key groups that meet in LDS -- and the same bits, but
+// a grid of the resident workgroups, each taking a balanced contiguous range
+// of units (ordered by sequence, partition, head-group block).  A wave's
+// loads run ahead across unit boundaries, so there is no start-up wait per
+// partition and no loads issued past a short range's end.  Every wave of a
+// workgroup finishes every unit of the range (a key group without tiles in it
+// contributes an empty state), so the barriers of the LDS exchange match.
+// Requires TS == NW / KS.  LDS: the engine areas, the exchange area and the
+// unit prefix over sequences.
+template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
+__global__ __launch_bounds__(TU::NW * kWave) void decode_partition_persistent_kernel(DecodeParams p) {
+    constexpr int NW = TU::NW;
+    constexpr int KS = TU::KS;
+    constexpr int NWK = NW / KS;  // waves per key group = the team
+    constexpr int NS = A::NS;
+    constexpr int DEPTH = TU::DEPTH;
+    constexpr int HG = A::HG;
+    using Result = typename A::Result;
+    constexpr int SLOT = PartSlot<D, HG>::kFloats;  // one staged state: acc, (m, l), destination
+    constexpr int KB = kPartStaged;                  // records a wave stages before writing them
+    extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+    char* sm_eng = dyn_lds;
+    // exchange slots of key groups 1.. (one per wave), then KB staging slots per wave of group 0
+    float* sm_x = reinterpret_cast<float*>(dyn_lds + NW * A::kLdsBytes);
+    float* sm_st = sm_x + (KS - 1) * NWK * SLOT;
+    int32_t* upre = reinterpret_cast<int32_t*>(sm_st + NWK * KB * SLOT);
+
+    const int S = p.num_seqs;
+    const int NG = p.n_kv_heads / A::NH;
+    const int NGB = NG / NWK;
+    const int Hq = p.n_q_heads;
+    const int P = p.part_tokens;
+    const int PB = P / kBlock;
+    const int HB = (PB + KS - 1) / KS;  // tiles per key group of a partition
+    const int max_len = p.max_blocks << p.block_shift;
+    auto seq_len = [&](int s) { return min(max(table_entry(p.context_lens, s), 0), max_len); };
+
+    // units of sequence s: n_parts(s) * NGB; upre[s] = units of sequences < s
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        int carry = 0;
+        for (int base = 0; base < S; base += kWave) {
+            const int i = base + lane;
+            // per-lane index: a vector read (seq_len reads a uniform index with a scalar load)
+            int v = i < S ? ((min(max(p.context_lens[i], 0), max_len) + P - 1) / P) * NGB : 0;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int y = __shfl_up(v, off, kWave);
+                if (lane >= off) v += y;
+            }
+            if (i < S) upre[i + 1] = carry + v;
+            carry += __shfl(v, kWave - 1, kWave);
+        }
+        if (lane == 0) upre[0] = 0;
+    }
+    __syncthreads();
+    // empty sequences: zero rows (workgroups share them out)
+    for (int si = blockIdx.x; si < S; si += gridDim.x)
+        if (upre[si + 1] == upre[si]) {
+            char* o = static_cast<char*>(p.out) + (int64_t)si * Hq * D * E::kBytes;
+            for (int i = threadIdx.x; i < Hq * D; i += blockDim.x) E::store(o + i * E::kBytes, 0.f);
+        }
+    const int U = upre[S];
+    const int u0 = (int)((int64_t)U * blockIdx.x / gridDim.x);
+    const int u1 = (int)((int64_t)U * (blockIdx.x + 1) / gridDim.x);
+    if (u0 >= u1) return;  // uniform over the workgroup
+
+    const int w = wave_id_uniform();
+    const int kg = w / NWK;
+    const int tj = w - kg * NWK;
+    const int lane = threadIdx.x % kWave;
+    const uint32_t row_stride = (uint32_t)p.n_kv_heads * A::RB;
+
+    // Unit cursor: sequence, partition, head-group block, length, and this
+    // wave's tiles [kb0, kb1) of the unit (possibly none).
+    struct UC {
+        int u, s, part, hb, L, kb0, kb1;
+    };
+    auto set_range = [&](UC& c) {
+        const int nblk = (c.L + kBlock - 1) / kBlock;
+        c.kb0 = c.part * PB + kg * HB;
+        c.kb1 = min(min(c.kb0 + HB, c.part * PB + PB), nblk);
+        c.kb1 = max(c.kb1, c.kb0);
+    };
+    auto uniform = [](UC& c) {
+        c.u = __builtin_amdgcn_readfirstlane(c.u);
+        c.s = __builtin_amdgcn_readfirstlane(c.s);
+        c.part = __builtin_amdgcn_readfirstlane(c.part);
+        c.hb = __builtin_amdgcn_readfirstlane(c.hb);
+        c.L = __builtin_amdgcn_readfirstlane(c.L);
+        c.kb0 = __builtin_amdgcn_readfirstlane(c.kb0);
+        c.kb1 = __builtin_amdgcn_readfirstlane(c.kb1);
+    };
+    auto locate = [&](int u) {
+        int lo = 0, hi = S;  // largest s with upre[s] <= u
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (upre[mid] <= u) lo = mid;
+            else hi = mid;
+        }
+        UC c;
+        c.u = u;
+        c.s = lo;
+        c.L = seq_len(lo);
+        const int r = u - upre[lo];
+        c.part = r / NGB;
+        c.hb = r - c.part * NGB;
+        set_range(c);
+        uniform(c);
+        return c;
+    };
+    auto next_unit = [&](UC& c) {
+        ++c.u;
+        if (++c.hb == NGB) {
+            c.hb = 0;
+            ++c.part;
+            if (c.part * P >= c.L) {  // past the sequence: the next one with units
+                c.part = 0;
+                do {
+                    ++c.s;
+                } while (c.s < S && upre[c.s + 1] == upre[c.s]);
+                c.L = c.s < S ? seq_len(c.s) : 0;
+            }
+        }
+        set_range(c);
+        uniform(c);
+    };
+
+    A a;
+    a.init(lane, row_stride, sm_eng + w * A::kLdsBytes);
+    a.reset();
+    bool oks[NS];
+
+    // Issue cursor: (unit, block) over the wave's tiles of units u0 .. u1-1.
+    UC ic = locate(u0);
+    int ib = ic.kb0;
+    auto skip_empty = [&]() {  // move to the first unit with a tile for this wave, if any
+        while (ib >= ic.kb1 && ic.u < u1 - 1) {
+            next_unit(ic);
+            ib = ic.kb0;
+        }
+    };
+    skip_empty();
+    int q_s = -1, q_hb = -1;  // the (sequence, head-group block) whose q rows the last issued tile loaded
+    auto issue = [&](int slot) {
+        const bool real = ib < ic.kb1;
+        TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
+        int64_t hoff = 0;
+        if (real) {
+            const int hg = ic.hb * NWK + tj;
+            hoff = (int64_t)hg * A::NH * A::RB;
+            if (ic.s != q_s || ic.hb != q_hb) {
+                q_s = ic.s;
+                q_hb = ic.hb;
+                a.load_q_slot(slot, static_cast<const char*>(p.q) + ((int64_t)ic.s * Hq + hg * HG) * A::RB);
+            }
+            const int ntab = (ic.L + (1 << p.block_shift) - 1) >> p.block_shift;
+            ta = tile_addr(p.block_tables + (int64_t)ic.s * p.max_blocks, ib, ntab, p.block_shift, p.num_blocks,
+                           row_stride);
+        }
+        const char* kb = static_cast<const char*>(p.k_cache) + hoff;
+        const char* vb = static_cast<const char*>(p.v_cache) + hoff;
+        a.template issue<false>(slot, kb, vb, ta.lo, ta.hi, -1, kb, vb);
+        oks[slot] = ta.ok;
+        if (real) {
+            ++ib;
+            skip_empty();
+        }
+    };
+
+    // Processing cursor and the unit being accumulated.
+    UC pc = locate(u0);
+    int pb = pc.kb0;
+    int cu = u0;  // the next unit to finish
+    int cq_s = -1, cq_hb = -1;
+
+    // Finished records wait in LDS (KB per wave of key group 0) and are written
+    // together: a store is counted with the loads in flight, and under the
+    // read traffic its acknowledgement takes longer than a tile, so every wait
+    // after it would stall.  Slot: acc [HG][D], (m, l) [HG][2], then the
+    // destination (kind, record index low and high words).
+    int nst = 0;
+    const float* const xs_own = sm_x + ((kg > 0 ? kg - 1 : 0) * NWK + tj) * SLOT;
+    float* const st_own = sm_st + tj * KB * SLOT;
+    auto lds_sync_wave = []() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto flush = [&]() {
+        lds_sync_wave();
+        for (int b = 0; b < nst; ++b) {
+            const float* sl = st_own + b * SLOT;
+            const int kind = __builtin_amdgcn_readfirstlane(__float_as_int(sl[SLOT - 3]));
+            const uint32_t lo = __builtin_amdgcn_readfirstlane(__float_as_uint(sl[SLOT - 2]));
+            const uint32_t hi = __builtin_amdgcn_readfirstlane(__float_as_uint(sl[SLOT - 1]));
+            const int64_t dst = (int64_t)(((uint64_t)hi << 32) | lo);
+            if (kind == 0) {  // a record: acc rows and (m, l)
+                // Nontemporal stores: under the read traffic they are acknowledged
+                // sooner (measured: 512-token partitions of the long-context
+                // layer 5.74 -> 6.12 TB/s), at the price of the merge reading the
+                // records from memory rather than from cache.
+                float* ra = p.ws_acc + dst * HG * D;
+                for (int i = lane * 4; i < HG * D; i += kWave * 4) {
+                    const v4u32_t v = *reinterpret_cast<const v4u32_t*>(sl + i);
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4u32_t*>(ra + i));
+                }
+                if (lane < 2 * HG) p.ws_ml[dst * HG * 2 + lane] = sl[HG * D + lane];
+            } else {  // a sequence with one partition: the normalised output rows
+                char* o = static_cast<char*>(p.out) + dst * D * E::kBytes;
+                for (int i = lane; i < HG * D; i += kWave) E::store(o + i * E::kBytes, sl[i] / sl[HG * D + (i / D) * 2 + 1]);
+            }
+        }
+        nst = 0;
+    };
+
+    // Finish unit cu: combine the key groups' states and stage its record.
+    auto finish = [&]() {
+        a.reduce();
+        Result r;
+        a.take(r);
+        if constexpr (KS > 1) {
+            if (kg > 0) a.stage(r, const_cast<float*>(xs_own));
+            __syncthreads();
+            if (kg == 0) {
+#pragma unroll
+                for (int k = 1; k < KS; ++k) {
+                    Result o;
+                    a.unstage(sm_x + ((k - 1) * NWK + tj) * SLOT, o);
+                    A::combine(r, o);
+                }
+            }
+            __syncthreads();  // the exchange slots are free again
+        }
+        if (kg == 0) {
+            // pc is still at unit cu here (it moves on after finish)
+            const int hg = pc.hb * NWK + tj;
+            const int n_parts = (pc.L + P - 1) / P;
+            float* sl = st_own + nst * SLOT;
+            a.stage(r, sl);
+            const int64_t dst = n_parts == 1 ? (int64_t)pc.s * Hq + hg * HG
+                                             : ((int64_t)pc.s * NG + hg) * p.n_parts_max + pc.part;
+            if (lane == 0) {
+                sl[SLOT - 3] = __int_as_float(n_parts == 1 ? 1 : 0);
+                sl[SLOT - 2] = __uint_as_float((uint32_t)(uint64_t)dst);
+                sl[SLOT - 1] = __uint_as_float((uint32_t)((uint64_t)dst >> 32));
+            }
+            if (++nst == KB) flush();
+        }
+        a.reset();
+        ++cu;
+        if (cu < u1) {
+            next_unit(pc);
+            pb = pc.kb0;
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d);
+    // Each pass processes one tile of this wave (after finishing the units
+    // that precede it), or, once the tiles are done, finishes the rest.
+    bool more = true;
+    while (more) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            issue((u + DEPTH) % NS);
+            // units with no tile left for this wave are finished first
+            while (cu < u1 && pb >= pc.kb1) finish();
+            if (cu < u1) {
+                if (pc.s != cq_s || pc.hb != cq_hb) {
+                    cq_s = pc.s;
+                    cq_hb = pc.hb;
+                    a.take_q(u);
+                }
+                const int nblk = (pc.L + kBlock - 1) / kBlock;
+                const int valid = !oks[u] ? 0 : (pb == nblk - 1 ? pc.L - (nblk - 1) * kBlock : kBlock);
+                a.process(u, valid, p.scale_log2);
+                ++pb;
+            } else {
+                more = false;
+            }
+        }
+    }
+    if (kg == 0 && nst > 0) flush();
+}
+
+// Fixed partitions: one 512-thread workgroup per (sequence, query head) whose
 // sequence has >= 2 partitions.  A long sequence has hundreds of records, so
 // the workgroup reads RS records side by side (thread t owns float4 column
-// t % VPR of record slot t / VPR), UNROLL deep, and the slots' partial sums
-// meet in LDS.
-constexpr int kMergeThreads = 256;
+// t % VPR of record slot t / VPR), UNROLL deep (128 records of D = 128 in
+// flight), and the slots' partial sums meet in LDS.
+constexpr int kMergeThreads = 512;
 
 template <class E, int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
@@ -1141,7 +1553,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     constexpr int NWV = NT / kWave;
     constexpr int VPR = D / 4;    // float4 columns of a record row
     constexpr int RS = NT / VPR;  // record slots
-    constexpr int UNROLL = 4;
+    constexpr int UNROLL = 8;
     __shared__ float sm_max[NWV], sm_den[NWV];
     __shared__ __attribute__((aligned(16))) float4 sm_num[RS][VPR];
 
@@ -1255,7 +1667,9 @@ struct DefaultTune {
     // SIMD) streams 2-3 % faster than the two waves per SIMD that fit
     using valu = typename std::conditional<kNH == 2, Tune<4, kR, 1, true, false, 2, 1>, Tune<4, kRf, 1, true, false, 1>>::type;
     using type = typename std::conditional<kMfma, mfma_flat, valu>::type;
-    using parts = typename std::conditional<kMfma, Tune<8, 8, 2, true, true, 1, 0, 8>, valu>::type;
+    // fixed partitions: a partition's tiles split between two key groups, each
+    // a team of four KV heads (the tail of a grid of equal partitions is half as long)
+    using parts = typename std::conditional<kMfma, Tune<8, 8, 1, true, true, 1, 0, 4, 2>, valu>::type;
     using NH1 = Tune<4, kMfma ? 8 : kRf, 1, true, kMfma, 1>;
 };
 
@@ -1274,16 +1688,68 @@ static int flat_team_t(int n_kv_heads) {
                                                             : team_size<TU1>(n_kv_heads);
 }
 
+// Fixed partitions, one workgroup per (partition, team) (p.team set).
+template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
+hipError_t launch_parts_fallback(const DecodeParams& p, hipStream_t stream) {
+    const int ng = p.n_kv_heads / A::NH;
+    const int pw = TU::NW / TU::KS / p.team;  // partitions per key group
+    const int64_t chunks = (p.n_parts_max + pw - 1) / pw;
+    const int64_t wgs = chunks * p.num_seqs * (ng / p.team);
+    if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU, A>), dim3((unsigned)wgs), dim3(TU::NW * kWave), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
+hipError_t launch_parts_persistent(const DecodeParams& pin, hipStream_t stream);
+
+// Largest LDS the persistent partition kernel asks for (beyond it, the batch
+// has too many sequences for the unit prefix and the one-launch-per-partition
+// kernel runs instead; both give the same bits).
+constexpr size_t kMaxPersistentLds = 160 * 1024;
+
 template <class E, int D, int G, class TU, class A = Engine<E, D, G, TU>>
 hipError_t launch_parts_tuned(const DecodeParams& pin, hipStream_t stream) {
     DecodeParams p = pin;
     p.heads_per_wave = A::NH;
     const int ng = p.n_kv_heads / A::NH;
     p.team = team_size<TU>(ng);
-    const int64_t chunks = (p.n_parts_max + TU::NW / p.team - 1) / (TU::NW / p.team);
-    if (chunks * p.num_seqs > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(chunks * p.num_seqs), ng / p.team);
-    hipLaunchKernelGGL((decode_partition_kernel<E, D, G, TU, A>), grid, dim3(TU::NW * kWave), 0, stream, p);
+    // The persistent kernel when the team fills a key group.
+    if constexpr (TU::KS > 1)
+        if (p.team == TU::NW / TU::KS) return launch_parts_persistent<E, D, G, TU, A>(p, stream);
+    return launch_parts_fallback<E, D, G, TU, A>(p, stream);
+}
+
+// One workgroup per resident slot on the device (at most one per unit of work).
+template <class E, int D, int G, class TU, class A>
+hipError_t launch_parts_persistent(const DecodeParams& p, hipStream_t stream) {
+    auto kern = decode_partition_persistent_kernel<E, D, G, TU, A>;
+    constexpr size_t slot = (size_t)PartSlot<D, A::HG>::kFloats * 4;
+    const size_t lds = (size_t)TU::NW * A::kLdsBytes + (size_t)(TU::KS - 1) * (TU::NW / TU::KS) * slot +
+                       (size_t)(TU::NW / TU::KS) * kPartStaged * slot + (size_t)(p.num_seqs + 1) * sizeof(int32_t);
+    if (lds > kMaxPersistentLds) return launch_parts_fallback<E, D, G, TU, A>(p, stream);
+    static thread_local int cached_dev = -1, cached_per_cu = 0, cached_cus = 0;
+    static thread_local size_t cached_lds = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev != cached_dev || lds != cached_lds) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, TU::NW * kWave, lds);
+        if (e != hipSuccess) return e;
+        cached_dev = dev;
+        cached_lds = lds;
+        cached_cus = cus;
+        cached_per_cu = per_cu < 1 ? 1 : per_cu;
+    }
+    const int64_t units = (int64_t)p.num_seqs * p.n_parts_max * (p.n_kv_heads / A::NH / p.team);
+    int64_t wgs = (int64_t)cached_cus * cached_per_cu;
+    if (wgs > units) wgs = units;
+    if (wgs < 1) wgs = 1;
+    hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(TU::NW * kWave), lds, stream, p);
     return hipGetLastError();
 }
 

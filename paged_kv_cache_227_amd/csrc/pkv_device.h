@@ -86,6 +86,9 @@ struct F32 {
     __device__ static __forceinline__ void store(void* p, float x) {
         *reinterpret_cast<float*>(p) = x;
     }
+    __device__ static __forceinline__ uint32_t bits(float x) {
+        return __float_as_uint(x);
+    }
 };
 
 struct F16 {
@@ -110,6 +113,9 @@ struct F16 {
     __device__ static __forceinline__ void store(void* p, float x) {
         *reinterpret_cast<_Float16*>(p) = (_Float16)x;  // v_cvt_f16_f32 rounds to nearest even
     }
+    __device__ static __forceinline__ uint32_t bits(float x) {  // the rounded value's 16 bits
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
 };
 
 struct BF16 {
@@ -133,7 +139,21 @@ struct BF16 {
     __device__ static __forceinline__ void store(void* p, float x) {
         *reinterpret_cast<__bf16*>(p) = (__bf16)x;  // round to nearest even
     }
+    __device__ static __forceinline__ uint32_t bits(float x) {
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    }
 };
+
+// Four consecutive elements, each rounded like E::store, in one store (8 bytes
+// for 16-bit types, 16 for fp32; p aligned accordingly).
+template <class E>
+__device__ __forceinline__ void store4(char* p, float a, float b, float c, float d) {
+    if constexpr (E::kBytes == 2) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(E::bits(a) | (E::bits(b) << 16), E::bits(c) | (E::bits(d) << 16));
+    } else {
+        *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+    }
+}
 
 // ---- cross-lane helpers ------------------------------------------------------
 
