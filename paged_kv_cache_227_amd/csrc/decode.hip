@@ -149,8 +149,11 @@ struct WaveAttn {
 
     // The flat schedule loads the q rows of a segment's pair into the slot of
     // the segment's first tile, right before that tile's K/V loads, so the
-    // wait for the tile covers them; take_q makes them current.
-    Vec16 qs[NS][G][CPL];
+    // wait for the tile covers them; take_q makes them current.  Only when the
+    // extra q sets are few registers (kQAhead); otherwise q is loaded where a
+    // segment starts, and waited for there.
+    static constexpr bool kQAhead = NS * G * CPL * 4 <= 32;
+    Vec16 qs[kQAhead ? NS : 1][G][CPL];
     __device__ __forceinline__ void load_q_slot(int slot, const char* q_rows) {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi)
@@ -458,7 +461,8 @@ struct MfmaAttn {
     }
 
     // As in WaveAttn: a segment's q rows ride in the slot of its first tile.
-    Vec16 qs[NS][NH][KK];
+    static constexpr bool kQAhead = NS * NH * KK * 4 <= 32;
+    Vec16 qs[kQAhead ? NS : 1][NH][KK];
     __device__ __forceinline__ void load_q_slot(int slot, const char* q_rows) {
 #pragma unroll
         for (int h = 0; h < NH; ++h)
@@ -730,6 +734,64 @@ __device__ __forceinline__ TileAddr tile_addr(const int32_t* table, int t, int n
 }
 
 // ============================================================================
+// Staged results.  A finished piece of work (the state of HG query heads) can
+// wait in LDS and be written later with the others: a store is counted with
+// the loads in flight, and under the read traffic its acknowledgement takes
+// longer than a tile, so every wait after a store in the tile loop stalls.
+// Slot: acc [HG][D], (m, l) [HG][2], then the destination: kind (0: a partial
+// record at index dst, 1: normalised output rows from row dst), dst low and
+// high words, one word of padding (slots stay 16-byte aligned).
+// ============================================================================
+
+template <int D, int HG>
+struct StageSlot {
+    static constexpr int kFloats = HG * D + 2 * HG + 4;
+};
+constexpr int kPartStaged = 4;  // slots per wave of the fixed-partition kernel
+
+__device__ __forceinline__ void stage_header(float* slot, int nfloats, bool out_rows, int64_t dst) {
+    if (threadIdx.x % kWave == 0) {
+        slot[nfloats - 3] = __int_as_float(out_rows ? 1 : 0);
+        slot[nfloats - 2] = __uint_as_float((uint32_t)(uint64_t)dst);
+        slot[nfloats - 1] = __uint_as_float((uint32_t)((uint64_t)dst >> 32));
+    }
+}
+
+// Write n staged slots (one wave).  Records go out with nontemporal stores
+// (acknowledged sooner under the read traffic); output rows are rounded to
+// the cache type, four elements a store.
+template <class E, int D, int HG>
+__device__ __forceinline__ void write_staged(const float* slots, int n, const DecodeParams& p) {
+    constexpr int SLOT = StageSlot<D, HG>::kFloats;
+    const int lane = threadIdx.x % kWave;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the slots were written by other lanes
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int b = 0; b < n; ++b) {
+        const float* sl = slots + b * SLOT;
+        const int kind = __builtin_amdgcn_readfirstlane(__float_as_int(sl[SLOT - 3]));
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(__float_as_uint(sl[SLOT - 2]));
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(__float_as_uint(sl[SLOT - 1]));
+        const int64_t dst = (int64_t)(((uint64_t)hi << 32) | lo);
+        if (kind == 0) {
+            float* ra = p.ws_acc + dst * HG * D;
+            for (int i = lane * 4; i < HG * D; i += kWave * 4) {
+                const v4u32_t v = *reinterpret_cast<const v4u32_t*>(sl + i);
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u32_t*>(ra + i));
+            }
+            if (lane < 2 * HG) p.ws_ml[dst * HG * 2 + lane] = sl[HG * D + lane];
+        } else {
+            char* o = static_cast<char*>(p.out) + dst * D * E::kBytes;
+            for (int i = lane * 4; i < HG * D; i += kWave * 4) {
+                const float inv = 1.f / sl[HG * D + (i / D) * 2 + 1];  // D is a multiple of 4
+                const float4 v = *reinterpret_cast<const float4*>(sl + i);
+                store4<E>(o + i * E::kBytes, v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+            }
+        }
+    }
+}
+
+// ============================================================================
 // Flat schedule: a persistent grid deals equal ranges of the tile stream.
 // ============================================================================
 
@@ -867,10 +929,13 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     // being computed also wait for the tiles issued after it.
     int qs_s = -1, qs_k = -1;  // pair of the last tile issued
     auto issue = [&](int slot, const Cur& q, const Ahead& f, bool real) {
-        if (real && (q.s != qs_s || q.kvh != qs_k)) {  // the first tile of a segment carries its q rows
-            qs_s = q.s;
-            qs_k = q.kvh;
-            a.load_q_slot(slot, static_cast<const char*>(p.q) + ((int64_t)q.s * Hq + (q.kvh * TS + tj) * A::HG) * A::RB);
+        if constexpr (A::kQAhead) {
+            if (real && (q.s != qs_s || q.kvh != qs_k)) {  // the first tile of a segment carries its q rows
+                qs_s = q.s;
+                qs_k = q.kvh;
+                a.load_q_slot(slot,
+                              static_cast<const char*>(p.q) + ((int64_t)q.s * Hq + (q.kvh * TS + tj) * A::HG) * A::RB);
+            }
         }
         TileAddr ta = {0, -kDummyRows * (int64_t)row_stride, false};
         if (real) {
@@ -960,7 +1025,12 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
                     as = cur.s;
                     akvh = cur.kvh;
                     aL = cur.L;
-                    a.take_q(u);
+                    if constexpr (A::kQAhead) {
+                        a.take_q(u);
+                    } else {
+                        a.load_q(static_cast<const char*>(p.q) + ((int64_t)as * Hq + (akvh * TS + tj) * A::HG) * A::RB);
+                        a.settle_q();  // here, not at the next product, where it would also wait for the next tiles
+                    }
                     a.reset();
                 }
                 const int valid = !oks[u] ? 0 : (cur.b == cur.nb - 1 ? cur.L - cur.b * kBlock : kBlock);
@@ -1244,14 +1314,6 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_kernel(Decode
     }
 }
 
-// A staged state of HG query heads in LDS: acc [HG][D], (m, l) [HG][2], and
-// three words naming its destination.
-template <int D, int HG>
-struct PartSlot {
-    static constexpr int kFloats = HG * D + 2 * HG + 4;  // + 1 padding keeps slots 16-byte aligned
-};
-constexpr int kPartStaged = 4;
-
 // Fixed partitions, persistent: the same units of work as
 // decode_partition_kernel -- (sequence, partition, block of TS head groups),
 // each split between KS key groups that meet in LDS -- and the same bits, but
@@ -1272,7 +1334,8 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_persistent_ke
     constexpr int DEPTH = TU::DEPTH;
     constexpr int HG = A::HG;
     using Result = typename A::Result;
-    constexpr int SLOT = PartSlot<D, HG>::kFloats;  // one staged state: acc, (m, l), destination
+    static_assert(A::kQAhead, "a unit's q rows ride in the slot of its first tile");
+    constexpr int SLOT = StageSlot<D, HG>::kFloats;  // one staged state: acc, (m, l), destination
     constexpr int KB = kPartStaged;                  // records a wave stages before writing them
     extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
     char* sm_eng = dyn_lds;
@@ -1431,42 +1494,12 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_persistent_ke
     int cq_s = -1, cq_hb = -1;
 
     // Finished records wait in LDS (KB per wave of key group 0) and are written
-    // together: a store is counted with the loads in flight, and under the
-    // read traffic its acknowledgement takes longer than a tile, so every wait
-    // after it would stall.  Slot: acc [HG][D], (m, l) [HG][2], then the
-    // destination (kind, record index low and high words).
+    // together (see write_staged).
     int nst = 0;
     const float* const xs_own = sm_x + ((kg > 0 ? kg - 1 : 0) * NWK + tj) * SLOT;
     float* const st_own = sm_st + tj * KB * SLOT;
-    auto lds_sync_wave = []() {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
     auto flush = [&]() {
-        lds_sync_wave();
-        for (int b = 0; b < nst; ++b) {
-            const float* sl = st_own + b * SLOT;
-            const int kind = __builtin_amdgcn_readfirstlane(__float_as_int(sl[SLOT - 3]));
-            const uint32_t lo = __builtin_amdgcn_readfirstlane(__float_as_uint(sl[SLOT - 2]));
-            const uint32_t hi = __builtin_amdgcn_readfirstlane(__float_as_uint(sl[SLOT - 1]));
-            const int64_t dst = (int64_t)(((uint64_t)hi << 32) | lo);
-            if (kind == 0) {  // a record: acc rows and (m, l)
-                // Nontemporal stores: under the read traffic they are acknowledged
-                // sooner (measured: 512-token partitions of the long-context
-                // layer 5.74 -> 6.12 TB/s), at the price of the merge reading the
-                // records from memory rather than from cache.
-                float* ra = p.ws_acc + dst * HG * D;
-                for (int i = lane * 4; i < HG * D; i += kWave * 4) {
-                    const v4u32_t v = *reinterpret_cast<const v4u32_t*>(sl + i);
-                    __builtin_nontemporal_store(v, reinterpret_cast<v4u32_t*>(ra + i));
-                }
-                if (lane < 2 * HG) p.ws_ml[dst * HG * 2 + lane] = sl[HG * D + lane];
-            } else {  // a sequence with one partition: the normalised output rows
-                char* o = static_cast<char*>(p.out) + dst * D * E::kBytes;
-                for (int i = lane; i < HG * D; i += kWave) E::store(o + i * E::kBytes, sl[i] / sl[HG * D + (i / D) * 2 + 1]);
-            }
-        }
+        write_staged<E, D, HG>(st_own, nst, p);
         nst = 0;
     };
 
@@ -1496,11 +1529,7 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_partition_persistent_ke
             a.stage(r, sl);
             const int64_t dst = n_parts == 1 ? (int64_t)pc.s * Hq + hg * HG
                                              : ((int64_t)pc.s * NG + hg) * p.n_parts_max + pc.part;
-            if (lane == 0) {
-                sl[SLOT - 3] = __int_as_float(n_parts == 1 ? 1 : 0);
-                sl[SLOT - 2] = __uint_as_float((uint32_t)(uint64_t)dst);
-                sl[SLOT - 1] = __uint_as_float((uint32_t)((uint64_t)dst >> 32));
-            }
+            stage_header(sl, SLOT, n_parts == 1, dst);
             if (++nst == KB) flush();
         }
         a.reset();
@@ -1725,7 +1754,7 @@ hipError_t launch_parts_tuned(const DecodeParams& pin, hipStream_t stream) {
 template <class E, int D, int G, class TU, class A>
 hipError_t launch_parts_persistent(const DecodeParams& p, hipStream_t stream) {
     auto kern = decode_partition_persistent_kernel<E, D, G, TU, A>;
-    constexpr size_t slot = (size_t)PartSlot<D, A::HG>::kFloats * 4;
+    constexpr size_t slot = (size_t)StageSlot<D, A::HG>::kFloats * 4;
     const size_t lds = (size_t)TU::NW * A::kLdsBytes + (size_t)(TU::KS - 1) * (TU::NW / TU::KS) * slot +
                        (size_t)(TU::NW / TU::KS) * kPartStaged * slot + (size_t)(p.num_seqs + 1) * sizeof(int32_t);
     if (lds > kMaxPersistentLds) return launch_parts_fallback<E, D, G, TU, A>(p, stream);
