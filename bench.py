@@ -79,6 +79,18 @@ def make_workload(name):
     return W.CONFIGS[name]()
 
 
+def decode_kernel_name(w, part):
+    """The partition-pass kernel that runs for this workload: the flat schedule,
+    or fixed partitions (persistent workgroups for the matrix-core shapes whose
+    KV heads form teams of four)."""
+    if part == 0:
+        return "decode_flat_kernel"
+    g = w.n_q_heads // w.n_kv_heads
+    if w.dtype in ("f16", "bf16") and g >= 4 and w.n_kv_heads % 4 == 0:
+        return "decode_partition_persistent_kernel"
+    return "decode_partition_kernel"
+
+
 def with_schedule(w, schedule):
     """The workload as given ("workload": its own partition length, if it fixes
     one), or under the library's default schedule ("default"), then named
@@ -167,8 +179,7 @@ def run_gpu(w, steps, warmup, extras, graph=False):
     t_app = [e[0].elapsed_time(e[1]) for e in events]
     t_part = [e[1].elapsed_time(e[2]) for e in events]
     t_merge = [e[2].elapsed_time(e[3]) for e in events]
-    res = dict(ms_per_step=ms_step, part_tokens=part, **res_graph,
-               kernel="decode_flat_kernel" if part == 0 else "decode_partition_kernel",
+    res = dict(ms_per_step=ms_step, part_tokens=part, **res_graph, kernel=decode_kernel_name(w, part),
                partition_ms_mean=statistics.fmean(t_part), partition_ms_median=statistics.median(t_part),
                partition_ms_p10=sorted(t_part)[len(t_part) // 10],
                partition_ms_p90=sorted(t_part)[(len(t_part) * 9) // 10],
@@ -306,7 +317,7 @@ def measure_side_configs(iters, flush_bytes=2 << 30):
         kv = w.kv_read_bytes()
         kms = statistics.fmean(t_k)
         gbs = kv / (kms * 1e-3) / 1e9
-        kernel = "decode_flat_kernel" if part == 0 else "decode_partition_kernel"
+        kernel = decode_kernel_name(w, part)
         row = {"label": label, "workload": name, "kernel": kernel, "partition_tokens": part, "dtype": w.dtype,
                "num_seqs": w.num_seqs, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                "kv_read_bytes": kv, "mean_launch_ms": round(kms, 5),
@@ -411,14 +422,20 @@ def run_copy(cw, steps, warmup):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    # per-launch HIP events, each launch after a 2 GiB copy: a small copy workload's
+    # rows would otherwise stay in the L2s from the call before, and the rate
+    # would not be an HBM one
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e in ev:
+        P.probe_copy(buf[:1 << 30], buf[1 << 30:])
         e[0].record()
         step()
         e[1].record()
     torch.cuda.synchronize()
     t = [a.elapsed_time(b) for a, b in ev]
-    del kc, vc
+    del kc, vc, buf
     torch.cuda.empty_cache()
     return dict(ms_per_step=ms_step, kernel_ms_mean=statistics.fmean(t), kernel_ms_median=statistics.median(t))
 
@@ -469,7 +486,8 @@ def main_copy(a):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "copy_blocks_kernel",
                      "algorithmic_bytes_per_launch": moved,
-                     "timing": "HIP events around each launch, %d calls right after the timed region" % a.steps,
+                     "timing": "HIP events around each of %d launches right after the timed region, each after "
+                               "a 2 GiB cache-evicting copy" % a.steps,
                      "mean_launch_ms": round(g["kernel_ms_mean"], 5)},
         "us_per_call": round(g["ms_per_step"] * 1e3, 2),
     }
@@ -745,6 +763,8 @@ def write_traffic(fetch_dir, write_dir, config, kv_bytes, copy_bytes, out_path, 
 
     def pick(d, key):
         names = [n for n in d if key in n]
+        if len(names) > 1:  # the flat kernel with and without a fused append: the plain one
+            names = [n for n in names if ">, false, " in n]
         if len(names) != 1:
             raise SystemExit("expected one kernel matching %r, found %r" % (key, names))
         return d[names[0]], names[0]
@@ -821,7 +841,7 @@ def main():
             w = with_schedule(make_workload(a.config), a.schedule)
             t = write_traffic(a.write_traffic[0], a.write_traffic[1], w.name, w.kv_read_bytes(),
                               a.copy_probe_bytes // 16 * 16, TRAFFIC_FILE.format(config=w.name),
-                              "decode_partition_kernel" if w.part_tokens else "decode_flat_kernel")
+                              decode_kernel_name(w, w.part_tokens))
         print(json.dumps(t, indent=1))
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
