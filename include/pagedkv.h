@@ -187,12 +187,14 @@ pkv_status paged_kv_append_tokens(const void* k_new, const void* v_new, void* k_
  *   q, out        [total][n_q_heads][head_dim], element type layout->dtype
  *   cu_q          [num_seqs + 1] int32 device array
  *   context_lens  [num_seqs] int32: n <= L <= max_blocks_per_seq * block_size
- *   max_q_len     host int: the longest chunk (sizes the grid); rows of a
- *                 longer chunk are not computed
+ *   max_q_len     host int: the longest chunk (sizes the grid); a longer
+ *                 chunk gets the rows of its first max_q_len tokens, the rest
+ *                 of out is left as it was
  *
  * Supported: fp16 / bf16 caches, block_size 8, 16, 32 or 64, head_dim 64 or
- * 128, group 1, 2, 4 or 8, num_seqs <= 65535 and max_q_len x group <= 65535 x 128 query
- * rows (PKV_ENOTSUP otherwise; fp32 prefill is not served).  A sequence whose
+ * 128, group 1, 2, 4 or 8, num_seqs <= 65535, max_q_len x group <= 65535 x 128 query
+ * rows, num_seqs x ceil(max_q_len x group / 128) < 2^31 and n_kv_heads x
+ * num_seqs < 2^23 (PKV_ENOTSUP otherwise; fp32 prefill is not served).  A sequence whose
  * chunk is empty or longer than its context is skipped.
  * pkv_validate_prefill() checks cu_q, the lengths and the tables on the host.
  */

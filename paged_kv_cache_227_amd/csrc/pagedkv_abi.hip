@@ -393,6 +393,13 @@ pkv_status paged_attention_prefill(const void* q, const void* k_cache, const voi
         return fail(PKV_ENOTSUP, "max_q_len %d x group %d exceeds %lld query rows", max_q_len, group,
                     (long long)(pkv::kMaxPrefillTiles * pkv::kPrefillRows));
     if (num_seqs == 0 || max_q_len == 0) return ok();
+    {
+        // the grid: (KV heads x sequences, tiles), 512 threads per workgroup
+        const int64_t tiles = ((int64_t)max_q_len * group + pkv::kPrefillRows - 1) / pkv::kPrefillRows;
+        if (tiles * num_seqs > INT32_MAX || (int64_t)layout->n_kv_heads * num_seqs * 512 > UINT32_MAX)
+            return fail(PKV_ENOTSUP, "prefill grid too large: %d sequences x %lld tiles x %d KV heads", num_seqs,
+                        (long long)tiles, layout->n_kv_heads);
+    }
     pkv::PrefillParams p{};
     p.q = q;
     p.k_cache = k_cache;

@@ -17,33 +17,30 @@
 // (n x G query rows against every key), so the work runs on the matrix cores.
 // A query row is one (chunk token, head of the KV head's group) pair; rows of
 // one (sequence, KV head) are ordered token-major.  A workgroup holds one tile
-// of NW x 16 x NQ consecutive rows, in KS key groups of NW waves:
-//   * each key group takes its share of the tile's key iterations; an
-//     iteration's K and V tiles (NB blocks) are loaded once per group (the
-//     table entries first, then every 16-byte load in flight at once, one
-//     iteration ahead of the compute) and stored in LDS, double-buffered,
-//     16-byte chunks XOR-swizzled by row;
-//   * each wave owns NQ groups of 16 rows.  Per block and group:
-//       S^T = K Q^T   (v_mfma_f32_16x16x32, K from LDS as the A operand, the
-//                      group's q rows as B, held in registers),
-//     the prefix-causal mask (key position <= the row's position) entering as
-//     the products' initial value (0 or -inf) in the steps that need it, an
-//     online softmax per row in base-2 units with a lazily moved reference
-//     maximum (each row's state lives in one lane column), then, for each
-//     pair of blocks,
-//       O^T += V^T P^T (v_mfma_f32_16x16x32, V^T read transposed from LDS,
-//                      P^T straight from S^T's accumulator layout; the two
-//                      blocks' 4-key lane slices make the 8 contraction slots),
-//     with P split into high and low 16-bit parts for bf16 so about 16 bits of
-//     each weight survive;
+// of 128 consecutive rows in two key groups of four waves, 32 rows per wave:
+//   * tiles are launched longest first (by the position of their last row),
+//     so that the compute units take the long tiles at once and the short
+//     ones fill in behind them;
+//   * each key group takes half of the tile's key iterations (64 keys each),
+//     whose K and V tiles go from memory straight into LDS (two buffers for
+//     K, two for V, 16-byte chunks XOR-swizzled by row);
+//   * an iteration is two phases between workgroup barriers: M, all matrix
+//     products (S^T = K Q^T of this iteration, O^T += V^T P^T of the one
+//     before, v_mfma_f32_16x16x32), and V, all vector work (the online softmax
+//     per row in base-2 units with a lazily moved reference maximum, the
+//     prefix-causal mask having entered the score products as their initial
+//     value); group 1 runs one phase behind group 0 and each SIMD holds one
+//     wave of each, so one wave's products overlap the other's softmax;
+//   * the row sums come from the matrix core too, from the same rounded
+//     weights as the outputs;
 //   * the key groups' softmax states meet in LDS at the end (the decode merge's
-//     rule), and group 0 writes the rows;
-//   * iterations wholly past a wave's last position are skipped by that wave.
+//     rule), and group 0 writes the rows.
 // Rows past L in a sequence's last block are loaded as zeros, so whatever
 // those slots hold never reaches the output.
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -100,26 +97,37 @@ hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream)
 
 // ---- attention ---------------------------------------------------------------
 
-template <class E, int D, int G, int NW, int NQ, int NB, int KS>
+// Shape of the attention workgroup: a tile of kPrefillRows query rows of one
+// (sequence, KV head) in KS = 2 key groups of NW_ row waves; each wave owns
+// NQ_ groups of 16 rows; an iteration covers NB = 4 blocks (64 keys).
+template <int D, int NW_, int NQ_>
 struct PrefillShape {
-    static constexpr int RB = D * 2;            // bytes per head row
-    static constexpr int CH = RB / 16;          // 16-byte chunks per head row
-    static constexpr int KK = D / 32;           // 16x16x32 products per score tile
-    static constexpr int TT = D / 16;           // 16-wide output tiles
-    static constexpr int ROWS_W = 16 * NQ;      // query rows per wave
-    static constexpr int ROWS = NW * ROWS_W;    // query rows per workgroup
-    static constexpr int TILE = kBlock * RB;    // bytes of one block's K (or V) rows of one head
-    static constexpr int SPAN = NB * TILE;      // bytes of an iteration's K (or V) rows
-    static constexpr int BUF_BYTES = KS * 2 * SPAN;      // one buffer: [group][K, V] tiles
-    static constexpr int STATE = TT * 4 + 2;             // floats of one lane's row state (acc, m, l)
-    // Group 1's states go to the two (by then idle) buffers, half each, when
-    // they fit there, else to an array of their own.
-    static constexpr int STATE_A = (STATE + 1) / 2;      // floats in the first buffer
-    static constexpr bool STATE_IN_BUFFERS = KS > 1 && NW * NQ * STATE_A * kWave * 4 <= BUF_BYTES;
-    static constexpr int MERGE_BYTES = KS > 1 && !STATE_IN_BUFFERS ? NW * NQ * STATE * kWave * 4 : 16;
-    static_assert(E::kBytes == 2 && D % 32 == 0 && CH == 4 * KK, "16-bit caches, head_dim a multiple of 32");
-    static_assert(NB % 2 == 0, "PV takes blocks in pairs");
-    static_assert(KS == 1 || KS == 2, "one or two key groups");
+    static constexpr int NW = NW_;               // row waves per key group
+    static constexpr int NQ = NQ_;               // 16-row groups per wave
+    static constexpr int WAVES = 2 * NW;         // waves per workgroup
+    static constexpr int PER_SIMD = WAVES / 4;   // waves per SIMD (one workgroup per CU)
+    static constexpr int KS = 2;                 // key groups
+    static constexpr int NB = 4;                 // 16-token tiles per iteration
+    static constexpr int RB = D * 2;             // bytes per head row
+    static constexpr int CH = RB / 16;           // 16-byte chunks per head row
+    static constexpr int KK = D / 32;            // 16x16x32 products per score tile
+    static constexpr int TT = D / 16;            // 16-wide output tiles
+    static constexpr int ROWS_W = 16 * NQ;       // query rows per wave
+    static constexpr int ROWS = NW * ROWS_W;     // query rows per tile
+    static constexpr int TILE = kBlock * RB;     // bytes of one 16-token tile of one head
+    static constexpr int SPAN = NB * TILE;       // an iteration's K (or V) rows of one group
+    static constexpr int ARR = KS * SPAN;        // one LDS buffer: both groups' tiles
+    static constexpr int RPR = 1024 / RB;        // rows per 1 KiB load instruction
+    static constexpr int RG = kBlock / RPR;      // load instructions per 16-token tile
+    static constexpr int PER_W = NB * RG / NW;   // load instructions per wave, iteration and cache
+    static constexpr int STEP = NB * kBlock;     // keys per iteration
+    static constexpr int STATE = TT * 4 + 2;     // floats of one lane's row state (acc, m, l)
+    static constexpr int SQ = (STATE + 3) / 4;   // of them in each of the four buffers
+    static_assert(ROWS == kPrefillRows, "the grid's tile height");
+    static_assert(CH == 4 * KK && D % 32 == 0, "head_dim a multiple of 32");
+    static_assert(RPR * RB == 1024 && 8 % RPR == 0 && (NB * RG) % NW == 0,
+                  "whole 1 KiB slices inside one block of 8 to 64, the same count per wave");
+    static_assert(NW * NQ * SQ * kWave * 4 <= ARR, "group 1's final state fits the four buffers");
 };
 
 // Word 3 of a raw buffer resource: 32-bit data format, no swizzle; with a
@@ -135,6 +143,12 @@ __device__ __forceinline__ void lds_load_1k(const char* base, int bytes, char* l
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// A block-table entry through the scalar cache (the index is uniform).
+typedef const __attribute__((address_space(4))) int32_t prefill_const_i32;
+__device__ __forceinline__ int scalar_entry(const int32_t* table, int i) {
+    return ((prefill_const_i32*)table)[__builtin_amdgcn_readfirstlane(i)];
+}
+
 // Headroom of the online softmax's reference maximum (log2 units): weights
 // reach at most 2^8, well inside fp16 and bf16 range.
 constexpr float kLazy = 8.f;
@@ -148,60 +162,280 @@ __device__ __forceinline__ uint32_t tile_pos(int row, int chunk) {
     return (uint32_t)(row * RB + ((chunk ^ (row % CH)) * 16));
 }
 
-// One iteration covers NB consecutive blocks: their K and V tiles are loaded
-// together (one iteration ahead) and one softmax rescale covers all NB x 16 keys.
-// With KS = 2 the workgroup holds two key groups of NW waves over the same rows:
-// group 0 takes the first half of the iterations, group 1 the rest, and their
-// softmax states (the same combination rule as the decode split merge) meet in
-// LDS at the end, so a tile that sees many keys gets twice the waves.
-template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int KS>
-__global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillParams p) {
-    using SH = PrefillShape<E, D, G, NW, NQ, NB, KS>;
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) with lgkmcnt(0), expcnt left open.
+constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
+
+// A workgroup barrier between phases.  No memory fence: a fence would also
+// wait for every LDS load in flight, and the point of the phase barriers is
+// to leave the next loads in flight (LDS reads finished before it, lgkmcnt
+// 0, so no read can see a later write).  The empty asm statements keep memory
+// accesses on their side of it and the scheduling barriers every other
+// instruction: the phases only overlap the two key groups' work if each
+// phase's products and softmax stay in it.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Ties a value to this point of the program: it must be computed before,
+// and is taken as changed after, so the compiler can move its computation
+// neither later (into the next phase) nor its uses earlier.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+    asm volatile("" : "+v"(x));
+}
+
+// ---- wave-wide integer reductions (every lane gets the result, uniform) ----
+__device__ __forceinline__ int wave_sum_i32(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppQuadXor1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppQuadXor2, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowHalfMirror, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowMirror, 0xF, 0xF, false);
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = (int)a[0] + (int)a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return __builtin_amdgcn_readfirstlane((int)b[0] + (int)b[1]);
+}
+
+__device__ __forceinline__ int wave_max_i32(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, kDppQuadXor1, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, kDppQuadXor2, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, kDppRowHalfMirror, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, kDppRowMirror, 0xF, 0xF, false));
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = max((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return __builtin_amdgcn_readfirstlane(max((int)b[0], (int)b[1]));
+}
+
+// ---- tile order: longest first ----------------------------------------------
+//
+// Workgroups are handed to the compute units in launch order, each to the
+// first one free, so launching tiles in decreasing key count is the
+// longest-first list schedule: the long tiles start at once and the short
+// ones fill in behind them, where the launch order (sequence, tile) of the
+// batch could leave a long tile for the end.  Tile t of a sequence covers
+// chunk tokens [tQ, min((t+1)Q, n)) (Q = kPrefillRows / G) and reads keys 0 ..
+// its last token's position.  The order sorts tiles by that last position,
+// descending, ties by sequence; a sequence's tiles end at distinct positions,
+// so each sequence has at most one tile per position.
+
+// Tiles of a chunk of n tokens after ctx cached ones whose last position is
+// at or past K.
+template <int Q>
+__device__ __forceinline__ int tiles_reaching(int ctx, int n, int K) {
+    if (n <= 0 || ctx + n - 1 < K) return 0;
+    const int nt = (n + Q - 1) / Q;
+    // tile t < nt - 1 ends at ctx + (t + 1) Q - 1, which reaches K from t = (K - ctx) / Q on
+    return nt - min(max(K - ctx, 0) / Q, nt - 1);
+}
+
+struct TileRef {
+    int s, t;  // sequence (-1: no tile of this rank) and tile index within its chunk
+};
+
+// The rank-th tile in that order, found by the wave alone (every wave of the
+// workgroup computes the same answer): a binary search for the last position
+// of that tile, counting the tiles that reach a position over all sequences
+// (lanes take sequences lane, lane + 64, ...), then its place among the tiles
+// ending there, in sequence order.
+template <int Q>
+__device__ TileRef pick_tile(const PrefillParams& p, int rank, int lane, int max_len) {
+    const int S = p.num_seqs;
+    // (ctx, n): tokens before the chunk and the chunk tokens computed (the
+    // first max_q_len); an empty or impossible chunk has none.
+    auto info = [&](int s, int& ctx, int& n) __attribute__((always_inline)) {
+        const int L = min(max(p.context_lens[s], 0), max_len);
+        const int nn = p.cu_q[s + 1] - p.cu_q[s];
+        const bool ok = nn > 0 && nn <= L;
+        ctx = ok ? L - nn : 0;
+        n = ok ? min(nn, p.max_q_len) : 0;
+    };
+    int ctx0 = 0, n0 = 0;  // sequence `lane`
+    if (lane < S) info(lane, ctx0, n0);
+    auto count = [&](int K) __attribute__((always_inline)) {
+        int c = tiles_reaching<Q>(ctx0, n0, K);
+        for (int s = kWave + lane; s < S; s += kWave) {
+            int cx, nn;
+            info(s, cx, nn);
+            c += tiles_reaching<Q>(cx, nn, K);
+        }
+        return wave_sum_i32(c);
+    };
+    int last = n0 > 0 ? ctx0 + n0 - 1 : -1;
+    for (int s = kWave + lane; s < S; s += kWave) {
+        int cx, nn;
+        info(s, cx, nn);
+        if (nn > 0) last = max(last, cx + nn - 1);
+    }
+    last = wave_max_i32(last);
+    if (last < 0 || count(0) <= rank) return {-1, 0};
+    int lo = 0, hi = last + 1;  // count(lo) > rank >= count(hi) = 0
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (count(mid) > rank) lo = mid;
+        else hi = mid;
+    }
+    int r = rank - count(lo + 1);  // place among the tiles ending at lo
+    for (int s0 = 0; s0 < S; s0 += kWave) {
+        const int s = s0 + lane;
+        int cx = ctx0, nn = n0;
+        if (s0 > 0) {
+            cx = 0;
+            nn = 0;
+            if (s < S) info(s, cx, nn);
+        }
+        const bool has = s < S && tiles_reaching<Q>(cx, nn, lo) > tiles_reaching<Q>(cx, nn, lo + 1);
+        uint64_t m = __builtin_amdgcn_ballot_w64(has);
+        const int cnt = __builtin_popcountll(m);
+        if (r < cnt) {
+            for (int k = 0; k < r; ++k) m &= m - 1;
+            const int sp = s0 + __builtin_ctzll(m);
+            int cp, np;
+            info(sp, cp, np);
+            return {sp, (np + Q - 1) / Q - tiles_reaching<Q>(cp, np, lo)};
+        }
+        r -= cnt;
+    }
+    return {-1, 0};
+}
+
+// The softmax weights as 16-bit matrix-core operands, four per lane and
+// block, rounded to nearest even (fp16 keeps 11 significant bits, bf16 8).
+// Row sums come from the same rounded weights (a product with a V^T of
+// ones), so each output row is an exact convex combination of V rows under
+// weights that differ from the true ones by a common factor and at most
+// 2^-8 (bf16) each: the weights' rounding moves an output by at most 2^-8 of
+// the spread of the V values its heavy keys hold, not of their size.
+template <class E>
+struct Weights;
+
+template <>
+struct Weights<F16> {
+    typedef typename MfmaOps<F16>::op4_t op4_t;
+    __device__ static __forceinline__ op4_t ones() { return op4_t{1.0f16, 1.0f16, 1.0f16, 1.0f16}; }
+    __device__ static __forceinline__ op4_t pack(const float (&x)[4]) {
+        return op4_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    }
+};
+
+template <>
+struct Weights<BF16> {
+    typedef typename MfmaOps<BF16>::op4_t op4_t;
+    __device__ static __forceinline__ op4_t ones() { return op4_t{0x3F80, 0x3F80, 0x3F80, 0x3F80}; }
+    __device__ static __forceinline__ op4_t pack(const float (&x)[4]) {
+        return op4_t{__builtin_bit_cast(short, (__bf16)x[0]), __builtin_bit_cast(short, (__bf16)x[1]),
+                     __builtin_bit_cast(short, (__bf16)x[2]), __builtin_bit_cast(short, (__bf16)x[3])};
+    }
+};
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier (LLVM AMDGPU).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// The products' schedule: step u's two fragment reads of step u + AHEAD
+// (while there is one), then its products (with the row sums at a pair's end).
+template <int U, int AHEAD, int TT, int MPS, int... I>
+__device__ __forceinline__ void pv_schedule(std::integer_sequence<int, I...>) {
+    auto one = [](auto u) __attribute__((always_inline)) {
+        constexpr int i = decltype(u)::value;
+        if constexpr (i + AHEAD < U) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, i % TT == TT - 1 ? 2 * MPS : MPS, 0);
+    };
+    (one(std::integral_constant<int, I>{}), ...);
+}
+
+// The scores' schedule: per block, the K reads of block nb + AHEAD (while
+// there is one), then block nb's products.
+template <int NB, int AHEAD, int KK, int MPB, int... I>
+__device__ __forceinline__ void qk_schedule(std::integer_sequence<int, I...>) {
+    auto one = [](auto b) __attribute__((always_inline)) {
+        constexpr int i = decltype(b)::value;
+        if constexpr (i + AHEAD < NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KK, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, MPB, 0);
+    };
+    (one(std::integral_constant<int, I>{}), ...);
+}
+
+// ---- the attention kernel -----------------------------------------------------
+//
+// Each key group takes half of the tile's key iterations (group 0 the first,
+// group 1 the rest) and runs them as alternating phases, each ending at a
+// workgroup barrier:
+//   M_j: the output products of iteration j - 1 (O^T += V^T P^T, from V_{j-1}
+//        in LDS), the scores of iteration j (S^T = K Q^T, from K_j), and the
+//        loads of K_{j+1},
+//   V_j: the softmax of iteration j's scores (weights P_j, the lazy rescale of
+//        O and l) and the loads of V_{j+1},
+// M_j all matrix-core work, V_j all vector work.  Group 1 runs one phase
+// behind group 0, and each SIMD holds one wave of each group (waves w and
+// w + 4 share a SIMD), so while one wave's products run on the matrix core
+// the other wave's softmax runs on the vector ALU.  K and V have two LDS
+// buffers each per group: K_j lives in K buffer j % 2 from M_{j-1} to M_j,
+// V_j in V buffer j % 2 from V_{j-1} to M_{j+1}; each wave waits (vmcnt) for
+// its own loads at the end of the V phase before their reader.
+template <class E, int D, int G, int NW, int NQ>
+__global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(PrefillParams p) {
+    using SH = PrefillShape<D, NW, NQ>;
+    static_assert(SH::WAVES == 2 * NW && SH::PER_SIMD == NW / 2, "the launch bounds above");
     using OPS = MfmaOps<E>;
     using op4_t = typename OPS::op4_t;
-    using el_t = typename std::remove_reference<decltype(op4_t{}[0])>::type;
-    constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT;
-    // The two buffers are separate arrays, so the compiler can tell the LDS
-    // loads filling one from the reads of the other (and need not wait for
-    // them before reading); the key groups' states meet in them or in a third.
-    __shared__ __attribute__((aligned(16))) char lds_a[SH::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds_b[SH::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) float lds_state[SH::MERGE_BYTES / 4];
+    constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT, NB = SH::NB;
+    constexpr int PER_W = SH::PER_W, STEP = SH::STEP;
+    constexpr int Q = kPrefillRows / G;  // chunk tokens per tile
+    // Four separate arrays, so the compiler can tell the loads filling one
+    // buffer from the reads of another and waits only where they meet.
+    __shared__ __attribute__((aligned(16))) char lds_k0[SH::ARR];
+    __shared__ __attribute__((aligned(16))) char lds_k1[SH::ARR];
+    __shared__ __attribute__((aligned(16))) char lds_v0[SH::ARR];
+    __shared__ __attribute__((aligned(16))) char lds_v1[SH::ARR];
+    // The tile's q rows (both key groups use the same), XOR-swizzled like K:
+    // read back for each iteration's scores rather than held in registers,
+    // which leaves room to read the V and K fragments well ahead.
+    __shared__ __attribute__((aligned(16))) char lds_q[SH::ROWS * RB];
 
-    // Grid (KV head, tile rank, sequence), KV head fastest: workgroups are
-    // dealt to the XCDs round-robin in launch order, so 8 consecutive ones of
-    // equal work (the same tile of 8 heads) give every XCD the same mix of
-    // long and short tiles; within a sequence the last tile (most keys) goes
-    // first.
-    const int s = blockIdx.z;
-    const int kvh = blockIdx.x;
-    const int Hq = p.n_q_heads;
+    // Grid (KV head x sequence slot, tile slot), KV head fastest: the
+    // workgroup of rank i and head h is the (h + Hkv i)-th launched, so every
+    // rank goes out to all heads before the next; the XCDs take workgroups
+    // round-robin, and a head's tiles all land on one XCD (its K and V stay in
+    // that XCD's L2) when Hkv is a multiple of 8.
+    const int Hkv = p.n_kv_heads;
+    const int kvh = blockIdx.x % Hkv;
+    const int rank = blockIdx.x / Hkv + p.num_seqs * blockIdx.y;
+    const int lane = threadIdx.x % kWave;
+    const int max_len = p.max_blocks << p.block_shift;
+    const TileRef tr = pick_tile<Q>(p, rank, lane, max_len);
+    if (tr.s < 0) return;
+    const int s = tr.s;
     const int q0 = p.cu_q[s];
     const int n = p.cu_q[s + 1] - q0;
-    const int L = min(max(p.context_lens[s], 0), p.max_blocks << p.block_shift);
-    if (n <= 0 || n > L) return;  // an empty or impossible chunk
-    const int nrows = n * G;
-    const int ntiles = (nrows + SH::ROWS - 1) / SH::ROWS;
-    const int tile = ntiles - 1 - (int)blockIdx.y;
-    if (tile < 0) return;
-    const int r0 = tile * SH::ROWS;
+    const int L = min(max(p.context_lens[s], 0), max_len);
+    const int Hq = p.n_q_heads;
+    const int nrows = min(n, p.max_q_len) * G;  // rows computed
+    const int r0 = tr.t * SH::ROWS;
     const int ctx = L - n;  // tokens before the chunk
     const int wg_last_pos = ctx + (min(r0 + SH::ROWS, nrows) - 1) / G;
     const int nblk = wg_last_pos / kBlock + 1;  // 16-token tiles the workgroup reads
     const int nit = (nblk + NB - 1) / NB;
+    const int NJ = (nit + 1) / 2;                // phase pairs of either group
 
-    const int tid = threadIdx.x;
-    const int kg = wave_id_uniform() / NW;  // key group
-    const int w = wave_id_uniform() % NW;   // row wave within the group
-    const int lane = tid % kWave;
-    // iterations [kb, ke) belong to this wave's key group
-    const int half = KS == 1 ? nit : (nit + 1) / 2;
-    const int kb = kg == 0 ? 0 : half;
-    const int ke = kg == 0 ? half : nit;
+    const int kg = wave_id_uniform() / SH::NW;  // key group
+    const int w = wave_id_uniform() % SH::NW;   // row wave within the group
+    const int kb = kg == 0 ? 0 : NJ;            // the group's first iteration
+    const int nj = kg == 0 ? NJ : nit - NJ;     // and its count
     const int gq = lane / 16;  // MFMA lane coordinates
     const int jq = lane % 16;
     const int wr0 = r0 + w * SH::ROWS_W;  // this wave's first row
-    const int wave_last_pos = wr0 < nrows ? ctx + (min(wr0 + SH::ROWS_W, nrows) - 1) / G : -1;
+    const int wave_first_pos = ctx + wr0 / G;
+    // Iteration j of the group is masked unless every key of it is visible to
+    // every row of the wave.  A wave computes every phase of its group, also
+    // for an iteration none of its rows sees (or one past the group's range,
+    // loaded as zeros): the mask makes all its weights 0, and skipping it
+    // would not shorten the phase, which waits for every wave at its barrier.
+    auto masked = [&](int j) __attribute__((always_inline)) { return (kb + j + 1) * STEP - 1 > wave_first_pos; };
 
     // The softmax below needs a positive scale: a negative one moves into q's
     // sign bits (exact), and a zero one becomes the smallest normal float,
@@ -210,7 +444,9 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     const float scale_log2 = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
     // q rows of this wave: group c, column jq is row wr0 + 16c + jq.
-    Vec16 qf[NQ][KK];
+    // q rows of this wave: group c, column jq is row wr0 + 16c + jq (row
+    // 32w + 16c + jq of the tile); group 0's waves put them in LDS (rows past
+    // the chunk as zeros), the first barrier publishes them.
     int qpos[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
@@ -218,24 +454,31 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
         const bool ok = row < nrows;
         const int tok = row / G;
         qpos[c] = ok ? ctx + tok : -1;
-        const char* qrow = static_cast<const char*>(p.q) +
-                           (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
+        if (kg == 0) {
+            const char* qrow = static_cast<const char*>(p.q) +
+                               (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            qf[c][kk] = ok ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
+            for (int kk = 0; kk < KK; ++kk) {
+                Vec16 v = ok ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qf[c][kk].w[e] ^= qsign;
+                for (int e = 0; e < 4; ++e) v.w[e] ^= qsign;
+                lds_store16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq), v);
+            }
         }
     }
-    float m[NQ], l[NQ];
-    f32x4_t acc[NQ][TT];
+    // Row state: reference maximum m, output acc and the weights' sum, which
+    // the matrix core accumulates too (the product with a V^T of ones puts
+    // row jq's sum in every element of lane column jq).
+    float m[NQ];
+    f32x4_t acc[NQ][TT], lsum[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
         m[c] = -INFINITY;
-        l[c] = 0.f;
+        lsum[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[c][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    const op4_t ones = Weights<E>::ones();
 
     // K and V go from memory straight into LDS (buffer loads with an LDS
     // destination).  One such instruction of a wave fills a contiguous 1 KiB
@@ -245,282 +488,331 @@ __global__ __launch_bounds__(KS * NW * kWave, 4) void prefill_kernel(PrefillPara
     // its slot.  The block's base address and the bytes of its rows inside the
     // sequence make the buffer resource, so rows past the context and invalid
     // table entries arrive as zeros (out-of-range buffer reads return 0).
-    const uint32_t row_stride = (uint32_t)p.n_kv_heads * RB;
+    // Slice g = w + k NW of an iteration (per cache): tile g / RG, rows
+    // RPR (g % RG) ..; an iteration spans a whole number of blocks, so the
+    // slice's row offset inside its block is the same in every iteration and
+    // goes into the lane offsets.
+    // Wave w of a key group loads tile w of each iteration (K and V): slice
+    // k is rows RPR k .. RPR k + RPR - 1 of it, inside the tile's first eight
+    // rows (half 0) or its last eight (half 1); with blocks of 16 tokens or
+    // more the two halves are one block.
+    static_assert(SH::NW == NB && SH::PER_W == SH::RG, "one 16-token tile per row wave");
+    const uint32_t row_stride = (uint32_t)Hkv * RB;
     const int bshift = p.block_shift;
     const int bsize = 1 << bshift;
-    const int64_t blk_bytes = (int64_t)row_stride << bshift;
+    const uint32_t blk_bytes = row_stride << bshift;  // below 2^32: 64 x Hkv x 256 bytes at most
     const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
     const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
-    constexpr int RPR = 1024 / RB;           // rows per load instruction
-    constexpr int RG = kBlock / RPR;         // load instructions per tile and cache
-    constexpr int PER_W = 2 * NB * RG / NW;  // load instructions per wave and iteration
-    constexpr int STEP = NB * kBlock;        // tokens per iteration
-    static_assert(RPR * RB == 1024 && 8 % RPR == 0 && STEP % 64 == 0 && (2 * NB * RG) % NW == 0,
-                  "whole 1 KiB slices inside one block of 8 to 64, the same count per wave");
-    // Slice g = w + k NW of an iteration: cache g / (NB RG), tile (g / RG) % NB,
-    // rows RPR (g % RG) ..  An iteration spans a whole number of blocks, so
-    // the slice's row offset inside its block is the same in every iteration
-    // and goes into the lane offsets; the load's resource starts at the block
-    // and covers its rows inside the sequence.
-    int tok0[PER_W];   // first token of slice k in iteration 0
-    int tokb0[PER_W];  // first token of its block
+    const int tt0 = kb * STEP + w * kBlock;  // first token of the wave's tile in the group's iteration 0
     uint32_t voff[PER_W];
+    uint32_t ldso[PER_W];  // the slice's byte offset in an LDS buffer
 #pragma unroll
     for (int k = 0; k < PER_W; ++k) {
-        const int g = w + k * NW;
-        tok0[k] = ((g / RG) % NB) * kBlock + (g % RG) * RPR;
-        tokb0[k] = tok0[k] & -bsize;
-        const int row = (g % RG) * RPR + lane / CH;  // row in the tile
-        voff[k] = (uint32_t)(tok0[k] - tokb0[k] + lane / CH) * row_stride + (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
+        const int row = k * SH::RPR + lane / CH;  // row in the tile
+        voff[k] = (uint32_t)(((tt0 + k * SH::RPR) & (bsize - 1)) + lane / CH) * row_stride +
+                  (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
+        ldso[k] = (uint32_t)(kg * SH::SPAN + w * SH::TILE + k * 1024);
     }
-    // slices past the workgroup's last tile, or past the sequence's last table entry, load nothing
+    // halves past the workgroup's last tile, or past the sequence's last table entry, load nothing
     const int tok_lim = min(nblk * kBlock, (L + bsize - 1) & -bsize);
-    // LDS tiles of this key group in buffer BUF: [K, V][block][row][RB]
-    auto tiles = [&](auto bufc, int kv) {
-        return (decltype(bufc)::value ? lds_b : lds_a) + (kg * 2 + kv) * SH::SPAN;
+    typedef int Ents[2];
+    struct Blk {
+        uint64_t off;  // byte offset of the half's block in a cache
+        int size;      // bytes of its rows inside the sequence (0: load zeros)
     };
-    // Table entries are read one step ahead of their loads: the step barrier's
-    // wait covers them, and no wait for them lands behind an LDS load.
-    auto entries = [&](int it, int (&pbs)[PER_W]) {
+    // Table entries of the two halves of the group's iteration j, read a
+    // phase before their loads.  The read index is clamped into the table and
+    // nothing depends on the value until then, so no read waits or branches.
+    auto entries = [&](int j, Ents& e) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) e[h] = scalar_entry(table, min(j * STEP + tt0 + 8 * h, tok_lim - 1) >> bshift);
+    };
+    // Where the halves of iteration j come from; a half past the workgroup's
+    // keys, or of an iteration past the group's range, loads zeros (its loads
+    // still run, so that every phase issues the same number of loads and the
+    // waits are static).
+    auto place = [&](int j, const Ents& e, Blk (&bl)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tok = j * STEP + tt0 + 8 * h;
+            const bool ok = j < nj && tok < tok_lim && (uint32_t)e[h] < (uint32_t)p.num_blocks;
+            bl[h].off = (uint64_t)(uint32_t)(ok ? e[h] : 0) * blk_bytes;
+            bl[h].size = ok ? min(L - (tok & -bsize), bsize) * (int)row_stride : 0;
+        }
+    };
+    auto issue = [&](char* buf, const char* base, const Blk (&bl)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < PER_W; ++k) {
-            const int tok = it * STEP + tok0[k];
-            pbs[k] = tok < tok_lim ? table[tok >> bshift] : -1;
-        }
-    };
-    auto issue = [&](int it, const int (&pbs)[PER_W], auto buf) {
-#pragma unroll
-        for (int k = 0; k < PER_W; ++k) {
-            const int g = w + k * NW;  // uniform over the wave
-            const int kv = g / (NB * RG), nb = (g / RG) % NB;
-            const int pb = __builtin_amdgcn_readfirstlane(pbs[k]);
-            const bool ok = pb >= 0 && pb < p.num_blocks;
-            const int rows = min(max(L - (it * STEP + tokb0[k]), 0), bsize);  // rows of the block in the sequence
-            // the size is uniform already; readfirstlane keeps the resource in scalar registers
-            lds_load_1k((kv ? vbase : kbase) + (ok ? (int64_t)pb * blk_bytes : 0), ok ? (int)(rows * row_stride) : 0,
-                        tiles(buf, kv) + nb * SH::TILE + (g % RG) * 1024, voff[k]);
+            const Blk& b = bl[(k * SH::RPR) / 8];
+            lds_load_1k(base + b.off, b.size, buf + ldso[k], voff[k]);
         }
     };
 
-    // One iteration of one wave; MASK builds the prefix-causal mask into the
-    // score products' initial value (0, or -inf for a key past the row's
-    // position), else every key of the iteration is visible to every row.
-    auto compute = [&](auto masked, auto buf, int it) {
-        constexpr bool MASK = decltype(masked)::value;
-        const int b0 = it * NB;
-        if (b0 * kBlock <= wave_last_pos) {
-            const char* kl = tiles(buf, 0);
-            const char* vl = tiles(buf, 1);
-            // scores: lane (gq, jq) holds keys (b0 + nb) * 16 + 4gq + r of row column jq
-            f32x4_t sacc[NQ][NB];
-            if constexpr (!MASK) {
-#pragma unroll
-                for (int c = 0; c < NQ; ++c)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) sacc[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            } else {
-#pragma unroll
-                for (int c = 0; c < NQ; ++c) {
-                    const int lim = qpos[c] - b0 * kBlock - 4 * gq;  // last visible key offset of this lane
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) sacc[c][nb][r] = 16 * nb + r <= lim ? 0.f : -INFINITY;
-                }
-            }
-            // Every block of a computed iteration gets its products, those
-            // past the wave's rows included (their scores stay -inf from the
-            // mask): a branch around them would put the softmax's first reads
-            // of a product's result right after it, closer than its latency.
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                Vec16 ka[KK];
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) ka[kk] = lds_load16(kl + nb * SH::TILE, tile_pos<RB>(jq, 4 * kk + gq));
-#pragma unroll
-                for (int c = 0; c < NQ; ++c)
-#pragma unroll
-                    for (int kk = 0; kk < KK; ++kk) sacc[c][nb] = OPS::qk(ka[kk], qf[c][kk], sacc[c][nb]);
-            }
-            op4_t ph[NQ][NB], pl[NQ][NB];
-#pragma unroll
-            for (int c = 0; c < NQ; ++c) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[c][nb][r]);
-                mx = rows_max(mx);
-                const float mn = mx * scale_log2;  // the row's largest scaled score here
-                // The reference m[c] moves only when a row's scores pass it by
-                // more than kLazy (log2 units), so the weights stay below 2^kLazy
-                // and most iterations skip the rescale.
-                if (__builtin_amdgcn_ballot_w64(mn > m[c] + kLazy)) {
-                    const float nm = fmaxf(m[c], mn);
-                    const float alpha = __builtin_amdgcn_exp2f(m[c] - (nm == -INFINITY ? 0.f : nm));
-                    l[c] *= alpha;
-#pragma unroll
-                    for (int t = 0; t < TT; ++t) acc[c][t] *= alpha;
-                    m[c] = nm;
-                }
-                const float ms = m[c] == -INFINITY ? 0.f : m[c];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[c][nb][r], scale_log2, -ms));
-                        l[c] += pr;
-                        short hs, ls;
-                        OPS::split(pr, hs, ls);
-                        ph[c][nb][r] = __builtin_bit_cast(el_t, hs);
-                        pl[c][nb][r] = __builtin_bit_cast(el_t, ls);
-                    }
-            }
-            // V^T read transposed: lane (gq, jq) takes key row 4gq + jq/4, bytes 32t + 8(jq%4).
-            // Blocks nb and nb + 1 make one 16x16x32 product: contraction
-            // slots 0-3 are keys 4gq + r of block nb, slots 4-7 those of
-            // block nb + 1, in V^T and P^T alike.  A block past the wave's
-            // last position has P = 0 (masked) and finite V (loaded, or zero).
-            const int trow = 4 * gq + jq / 4;
-#pragma unroll
-            for (int nb = 0; nb < NB; nb += 2) {
-                if ((b0 + nb) * kBlock > wave_last_pos) continue;
-#pragma unroll
-                for (int t = 0; t < TT; ++t) {
-                    const uint32_t off = tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2);
-                    const op4_t a0 = OPS::read_tr(vl + nb * SH::TILE + off);
-                    const op4_t a1 = OPS::read_tr(vl + (nb + 1) * SH::TILE + off);
-#pragma unroll
-                    for (int c = 0; c < NQ; ++c) {
-                        acc[c][t] = OPS::pv2(a0, a1, ph[c][nb], ph[c][nb + 1], acc[c][t]);
-                        if constexpr (SPLIT) acc[c][t] = OPS::pv2(a0, a1, pl[c][nb], pl[c][nb + 1], acc[c][t]);
-                    }
-                }
-            }
-        }
-    };
-
-    // Both groups step together (the barrier is the workgroup's); a group
-    // whose range is shorter idles through its last step.
-    // Step j computes from buffer j % 2 while the next iteration's loads fill
-    // the other; they land before the step's barrier (vmcnt 0).
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    int pbs[PER_W];
-    if (kb < ke) {
-        entries(kb, pbs);
-        issue(kb, pbs, B0{});
-        if (kb + 1 < ke) entries(kb + 1, pbs);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    auto step = [&](auto masked, int j, auto buf) {
-        const int it = kb + j;
-        if (it + 1 < ke) {  // uniform over the group
-            issue(it + 1, pbs, std::integral_constant<int, 1 - decltype(buf)::value>{});
-            if (it + 2 < ke) entries(it + 2, pbs);
-        }
-        if (it < ke) compute(masked, buf, it);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    };
-    // Steps whose iterations (in both groups) hold only keys every row of the
-    // tile sees run without the mask (an even number of them, so that the
-    // buffers stay fixed per unrolled step); the rest, the causal diagonal,
-    // with it.
-    const int it_full = (ctx + r0 / G + 1) / (NB * kBlock);
-    const int j_full = (KS == 1 ? min(it_full, half) : min(max(it_full - half, 0), half)) & ~1;
-    int j = 0;
-    for (; j < j_full; j += 2) {
-        step(std::false_type{}, j, B0{});
-        step(std::false_type{}, j + 1, B1{});
-    }
-    for (; j < half; j += 2) {
-        step(std::true_type{}, j, B0{});
-        if (j + 1 < half) step(std::true_type{}, j + 1, B1{});
-    }
-
-    // Each lane summed its own 4 keys per block: add the other lane groups.
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) l[c] = rows_sum(l[c]);
-    if constexpr (KS == 2) {
-        // Group 1 leaves its state in LDS (the tiles are no longer read: the
-        // loop ended on a barrier); group 0 folds it into its own.  Lane-major
-        // layout, so each store and load is one conflict-free row of 64 words.
-        // State element e of row group c: acc[t][r] at e = 4t + r, then m, l.
-        auto slot = [&](int c, int e) -> float* {
-            if constexpr (SH::STATE_IN_BUFFERS) {
-                constexpr int SB = SH::STATE - SH::STATE_A;
-                return e < SH::STATE_A
-                           ? reinterpret_cast<float*>(lds_a) + ((w * NQ + c) * SH::STATE_A + e) * kWave + lane
-                           : reinterpret_cast<float*>(lds_b) + ((w * NQ + c) * SB + e - SH::STATE_A) * kWave + lane;
-            } else {
-                return lds_state + ((w * NQ + c) * SH::STATE + e) * kWave + lane;
-            }
-        };
-        if (kg == 1) {
-#pragma unroll
-            for (int c = 0; c < NQ; ++c) {
-#pragma unroll
-                for (int t = 0; t < TT; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) *slot(c, 4 * t + r) = acc[c][t][r];
-                *slot(c, 4 * TT) = m[c];
-                *slot(c, 4 * TT + 1) = l[c];
-            }
-        }
-        __syncthreads();
-        if (kg == 1) return;
+    f32x4_t sc[NQ][NB];            // scores of an iteration, from its M phase to its V phase
+    op4_t ph[NQ][NB];              // its weights, from its V phase to the next M
+    // S^T = K Q^T of iteration j: lane (gq, jq) holds keys 16 nb + 4 gq + r of
+    // row column jq.  MASK builds the prefix-causal mask into the products'
+    // initial value (0, or -inf for a key past the row's position).  Every
+    // block gets its products, those past the wave's rows included (their
+    // scores stay -inf): a branch around them would put the softmax's first
+    // reads of a product's result right after it, closer than its latency.
+    auto scores = [&](const char* kl, int j) __attribute__((always_inline)) {
+        const int key0 = (kb + j) * STEP;
+        const bool msk = masked(j);
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-            const float m1 = *slot(c, 4 * TT);
-            const float l1 = *slot(c, 4 * TT + 1);
-            const float mm = fmaxf(m[c], m1);
-            const float mr = mm == -INFINITY ? 0.f : mm;
-            const float a0 = __builtin_amdgcn_exp2f(m[c] - mr);
-            const float a1 = __builtin_amdgcn_exp2f(m1 - mr);
-            l[c] = l[c] * a0 + l1 * a1;
+            const int lim = msk ? qpos[c] - key0 - 4 * gq : STEP;  // last visible key offset of this lane
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[c][nb][r] = 16 * nb + r <= lim ? 0.f : -INFINITY;
+        }
+        Vec16 qf[NQ][KK];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                qf[c][kk] = lds_load16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq));
+        // block nb's K fragments are read AHEAD blocks before its products
+        constexpr int AHEAD = 1;
+        Vec16 ka[NB][KK];
+        auto fetch = [&](int nb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) ka[nb][kk] = lds_load16(kl + nb * SH::TILE, tile_pos<RB>(jq, 4 * kk + gq));
+        };
+#pragma unroll
+        for (int nb = 0; nb < AHEAD; ++nb) fetch(nb);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if (nb + AHEAD < NB) fetch(nb + AHEAD);
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) sc[c][nb] = OPS::qk(ka[nb][kk], qf[c][kk], sc[c][nb]);
+        }
+    };
+    // Online softmax of the scores: weights in base-2 units against a lazily
+    // moved reference maximum m (it moves only when a row's scores pass it by
+    // more than kLazy, so weights stay below 2^kLazy and most iterations skip
+    // the rescale of O and l).
+    auto softmax = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[c][nb][r]);
+            mx = rows_max(mx);
+            const float mn = mx * scale_log2;  // the row's largest scaled score here
+            if (__builtin_amdgcn_ballot_w64(mn > m[c] + kLazy)) {
+                const float nm = fmaxf(m[c], mn);
+                const float alpha = __builtin_amdgcn_exp2f(m[c] - (nm == -INFINITY ? 0.f : nm));
+                lsum[c] *= alpha;
+#pragma unroll
+                for (int t = 0; t < TT; ++t) acc[c][t] *= alpha;
+                m[c] = nm;
+            }
+            const float ms = m[c] == -INFINITY ? 0.f : m[c];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[c][nb][r], scale_log2, -ms));
+                ph[c][nb] = Weights<E>::pack(pr);
+                pin(ph[c][nb]);
+            }
+        }
+    };
+    // O^T += V^T P^T of iteration j.  V^T is read transposed: lane (gq, jq)
+    // takes key row 4gq + jq/4, bytes 32t + 8(jq%4).  Blocks nb and nb + 1 make
+    // one 16x16x32 product: contraction slots 0-3 are keys 4gq + r of block
+    // nb, slots 4-7 those of block nb + 1, in V^T and P^T alike.  The
+    // fragments of step u (pair u / TT, output tile u % TT) are read two steps
+    // ahead of their products, so that the reads' latency hides behind them.
+    // Also the weights' row sums (a V^T of ones).
+    auto products = [&](const char* vl) __attribute__((always_inline)) {
+        constexpr int U = (NB / 2) * TT;       // steps
+        constexpr int AHEAD = 4;               // steps whose fragments are in flight
+        constexpr int MPS = NQ;                // products per step
+        const int trow = 4 * gq + jq / 4;
+        op4_t fa[U], fb[U];
+        auto fetch = [&](int u) __attribute__((always_inline)) {
+            const int nb = 2 * (u / TT), t = u % TT;
+            const uint32_t off = tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2);
+            fa[u] = OPS::read_tr(vl + nb * SH::TILE + off);
+            fb[u] = OPS::read_tr(vl + (nb + 1) * SH::TILE + off);
+        };
+#pragma unroll
+        for (int u = 0; u < AHEAD; ++u) fetch(u);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u + AHEAD < U) fetch(u + AHEAD);
+            const int nb = 2 * (u / TT), t = u % TT;
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                acc[c][t] = OPS::pv2(fa[u], fb[u], ph[c][nb], ph[c][nb + 1], acc[c][t]);
+            }
+            if (t == TT - 1) {
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    lsum[c] = OPS::pv2(ones, ones, ph[c][nb], ph[c][nb + 1], lsum[c]);
+                }
+            }
+        }
+        // Keep that order through scheduling: the first AHEAD steps' reads,
+        // then per step the reads AHEAD steps on and the step's products.
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * AHEAD, 0);
+        pv_schedule<U, AHEAD, TT, MPS>(std::make_integer_sequence<int, U>{});
+    };
+
+    // Phase M_j (buffer parity b = j % 2): the loads of K_{j+1} (into K
+    // buffer 1 - b, last read in M_{j-1}); the products of j - 1 from V
+    // buffer 1 - b (their weights die there); the scores of j from K buffer b
+    // (born there), so weights and scores never hold registers together; the
+    // table entries of j + 2.  The K loads go here because this
+    // wave's issue slots between its products are free; its partner's are not.
+    Ents ec;     // table entries of iteration j + 1 when M_j starts
+    Blk bl[2];   // where iteration j + 1's halves come from, from M_j to V_j
+    // (M_0 has no products, the last M phase, M_NJ, no scores)
+    auto mphase = [&](int j, auto par, auto pv, auto qk) __attribute__((always_inline)) {
+        constexpr int b = decltype(par)::value;
+        // The products are the phase's critical path: this wave issues first
+        // (the SIMD otherwise favours the older wave, group 0's), and its
+        // partner's softmax fills the cycles between the products.
+        __builtin_amdgcn_s_setprio(1);
+        place(j + 1, ec, bl);
+        issue(b ? lds_k0 : lds_k1, kbase, bl);
+        if constexpr (decltype(pv)::value) products((b ? lds_v0 : lds_v1) + kg * SH::SPAN);
+        if constexpr (decltype(qk)::value) {
+            scores((b ? lds_k1 : lds_k0) + kg * SH::SPAN, j);
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) pin(sc[c][nb]);
+        }
+        // (scalar loads complete out of order with LDS reads: issued any
+        // earlier, they would turn the reads' partial waits into full ones)
+        entries(j + 2, ec);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // Phase V_j: the loads of V_{j+1} into V buffer 1 - b (read by every wave
+    // of the group in M_j, so not before this phase), the softmax of j; then
+    // this wave's loads of V_j and K_{j+1} land (those of V_{j+1} may stay in
+    // flight), so that after the barrier the whole group's K_{j+1} and V_j
+    // are in LDS.
+    auto vphase = [&](auto par) __attribute__((always_inline)) {
+        constexpr int b = decltype(par)::value;
+        issue(b ? lds_v0 : lds_v1, vbase, bl);
+        softmax();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_W));
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    // Prologue: K_0 and V_0; K_0 (and q) land before the first barrier.
+    {
+        entries(0, ec);
+        place(0, ec, bl);
+        issue(lds_k0, kbase, bl);
+        issue(lds_v0, vbase, bl);
+        entries(1, ec);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_W));
+    }
+    phase_barrier();
+    if (kg == 1) phase_barrier();  // group 1 runs one phase behind
+    using T = std::true_type;
+    using F = std::false_type;
+    mphase(0, B0{}, F{}, T{});
+    phase_barrier();
+    vphase(B0{});
+    phase_barrier();
+    int j = 1;
+    for (; j + 1 < NJ; j += 2) {
+        mphase(j, B1{}, T{}, T{});
+        phase_barrier();
+        vphase(B1{});
+        phase_barrier();
+        mphase(j + 1, B0{}, T{}, T{});
+        phase_barrier();
+        vphase(B0{});
+        phase_barrier();
+    }
+    if (j < NJ) {  // j odd
+        mphase(j, B1{}, T{}, T{});
+        phase_barrier();
+        vphase(B1{});
+        phase_barrier();
+    }
+    // M_NJ: the last products; then the last phases' zero fills land before
+    // the buffers take group 1's state.
+    if (NJ & 1) mphase(NJ, B1{}, T{}, F{});
+    else mphase(NJ, B0{}, T{}, F{});
+    __builtin_amdgcn_s_waitcnt(0);
+    phase_barrier();
+    if (kg == 0) phase_barrier();
+
+    float l[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) l[c] = lsum[c][0];
+    // Group 1 leaves its state in LDS (every load has landed and every read
+    // finished before the last barriers); group 0 folds it into its own with
+    // the decode merge's rule.  State element e of row group c (acc[t][r] at
+    // e = 4t + r, then m, l) goes to buffer e % 4, lane-major, so each store
+    // and load is one conflict-free row of 64 words.
+    auto slot = [&](int c, int e) __attribute__((always_inline)) -> float* {
+        char* arr = e % 4 == 0 ? lds_k0 : e % 4 == 1 ? lds_k1 : e % 4 == 2 ? lds_v0 : lds_v1;
+        return reinterpret_cast<float*>(arr) + (((w * NQ + c) * SH::SQ + e / 4) * kWave + lane);
+    };
+    if (kg == 1) {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
 #pragma unroll
             for (int t = 0; t < TT; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[c][t][r] = acc[c][t][r] * a0 + *slot(c, 4 * t + r) * a1;
+                for (int r = 0; r < 4; ++r) *slot(c, 4 * t + r) = acc[c][t][r];
+            *slot(c, 4 * TT) = m[c];
+            *slot(c, 4 * TT + 1) = l[c];
         }
     }
+    __syncthreads();
+    if (kg == 1) return;
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
+        const float m1 = *slot(c, 4 * TT);
+        const float l1 = *slot(c, 4 * TT + 1);
+        const float mm = fmaxf(m[c], m1);
+        const float mr = mm == -INFINITY ? 0.f : mm;
+        const float a0 = __builtin_amdgcn_exp2f(m[c] - mr);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - mr);
+        const float lt = l[c] * a0 + l1 * a1;
         const int row = wr0 + 16 * c + jq;
         if (row >= nrows) continue;
-        const float inv = 1.f / l[c];
+        const float inv = 1.f / lt;
         char* orow = static_cast<char*>(p.out) + (((int64_t)(q0 + row / G) * Hq + kvh * G + row % G) * D) * 2;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) E::store(orow + (16 * t + 4 * gq + r) * 2, acc[c][t][r] * inv);
+            for (int r = 0; r < 4; ++r)
+                E::store(orow + (16 * t + 4 * gq + r) * 2, (acc[c][t][r] * a0 + *slot(c, 4 * t + r) * a1) * inv);
     }
 }
 
-template <class E, int D, int G, int NW, int NQ, int NB, bool SPLIT, int KS>
-hipError_t launch_prefill_shape(const PrefillParams& p, hipStream_t stream) {
-    constexpr int ROWS = NW * 16 * NQ;
-    const int64_t tiles = ((int64_t)p.max_q_len * G + ROWS - 1) / ROWS;
-    if (tiles > kMaxPrefillTiles || p.num_seqs > 65535) return hipErrorInvalidConfiguration;
-    const dim3 grid(p.n_kv_heads, (unsigned)tiles, (unsigned)p.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ, NB, SPLIT, KS>), grid, dim3(KS * NW * kWave), 0, stream, p);
-    return hipGetLastError();
-}
-
-// Launch shape (measured on MI355X): 8 waves of 16 query rows (128 rows per
-// workgroup) in each of 2 key groups; 4 blocks (64 keys) per iteration, i.e.
-// 32 KiB (head_dim 128) or 16 KiB (64) of K and V per group and LDS buffer.  It
-// needs no accumulator registers beyond the architectural VGPRs and runs 4
-// waves per SIMD.  fp16 keeps one 16-bit P per weight (11 significant bits);
-// bf16 splits P into high and low parts, since one bf16 keeps only 8.
-template <class E, int D, int G>
+// Launch shape: 8 waves (two key groups of four) over 128-row tiles, 32 rows
+// per wave, 4 blocks (64 keys) per iteration: 32 KiB (head_dim 128) or 16 KiB
+// (64) per K or V buffer, four buffers and the tile's q, two waves per SIMD.
+template <class E, int D, int G, int NW = 4, int NQ = 2>
 static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
-    constexpr bool SPLIT = std::is_same<E, BF16>::value;
-    static_assert(8 * 16 == kPrefillRows, "the grid's tile height");
-    return launch_prefill_shape<E, D, G, 8, 1, 4, SPLIT, 2>(p, stream);
+    using SH = PrefillShape<D, NW, NQ>;
+    const int64_t tiles = ((int64_t)p.max_q_len * G + SH::ROWS - 1) / SH::ROWS;
+    const int64_t slots = (int64_t)p.n_kv_heads * p.num_seqs;
+    if (tiles > kMaxPrefillTiles || p.num_seqs > 65535 || tiles * p.num_seqs > INT32_MAX ||
+        slots * SH::WAVES * kWave > UINT32_MAX)
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)slots, (unsigned)tiles);
+    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ>), grid, dim3(SH::WAVES * kWave), 0, stream, p);
+    return hipGetLastError();
 }
 
 template <class E, int D>

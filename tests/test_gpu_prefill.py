@@ -258,3 +258,48 @@ def test_prefill_same_tokens_any_block_size_bitwise():
         outs.append(got)
         say("  B=%d done" % B)
     assert all(np.array_equal(outs[0], o) for o in outs[1:]), "outputs differ between block sizes"
+
+
+def test_prefill_many_sequences_mixed():
+    """150 sequences of every kind in one step (empty chunks, one-token chunks,
+    chunks of several tiles, contexts from 0 to a few hundred): the tiles are
+    launched longest first over the whole batch, and past 64 sequences the
+    order is counted over several sequences per lane; every row must come out
+    once and right."""
+    rng = np.random.default_rng(3800)
+    S = 150
+    chunk = rng.integers(0, 25, S)
+    chunk[rng.integers(0, S, 20)] = 1
+    chunk[rng.integers(0, S, 12)] = 0
+    chunk[7], chunk[90], chunk[149] = 300, 170, 129
+    context = rng.integers(0, 300, S)
+    context[rng.integers(0, S, 10)] = 0
+    w = W.build_prefill("many_seqs", context.tolist(), chunk.tolist(), 8, 2, 64, "f16", 3800, pool_factor=1.2)
+    _check(w)
+
+
+def test_prefill_rows_past_max_q_len_untouched():
+    """max_q_len caps the chunk tokens computed: a chunk longer than it gets its
+    first max_q_len tokens' rows (right), the rest stay as they were, and the
+    other sequences are unaffected."""
+    import torch
+    import paged_kv_cache_227_amd as P
+    w = _poisoned(W.build_prefill("capped", [10, 0, 200], [40, 150, 90], 8, 2, 128, "bf16", 3900))
+    cap = 100
+    kc, vc = dev_storage(w.k_cache, w.dtype), dev_storage(w.v_cache, w.dtype)
+    bt, cu, lens = _i32(w.block_tables), _i32(w.cu_q), _i32(w.context_lens)
+    P.paged_kv_append_tokens(dev_storage(w.k_new, w.dtype), dev_storage(w.v_new, w.dtype), kc, vc, bt, cu,
+                             _i32(w.start_pos))
+    q = dev_storage(w.q, w.dtype)
+    out = torch.full_like(q, float("nan"))
+    P.paged_attention_prefill(q, kc, vc, bt, cu, lens, w.scale, out, cap)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    _, _, want = oracle_prefill(w)
+    computed = np.concatenate([np.arange(int(w.cu_q[s]), int(w.cu_q[s]) + min(int(w.cu_q[s + 1] - w.cu_q[s]), cap))
+                               for s in range(w.num_seqs)])
+    skipped = np.setdiff1d(np.arange(got.shape[0]), computed)
+    assert skipped.size == 50 and np.all(np.isnan(got[skipped])), "rows past max_q_len were written"
+    err, ratio = row_check(got[computed], want[computed])
+    say("  max abs err %.3g, worst row at %.3g of its row-scaled bound" % (err, ratio))
+    assert err <= TOL and ratio <= 1.0
