@@ -336,28 +336,36 @@ struct Weights<BF16> {
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// The products' schedule: step u's two fragment reads of step u + AHEAD
-// (while there is one), then its products (with the row sums at a pair's end).
-template <int U, int AHEAD, int TT, int MPS, int... I>
-__device__ __forceinline__ void pv_schedule(std::integer_sequence<int, I...>) {
-    auto one = [](auto u) __attribute__((always_inline)) {
-        constexpr int i = decltype(u)::value;
-        if constexpr (i + AHEAD < U) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, i % TT == TT - 1 ? 2 * MPS : MPS, 0);
-    };
-    (one(std::integral_constant<int, I>{}), ...);
-}
-
-// The scores' schedule: per block, the K reads of block nb + AHEAD (while
-// there is one), then block nb's products.
-template <int NB, int AHEAD, int KK, int MPB, int... I>
-__device__ __forceinline__ void qk_schedule(std::integer_sequence<int, I...>) {
-    auto one = [](auto b) __attribute__((always_inline)) {
-        constexpr int i = decltype(b)::value;
-        if constexpr (i + AHEAD < NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KK, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, MPB, 0);
-    };
-    (one(std::integral_constant<int, I>{}), ...);
+// One M phase's schedule (see the kernel): PV products steps of NQ products
+// (plus the row sums' NQ at each block pair's end), each preceded by the
+// fragment reads of the step AHEAD on, the last AHEAD steps by the scores'
+// first reads instead (NQ KK q fragments and KK K fragments, spread over
+// them); then NB scores blocks of NQ KK products, each preceded by the next
+// block's KK K reads.
+template <bool PV, bool QK, int U, int AHEAD, int TT, int NQ, int NB, int KK, int... I, int... B>
+__device__ __forceinline__ void m_schedule(std::integer_sequence<int, I...>, std::integer_sequence<int, B...>) {
+    constexpr int FIRST_QK = NQ * KK + KK;  // the scores' reads before their first products
+    constexpr int TAIL = (FIRST_QK + AHEAD - 1) / AHEAD;
+    if constexpr (PV) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * AHEAD, 0);
+        auto step = [](auto u) __attribute__((always_inline)) {
+            constexpr int i = decltype(u)::value;
+            if constexpr (i + AHEAD < U) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            else if constexpr (QK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, TAIL, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, i % TT == TT - 1 ? 2 * NQ : NQ, 0);
+        };
+        (step(std::integral_constant<int, I>{}), ...);
+    } else if constexpr (QK) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FIRST_QK, 0);
+    }
+    if constexpr (QK) {
+        auto block = [](auto b) __attribute__((always_inline)) {
+            constexpr int i = decltype(b)::value;
+            if constexpr (i + 1 < NB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, KK, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NQ * KK, 0);
+        };
+        (block(std::integral_constant<int, B>{}), ...);
+    }
 }
 
 // ---- the attention kernel -----------------------------------------------------
@@ -385,6 +393,8 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     using op4_t = typename OPS::op4_t;
     constexpr int RB = SH::RB, CH = SH::CH, KK = SH::KK, TT = SH::TT, NB = SH::NB;
     constexpr int PER_W = SH::PER_W, STEP = SH::STEP;
+    constexpr int PV_STEPS = (NB / 2) * TT;  // products steps (block pair, output tile) per iteration
+    constexpr int PV_AHEAD = 4;              // steps whose V fragments are in flight
     constexpr int Q = kPrefillRows / G;  // chunk tokens per tile
     // Four separate arrays, so the compiler can tell the loads filling one
     // buffer from the reads of another and waits only where they meet.
@@ -557,24 +567,14 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // block gets its products, those past the wave's rows included (their
     // scores stay -inf): a branch around them would put the softmax's first
     // reads of a product's result right after it, closer than its latency.
-    auto scores = [&](const char* kl, int j) __attribute__((always_inline)) {
-        const int key0 = (kb + j) * STEP;
-        const bool msk = masked(j);
-#pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            const int lim = msk ? qpos[c] - key0 - 4 * gq : STEP;  // last visible key offset of this lane
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[c][nb][r] = 16 * nb + r <= lim ? 0.f : -INFINITY;
-        }
+    auto scores = [&](const char* kl) __attribute__((always_inline)) {
         Vec16 qf[NQ][KK];
 #pragma unroll
         for (int c = 0; c < NQ; ++c)
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
                 qf[c][kk] = lds_load16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq));
-        // block nb's K fragments are read AHEAD blocks before its products
+        // block nb's K fragments are read a block before its products
         constexpr int AHEAD = 1;
         Vec16 ka[NB][KK];
         auto fetch = [&](int nb) __attribute__((always_inline)) {
@@ -587,16 +587,32 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
         for (int nb = 0; nb < NB; ++nb) {
             if (nb + AHEAD < NB) fetch(nb + AHEAD);
 #pragma unroll
-            for (int c = 0; c < NQ; ++c)
+            for (int c = 0; c < NQ; ++c) {
+                sc[c][nb] = OPS::qk(ka[nb][0], qf[c][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) sc[c][nb] = OPS::qk(ka[nb][kk], qf[c][kk], sc[c][nb]);
+                for (int kk = 1; kk < KK; ++kk) sc[c][nb] = OPS::qk(ka[nb][kk], qf[c][kk], sc[c][nb]);
+            }
         }
     };
     // Online softmax of the scores: weights in base-2 units against a lazily
     // moved reference maximum m (it moves only when a row's scores pass it by
     // more than kLazy, so weights stay below 2^kLazy and most iterations skip
     // the rescale of O and l).
-    auto softmax = [&]() __attribute__((always_inline)) {
+    auto softmax = [&](int j) __attribute__((always_inline)) {
+        // The prefix-causal mask: a key past the row's position scores -inf
+        // (every key of an unmasked iteration is visible to every row).
+        if (masked(j)) {
+            const int key0 = (kb + j) * STEP;
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                const int lim = qpos[c] - key0 - 4 * gq;  // last visible key offset of this lane
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * nb + r > lim) sc[c][nb][r] = -INFINITY;
+            }
+        }
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
             float mx = -INFINITY;
@@ -633,9 +649,7 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // ahead of their products, so that the reads' latency hides behind them.
     // Also the weights' row sums (a V^T of ones).
     auto products = [&](const char* vl) __attribute__((always_inline)) {
-        constexpr int U = (NB / 2) * TT;       // steps
-        constexpr int AHEAD = 4;               // steps whose fragments are in flight
-        constexpr int MPS = NQ;                // products per step
+        constexpr int U = PV_STEPS, AHEAD = PV_AHEAD;
         const int trow = 4 * gq + jq / 4;
         op4_t fa[U], fb[U];
         auto fetch = [&](int u) __attribute__((always_inline)) {
@@ -661,10 +675,6 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
                 }
             }
         }
-        // Keep that order through scheduling: the first AHEAD steps' reads,
-        // then per step the reads AHEAD steps on and the step's products.
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * AHEAD, 0);
-        pv_schedule<U, AHEAD, TT, MPS>(std::make_integer_sequence<int, U>{});
     };
 
     // Phase M_j (buffer parity b = j % 2): the loads of K_{j+1} (into K
@@ -673,8 +683,8 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // (born there), so weights and scores never hold registers together; the
     // table entries of j + 2.  The K loads go here because this
     // wave's issue slots between its products are free; its partner's are not.
-    Ents ec;     // table entries of iteration j + 1 when M_j starts
-    Blk bl[2];   // where iteration j + 1's halves come from, from M_j to V_j
+    Ents ec;     // table entries of iteration j + 2 when V_j starts
+    Blk bl[2];   // where iteration j + 1's halves come from when V_j starts
     // (M_0 has no products, the last M phase, M_NJ, no scores)
     auto mphase = [&](int j, auto par, auto pv, auto qk) __attribute__((always_inline)) {
         constexpr int b = decltype(par)::value;
@@ -682,19 +692,21 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
         // (the SIMD otherwise favours the older wave, group 0's), and its
         // partner's softmax fills the cycles between the products.
         __builtin_amdgcn_s_setprio(1);
-        place(j + 1, ec, bl);
-        issue(b ? lds_k0 : lds_k1, kbase, bl);
         if constexpr (decltype(pv)::value) products((b ? lds_v0 : lds_v1) + kg * SH::SPAN);
         if constexpr (decltype(qk)::value) {
-            scores((b ? lds_k1 : lds_k0) + kg * SH::SPAN, j);
+            scores((b ? lds_k1 : lds_k0) + kg * SH::SPAN);
 #pragma unroll
             for (int c = 0; c < NQ; ++c)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) pin(sc[c][nb]);
         }
-        // (scalar loads complete out of order with LDS reads: issued any
-        // earlier, they would turn the reads' partial waits into full ones)
-        entries(j + 2, ec);
+        // The phase's order through scheduling: the products' first fragment
+        // reads, then per products step the reads PV_AHEAD steps on (in the
+        // last steps, the scores' q and first K reads) and the step's
+        // products; then per scores block the next block's K reads and the
+        // block's products.
+        m_schedule<decltype(pv)::value, decltype(qk)::value, PV_STEPS, PV_AHEAD, TT, NQ, NB, KK>(
+            std::make_integer_sequence<int, PV_STEPS>{}, std::make_integer_sequence<int, NB>{});
         __builtin_amdgcn_s_setprio(0);
     };
     // Phase V_j: the loads of V_{j+1} into V buffer 1 - b (read by every wave
@@ -702,11 +714,17 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // this wave's loads of V_j and K_{j+1} land (those of V_{j+1} may stay in
     // flight), so that after the barrier the whole group's K_{j+1} and V_j
     // are in LDS.
-    auto vphase = [&](auto par) __attribute__((always_inline)) {
+    auto vphase = [&](int j, auto par) __attribute__((always_inline)) {
         constexpr int b = decltype(par)::value;
+        Blk b2[2];
+        place(j + 2, ec, b2);
+        issue(b ? lds_k1 : lds_k0, kbase, b2);
         issue(b ? lds_v0 : lds_v1, vbase, bl);
-        softmax();
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_W));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bl[h] = b2[h];
+        entries(j + 3, ec);
+        softmax(j);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_W));
     };
 
     using B0 = std::integral_constant<int, 0>;
@@ -718,7 +736,10 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
         issue(lds_k0, kbase, bl);
         issue(lds_v0, vbase, bl);
         entries(1, ec);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_W));
+        place(1, ec, bl);
+        issue(lds_k1, kbase, bl);
+        entries(2, ec);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_W));
     }
     phase_barrier();
     if (kg == 1) phase_barrier();  // group 1 runs one phase behind
@@ -726,23 +747,23 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     using F = std::false_type;
     mphase(0, B0{}, F{}, T{});
     phase_barrier();
-    vphase(B0{});
+    vphase(0, B0{});
     phase_barrier();
     int j = 1;
     for (; j + 1 < NJ; j += 2) {
         mphase(j, B1{}, T{}, T{});
         phase_barrier();
-        vphase(B1{});
+        vphase(j, B1{});
         phase_barrier();
         mphase(j + 1, B0{}, T{}, T{});
         phase_barrier();
-        vphase(B0{});
+        vphase(j + 1, B0{});
         phase_barrier();
     }
     if (j < NJ) {  // j odd
         mphase(j, B1{}, T{}, T{});
         phase_barrier();
-        vphase(B1{});
+        vphase(j, B1{});
         phase_barrier();
     }
     // M_NJ: the last products; then the last phases' zero fills land before
