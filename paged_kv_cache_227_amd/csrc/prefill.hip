@@ -234,73 +234,119 @@ __device__ __forceinline__ int tiles_reaching(int ctx, int n, int K) {
 }
 
 struct TileRef {
-    int s, t;  // sequence (-1: no tile of this rank) and tile index within its chunk
+    int s, t;   // sequence (-1: no tile of this rank) and tile index within its chunk
+    int q0;     // the sequence's first query row
+    int L;      // its context length (clamped to its table)
+    int n;      // its chunk length (the chunk's last n positions of L)
 };
 
 // The rank-th tile in that order, found by the wave alone (every wave of the
-// workgroup computes the same answer): a binary search for the last position
-// of that tile, counting the tiles that reach a position over all sequences
-// (lanes take sequences lane, lane + 64, ...), then its place among the tiles
-// ending there, in sequence order.
+// workgroup computes the same answer): a search for the last position of
+// that tile, counting the tiles that reach a position over all sequences,
+// then its place among the tiles ending there, in sequence order.  Up to 64
+// sequences the lanes test 64 positions per round; beyond, the lanes take
+// sequences lane, lane + 64, ... and the search is four-way (three counts
+// per round, their reductions interleaved).
 template <int Q>
 __device__ TileRef pick_tile(const PrefillParams& p, int rank, int lane, int max_len) {
     const int S = p.num_seqs;
-    // (ctx, n): tokens before the chunk and the chunk tokens computed (the
-    // first max_q_len); an empty or impossible chunk has none.
-    auto info = [&](int s, int& ctx, int& n) __attribute__((always_inline)) {
-        const int L = min(max(p.context_lens[s], 0), max_len);
-        const int nn = p.cu_q[s + 1] - p.cu_q[s];
-        const bool ok = nn > 0 && nn <= L;
-        ctx = ok ? L - nn : 0;
-        n = ok ? min(nn, p.max_q_len) : 0;
+    // Sequence s: first query row q0, context L, chunk nn; (ctx, n): tokens
+    // before the chunk and chunk tokens computed (the first max_q_len); an
+    // empty or impossible chunk has none.
+    struct Seq {
+        int q0, L, nn, ctx, n;
     };
-    int ctx0 = 0, n0 = 0;  // sequence `lane`
-    if (lane < S) info(lane, ctx0, n0);
+    auto info = [&](int s) __attribute__((always_inline)) {
+        Seq q;
+        q.q0 = p.cu_q[s];
+        q.L = min(max(p.context_lens[s], 0), max_len);
+        q.nn = p.cu_q[s + 1] - q.q0;
+        const bool ok = q.nn > 0 && q.nn <= q.L;
+        q.ctx = ok ? q.L - q.nn : 0;
+        q.n = ok ? min(q.nn, p.max_q_len) : 0;
+        return q;
+    };
+    Seq q0{0, 0, 0, 0, 0};  // sequence `lane`
+    if (lane < S) q0 = info(lane);
     auto count = [&](int K) __attribute__((always_inline)) {
-        int c = tiles_reaching<Q>(ctx0, n0, K);
+        int c = tiles_reaching<Q>(q0.ctx, q0.n, K);
         for (int s = kWave + lane; s < S; s += kWave) {
-            int cx, nn;
-            info(s, cx, nn);
-            c += tiles_reaching<Q>(cx, nn, K);
+            const Seq q = info(s);
+            c += tiles_reaching<Q>(q.ctx, q.n, K);
         }
         return wave_sum_i32(c);
     };
-    int last = n0 > 0 ? ctx0 + n0 - 1 : -1;
+    int last = q0.n > 0 ? q0.ctx + q0.n - 1 : -1;
     for (int s = kWave + lane; s < S; s += kWave) {
-        int cx, nn;
-        info(s, cx, nn);
-        if (nn > 0) last = max(last, cx + nn - 1);
+        const Seq q = info(s);
+        if (q.n > 0) last = max(last, q.ctx + q.n - 1);
     }
     last = wave_max_i32(last);
-    if (last < 0 || count(0) <= rank) return {-1, 0};
+    if (last < 0 || count(0) <= rank) return {-1, 0, 0, 0, 0};
     int lo = 0, hi = last + 1;  // count(lo) > rank >= count(hi) = 0
+    int count_hi = 0;
+    if (S <= kWave) {
+        // Every lane holds one sequence, so each lane can count the tiles at
+        // or past a threshold of its own over all of them (the sequences'
+        // values broadcast by readlane): 64 thresholds per round, evenly
+        // spread over (lo, hi); the ones whose count exceeds rank are a
+        // prefix of the lanes.  Two rounds narrow 4096 positions to one.
+        while (hi - lo > 1) {
+            const int T = lo + 1 + (int)(((int64_t)lane * (hi - lo - 1)) >> 6);
+            int c = 0;
+            for (int s = 0; s < S; ++s)
+                c += tiles_reaching<Q>(__builtin_amdgcn_readlane(q0.ctx, s), __builtin_amdgcn_readlane(q0.n, s), T);
+            const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(c > rank));
+            if (k > 0) lo = __builtin_amdgcn_readlane(T, k - 1);
+            if (k < kWave) {
+                hi = __builtin_amdgcn_readlane(T, k);
+                count_hi = __builtin_amdgcn_readlane(c, k);
+            }
+        }
+    }
+    while (hi - lo >= 4) {
+        const int d = hi - lo;
+        const int m1 = lo + d / 4, m2 = lo + d / 2, m3 = lo + (3 * d) / 4;
+        int c1 = tiles_reaching<Q>(q0.ctx, q0.n, m1), c2 = tiles_reaching<Q>(q0.ctx, q0.n, m2),
+            c3 = tiles_reaching<Q>(q0.ctx, q0.n, m3);
+        for (int s = kWave + lane; s < S; s += kWave) {
+            const Seq q = info(s);
+            c1 += tiles_reaching<Q>(q.ctx, q.n, m1);
+            c2 += tiles_reaching<Q>(q.ctx, q.n, m2);
+            c3 += tiles_reaching<Q>(q.ctx, q.n, m3);
+        }
+        c1 = wave_sum_i32(c1);
+        c2 = wave_sum_i32(c2);
+        c3 = wave_sum_i32(c3);
+        if (c3 > rank) lo = m3;
+        else if (c2 > rank) lo = m2, hi = m3, count_hi = c3;
+        else if (c1 > rank) lo = m1, hi = m2, count_hi = c2;
+        else hi = m1, count_hi = c1;
+    }
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (count(mid) > rank) lo = mid;
-        else hi = mid;
+        const int cm = count(mid);
+        if (cm > rank) lo = mid;
+        else hi = mid, count_hi = cm;
     }
-    int r = rank - count(lo + 1);  // place among the tiles ending at lo
+    int r = rank - count_hi;  // place among the tiles ending at lo (hi = lo + 1)
     for (int s0 = 0; s0 < S; s0 += kWave) {
         const int s = s0 + lane;
-        int cx = ctx0, nn = n0;
-        if (s0 > 0) {
-            cx = 0;
-            nn = 0;
-            if (s < S) info(s, cx, nn);
-        }
-        const bool has = s < S && tiles_reaching<Q>(cx, nn, lo) > tiles_reaching<Q>(cx, nn, lo + 1);
+        Seq q = q0;
+        if (s0 > 0) q = s < S ? info(s) : Seq{0, 0, 0, 0, 0};
+        const bool has = s < S && tiles_reaching<Q>(q.ctx, q.n, lo) > tiles_reaching<Q>(q.ctx, q.n, lo + 1);
         uint64_t m = __builtin_amdgcn_ballot_w64(has);
         const int cnt = __builtin_popcountll(m);
         if (r < cnt) {
             for (int k = 0; k < r; ++k) m &= m - 1;
-            const int sp = s0 + __builtin_ctzll(m);
-            int cp, np;
-            info(sp, cp, np);
-            return {sp, (np + Q - 1) / Q - tiles_reaching<Q>(cp, np, lo)};
+            const int sl = __builtin_ctzll(m);  // the lane holding it
+            const int ctx = __builtin_amdgcn_readlane(q.ctx, sl), n = __builtin_amdgcn_readlane(q.n, sl);
+            return {s0 + sl, (n + Q - 1) / Q - tiles_reaching<Q>(ctx, n, lo), __builtin_amdgcn_readlane(q.q0, sl),
+                    __builtin_amdgcn_readlane(q.L, sl), __builtin_amdgcn_readlane(q.nn, sl)};
         }
         r -= cnt;
     }
-    return {-1, 0};
+    return {-1, 0, 0, 0, 0};
 }
 
 // The softmax weights as 16-bit matrix-core operands, four per lane and
@@ -417,12 +463,34 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     const int rank = blockIdx.x / Hkv + p.num_seqs * blockIdx.y;
     const int lane = threadIdx.x % kWave;
     const int max_len = p.max_blocks << p.block_shift;
-    const TileRef tr = pick_tile<Q>(p, rank, lane, max_len);
+    // One wave finds the tile (two waves share each SIMD, so eight copies of
+    // the search would take twice as long) and hands it to the others through
+    // LDS: the start of the last V buffer, whose first load comes phases later.
+    TileRef tr;
+    {
+        int* sh = reinterpret_cast<int*>(lds_v1);
+        if (wave_id_uniform() == 0) {
+            tr = pick_tile<Q>(p, rank, lane, max_len);
+            if (lane == 0) {
+                sh[0] = tr.s;
+                sh[1] = tr.t;
+                sh[2] = tr.q0;
+                sh[3] = tr.L;
+                sh[4] = tr.n;
+            }
+        }
+        __syncthreads();
+        tr.s = __builtin_amdgcn_readfirstlane(sh[0]);
+        tr.t = __builtin_amdgcn_readfirstlane(sh[1]);
+        tr.q0 = __builtin_amdgcn_readfirstlane(sh[2]);
+        tr.L = __builtin_amdgcn_readfirstlane(sh[3]);
+        tr.n = __builtin_amdgcn_readfirstlane(sh[4]);
+    }
     if (tr.s < 0) return;
     const int s = tr.s;
-    const int q0 = p.cu_q[s];
-    const int n = p.cu_q[s + 1] - q0;
-    const int L = min(max(p.context_lens[s], 0), max_len);
+    const int q0 = tr.q0;
+    const int n = tr.n;
+    const int L = tr.L;
     const int Hq = p.n_q_heads;
     const int nrows = min(n, p.max_q_len) * G;  // rows computed
     const int r0 = tr.t * SH::ROWS;
@@ -453,28 +521,22 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // is far below half an ulp of 1 for any 16-bit q and K).
     const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     const float scale_log2 = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
-    // q rows of this wave: group c, column jq is row wr0 + 16c + jq.
     // q rows of this wave: group c, column jq is row wr0 + 16c + jq (row
-    // 32w + 16c + jq of the tile); group 0's waves put them in LDS (rows past
-    // the chunk as zeros), the first barrier publishes them.
+    // 32w + 16c + jq of the tile); group 0's waves load them here and put
+    // them in LDS in the prologue (rows past the chunk as zeros), once the
+    // first K and V loads are under way; the first barrier publishes them.
     int qpos[NQ];
+    Vec16 qv[NQ][KK];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
         const int row = wr0 + 16 * c + jq;
         const bool ok = row < nrows;
         const int tok = row / G;
         qpos[c] = ok ? ctx + tok : -1;
-        if (kg == 0) {
-            const char* qrow = static_cast<const char*>(p.q) +
-                               (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
+        const char* qrow = static_cast<const char*>(p.q) + (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                Vec16 v = ok ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v.w[e] ^= qsign;
-                lds_store16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq), v);
-            }
-        }
+        for (int kk = 0; kk < KK; ++kk)
+            qv[c][kk] = ok && kg == 0 ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
     }
     // Row state: reference maximum m, output acc and the weights' sum, which
     // the matrix core accumulates too (the product with a V^T of ones puts
@@ -516,13 +578,11 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
     const int tt0 = kb * STEP + w * kBlock;  // first token of the wave's tile in the group's iteration 0
     uint32_t voff[PER_W];
-    uint32_t ldso[PER_W];  // the slice's byte offset in an LDS buffer
 #pragma unroll
     for (int k = 0; k < PER_W; ++k) {
         const int row = k * SH::RPR + lane / CH;  // row in the tile
         voff[k] = (uint32_t)(((tt0 + k * SH::RPR) & (bsize - 1)) + lane / CH) * row_stride +
                   (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
-        ldso[k] = (uint32_t)(kg * SH::SPAN + w * SH::TILE + k * 1024);
     }
     // halves past the workgroup's last tile, or past the sequence's last table entry, load nothing
     const int tok_lim = min(nblk * kBlock, (L + bsize - 1) & -bsize);
@@ -551,11 +611,17 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
             bl[h].size = ok ? min(L - (tok & -bsize), bsize) * (int)row_stride : 0;
         }
     };
+    // (The slice's LDS offset is formed at each use from one opaque value:
+    // left to itself the compiler would keep an offset per buffer and slice
+    // in scalar registers, which it has too few of here.)
+    const uint32_t wslot = (uint32_t)(kg * SH::SPAN + w * SH::TILE);
     auto issue = [&](char* buf, const char* base, const Blk (&bl)[2]) __attribute__((always_inline)) {
+        uint32_t ws = wslot;
+        asm volatile("" : "+s"(ws));
 #pragma unroll
         for (int k = 0; k < PER_W; ++k) {
             const Blk& b = bl[(k * SH::RPR) / 8];
-            lds_load_1k(base + b.off, b.size, buf + ldso[k], voff[k]);
+            lds_load_1k(base + b.off, b.size, buf + ws + k * 1024, voff[k]);
         }
     };
 
@@ -601,6 +667,9 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     auto softmax = [&](int j) __attribute__((always_inline)) {
         // The prefix-causal mask: a key past the row's position scores -inf
         // (every key of an unmasked iteration is visible to every row).
+        // Branch-free and without compares (whose lane masks would each take
+        // a scalar register pair): the sign of lim - key picks +inf or -inf,
+        // and the score takes the smaller of itself and that.
         if (masked(j)) {
             const int key0 = (kb + j) * STEP;
 #pragma unroll
@@ -609,8 +678,10 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (16 * nb + r > lim) sc[c][nb][r] = -INFINITY;
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t sign = (uint32_t)(lim - (16 * nb + r)) & 0x80000000u;
+                        sc[c][nb][r] = fminf(sc[c][nb][r], __uint_as_float(sign | 0x7f800000u));
+                    }
             }
         }
 #pragma unroll
@@ -729,16 +800,29 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    // Prologue: K_0 and V_0; K_0 (and q) land before the first barrier.
+    // Prologue: the loads of K_0, V_0 and K_1, then q into LDS; K_0 (and q)
+    // land before the first barrier.
     {
+        Ents e1;
         entries(0, ec);
+        entries(1, e1);
         place(0, ec, bl);
         issue(lds_k0, kbase, bl);
         issue(lds_v0, vbase, bl);
-        entries(1, ec);
-        place(1, ec, bl);
+        place(1, e1, bl);
         issue(lds_k1, kbase, bl);
         entries(2, ec);
+        if (kg == 0) {
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    Vec16 v = qv[c][kk];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v.w[e] ^= qsign;
+                    lds_store16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq), v);
+                }
+        }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_W));
     }
     phase_barrier();
