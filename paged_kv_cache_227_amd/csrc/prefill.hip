@@ -10,8 +10,8 @@
 // (position L-n+j) attends to positions 0 .. L-n+j: the whole earlier context
 // and the chunk up to itself.  With n = 1 this is a decode step.
 //
-// n-token append: workgroup x copies new row x (of all sequences' packed rows)
-// into the slot of its position, found through the block table.
+// n-token append: new row x (of all sequences' packed rows) goes to the slot
+// of its position, found through the block table; a wave per row.
 //
 // Attention: unlike decode, a chunk makes QK^T and PV real matrix products
 // (n x G query rows against every key), so the work runs on the matrix cores.
@@ -50,48 +50,60 @@ namespace pkv {
 
 // ---- n-token append ---------------------------------------------------------
 
+// One wave per new row (its K and its V row), four rows per workgroup: the
+// wave finds the row's sequence (a binary search of cu_new through the
+// scalar cache; every lane agrees), then copies VB bytes per lane and pass.
+constexpr int kAppendRowsPerBlock = 4;
+
 template <int VB>
-__global__ __launch_bounds__(256) void append_tokens_kernel(AppendTokensParams p) {
-    const int x = blockIdx.x;
+__global__ __launch_bounds__(kAppendRowsPerBlock * kWave) void append_tokens_kernel(AppendTokensParams p) {
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    const cint* cu = (const cint*)p.cu_new;
+    const int x = blockIdx.x * kAppendRowsPerBlock + wave_id_uniform();
+    const int lane = threadIdx.x % kWave;
     const int S = p.num_seqs;
-    if (x >= p.cu_new[S] || p.cu_new[0] > x) return;
+    if (x >= cu[S] || cu[0] > x) return;
     // the sequence owning row x: cu_new[s] <= x < cu_new[s + 1]
     int lo = 0, hi = S;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (p.cu_new[mid] <= x) lo = mid;
+        if (cu[mid] <= x) lo = mid;
         else hi = mid;
     }
     const int s = lo;
-    const int64_t pos = (int64_t)p.start_pos[s] + (x - p.cu_new[s]);
-    if (p.start_pos[s] < 0 || pos < 0 || pos / p.block_size >= p.max_blocks) return;
-    const int blk = p.block_tables[(int64_t)s * p.max_blocks + pos / p.block_size];
+    const int sp = ((const cint*)p.start_pos)[s];
+    const int64_t pos = (int64_t)sp + (x - cu[s]);
+    if (sp < 0 || pos < 0 || pos / p.block_size >= p.max_blocks) return;
+    const int blk = ((const cint*)p.block_tables)[(int64_t)s * p.max_blocks + pos / p.block_size];
     if (blk < 0 || blk >= p.num_blocks) return;
     const int64_t slot = (int64_t)blk * p.block_size + pos % p.block_size;
-    const bool is_v = blockIdx.y != 0;
-    const char* src = static_cast<const char*>(is_v ? p.v_new : p.k_new) + (int64_t)x * p.row_bytes;
-    char* dst = static_cast<char*>(is_v ? p.v_cache : p.k_cache) + slot * p.row_bytes;
-    for (int off = threadIdx.x * VB; off < p.row_bytes; off += blockDim.x * VB) {
-        if constexpr (VB == 16) {
-            const v4u32_t v = *reinterpret_cast<const v4u32_t*>(src + off);
-            *reinterpret_cast<v4u32_t*>(dst + off) = v;
-        } else if constexpr (VB == 4) {
-            *reinterpret_cast<uint32_t*>(dst + off) = *reinterpret_cast<const uint32_t*>(src + off);
-        } else {
-            *reinterpret_cast<uint16_t*>(dst + off) = *reinterpret_cast<const uint16_t*>(src + off);
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+        const char* src = static_cast<const char*>(kv ? p.v_new : p.k_new) + (int64_t)x * p.row_bytes;
+        char* dst = static_cast<char*>(kv ? p.v_cache : p.k_cache) + slot * p.row_bytes;
+        for (int off = lane * VB; off < p.row_bytes; off += kWave * VB) {
+            if constexpr (VB == 16) {
+                const v4u32_t v = *reinterpret_cast<const v4u32_t*>(src + off);
+                *reinterpret_cast<v4u32_t*>(dst + off) = v;
+            } else if constexpr (VB == 4) {
+                *reinterpret_cast<uint32_t*>(dst + off) = *reinterpret_cast<const uint32_t*>(src + off);
+            } else {
+                *reinterpret_cast<uint16_t*>(dst + off) = *reinterpret_cast<const uint16_t*>(src + off);
+            }
         }
     }
 }
 
 hipError_t launch_append_tokens(const AppendTokensParams& p, hipStream_t stream) {
     if (p.total <= 0 || p.num_seqs <= 0) return hipSuccess;
-    const dim3 grid(p.total, 2);
+    const dim3 grid((p.total + kAppendRowsPerBlock - 1) / kAppendRowsPerBlock);
+    const dim3 block(kAppendRowsPerBlock * kWave);
     if (p.row_bytes % 16 == 0)
-        hipLaunchKernelGGL(append_tokens_kernel<16>, grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(append_tokens_kernel<16>, grid, block, 0, stream, p);
     else if (p.row_bytes % 4 == 0)
-        hipLaunchKernelGGL(append_tokens_kernel<4>, grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(append_tokens_kernel<4>, grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL(append_tokens_kernel<2>, grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(append_tokens_kernel<2>, grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
