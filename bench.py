@@ -53,11 +53,39 @@ def log(*a):
 COPY_KERNEL_SOURCES = ["paged_kv_cache_227_amd/csrc/copy_blocks.hip"]
 
 
+def code_tokens(text):
+    """C++ source with its comments removed and each run of whitespace made one
+    space: an edit to comments or layout leaves it unchanged, any change to the
+    code does not."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash(sources=None):
+    """Hash of the kernel sources' code (comments and layout excluded), which keys
+    the stored counter summaries to the code they were taken on."""
     h = hashlib.sha256()
     for p in sources or KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -36,12 +36,19 @@
 //     contiguous ranges, so every wave does the same number of tiles whatever
 //     the length mix.  Segments are cut where a range ends; segment (pair j,
 //     wave w) keeps its record at index j + w, unique because j + w grows by
-//     at least one from one segment to the next.
-//   * fixed partitions: one wave per (P-token partition, head group,
-//     sequence), NW consecutive partitions of one sequence per workgroup;
-//     each wave writes its partition's record (or the output, for a
-//     sequence with one partition) and a workgroup per (sequence, query head)
-//     merges the records.
+//     at least one from one segment to the next.  With the matrix-core engine
+//     the unit is a team: up to 8 waves of a workgroup, one KV head each,
+//     walking the same blocks in lockstep (the stream is then ordered by
+//     sequence, block of team heads, block).
+//   * fixed partitions (P tokens each): every partition of every (sequence,
+//     head group) is computed on its own and writes its record (or the
+//     output, for a sequence with one partition); a workgroup per (sequence,
+//     query head) merges the records.  The matrix-core engine runs a
+//     persistent grid over balanced ranges of (sequence, partition, team)
+//     units, each partition split between two key groups that meet in LDS,
+//     records staged in LDS and written four at a time; the vector engine,
+//     and batches whose unit prefix does not fit LDS, run one workgroup per
+//     NW partitions.  Both give the same bits.
 //
 // Everything is bound by HBM bandwidth: each (token, KV head) costs
 // 2 * head_dim * element bytes of reads and 4 * head_dim * G flops.

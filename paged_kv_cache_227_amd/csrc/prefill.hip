@@ -26,11 +26,11 @@
 //     K, two for V, 16-byte chunks XOR-swizzled by row);
 //   * an iteration is two phases between workgroup barriers: M, all matrix
 //     products (S^T = K Q^T of this iteration, O^T += V^T P^T of the one
-//     before, v_mfma_f32_16x16x32), and V, all vector work (the online softmax
-//     per row in base-2 units with a lazily moved reference maximum, the
-//     prefix-causal mask having entered the score products as their initial
-//     value); group 1 runs one phase behind group 0 and each SIMD holds one
-//     wave of each, so one wave's products overlap the other's softmax;
+//     before, v_mfma_f32_16x16x32), and V, all vector work (the prefix-causal
+//     mask, the online softmax per row in base-2 units with a lazily moved
+//     reference maximum, and the loads of later iterations); group 1 runs one
+//     phase behind group 0 and each SIMD holds one wave of each, so one
+//     wave's products overlap the other's softmax;
 //   * the row sums come from the matrix core too, from the same rounded
 //     weights as the outputs;
 //   * the key groups' softmax states meet in LDS at the end (the decode merge's
@@ -432,17 +432,17 @@ __device__ __forceinline__ void m_schedule(std::integer_sequence<int, I...>, std
 // group 1 the rest) and runs them as alternating phases, each ending at a
 // workgroup barrier:
 //   M_j: the output products of iteration j - 1 (O^T += V^T P^T, from V_{j-1}
-//        in LDS), the scores of iteration j (S^T = K Q^T, from K_j), and the
-//        loads of K_{j+1},
-//   V_j: the softmax of iteration j's scores (weights P_j, the lazy rescale of
-//        O and l) and the loads of V_{j+1},
+//        in LDS) and the scores of iteration j (S^T = K Q^T, from K_j),
+//   V_j: the loads of K_{j+2} and V_{j+1}, the causal mask and the softmax of
+//        iteration j's scores (weights P_j, the lazy rescale of O and l),
 // M_j all matrix-core work, V_j all vector work.  Group 1 runs one phase
 // behind group 0, and each SIMD holds one wave of each group (waves w and
 // w + 4 share a SIMD), so while one wave's products run on the matrix core
 // the other wave's softmax runs on the vector ALU.  K and V have two LDS
-// buffers each per group: K_j lives in K buffer j % 2 from M_{j-1} to M_j,
-// V_j in V buffer j % 2 from V_{j-1} to M_{j+1}; each wave waits (vmcnt) for
-// its own loads at the end of the V phase before their reader.
+// buffers each per group: K_j lives in K buffer j % 2 from V_{j-2} to M_j,
+// V_j in V buffer j % 2 from V_{j-1} to M_{j+1}, so every load is issued
+// three phases before its first reader; each wave waits (vmcnt) for its own
+// loads at the end of the V phase before their reader.
 template <class E, int D, int G, int NW, int NQ>
 __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(PrefillParams p) {
     using SH = PrefillShape<D, NW, NQ>;
@@ -640,11 +640,10 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     f32x4_t sc[NQ][NB];            // scores of an iteration, from its M phase to its V phase
     op4_t ph[NQ][NB];              // its weights, from its V phase to the next M
     // S^T = K Q^T of iteration j: lane (gq, jq) holds keys 16 nb + 4 gq + r of
-    // row column jq.  MASK builds the prefix-causal mask into the products'
-    // initial value (0, or -inf for a key past the row's position).  Every
-    // block gets its products, those past the wave's rows included (their
-    // scores stay -inf): a branch around them would put the softmax's first
-    // reads of a product's result right after it, closer than its latency.
+    // row column jq.  Every block gets its products, those past the wave's
+    // rows included (the softmax masks them): a branch around them would put
+    // the first reads of a product's result right after it, closer than its
+    // latency.
     auto scores = [&](const char* kl) __attribute__((always_inline)) {
         Vec16 qf[NQ][KK];
 #pragma unroll
@@ -728,9 +727,9 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // takes key row 4gq + jq/4, bytes 32t + 8(jq%4).  Blocks nb and nb + 1 make
     // one 16x16x32 product: contraction slots 0-3 are keys 4gq + r of block
     // nb, slots 4-7 those of block nb + 1, in V^T and P^T alike.  The
-    // fragments of step u (pair u / TT, output tile u % TT) are read two steps
-    // ahead of their products, so that the reads' latency hides behind them.
-    // Also the weights' row sums (a V^T of ones).
+    // fragments of step u (pair u / TT, output tile u % TT) are read AHEAD
+    // steps ahead of their products, so that the reads' latency hides behind
+    // them.  Also the weights' row sums (a V^T of ones).
     auto products = [&](const char* vl) __attribute__((always_inline)) {
         constexpr int U = PV_STEPS, AHEAD = PV_AHEAD;
         const int trow = 4 * gq + jq / 4;
@@ -760,12 +759,10 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
         }
     };
 
-    // Phase M_j (buffer parity b = j % 2): the loads of K_{j+1} (into K
-    // buffer 1 - b, last read in M_{j-1}); the products of j - 1 from V
-    // buffer 1 - b (their weights die there); the scores of j from K buffer b
-    // (born there), so weights and scores never hold registers together; the
-    // table entries of j + 2.  The K loads go here because this
-    // wave's issue slots between its products are free; its partner's are not.
+    // Phase M_j (buffer parity b = j % 2): the products of j - 1 from V
+    // buffer 1 - b (their weights die there), then the scores of j from K
+    // buffer b (born there), so weights and scores never hold registers
+    // together.
     Ents ec;     // table entries of iteration j + 2 when V_j starts
     Blk bl[2];   // where iteration j + 1's halves come from when V_j starts
     // (M_0 has no products, the last M phase, M_NJ, no scores)
@@ -792,11 +789,12 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
             std::make_integer_sequence<int, PV_STEPS>{}, std::make_integer_sequence<int, NB>{});
         __builtin_amdgcn_s_setprio(0);
     };
-    // Phase V_j: the loads of V_{j+1} into V buffer 1 - b (read by every wave
-    // of the group in M_j, so not before this phase), the softmax of j; then
-    // this wave's loads of V_j and K_{j+1} land (those of V_{j+1} may stay in
-    // flight), so that after the barrier the whole group's K_{j+1} and V_j
-    // are in LDS.
+    // Phase V_j: the loads of K_{j+2} into K buffer b (last read by the
+    // group's scores in M_j) and of V_{j+1} into V buffer 1 - b (last read by
+    // the products in M_j), the table entries of j + 3, the softmax of j;
+    // then this wave's loads of K_{j+1} and V_j, issued in V_{j-1}, land
+    // (this phase's stay in flight), so that after the barrier the whole
+    // group's K_{j+1} and V_j are in LDS.
     auto vphase = [&](int j, auto par) __attribute__((always_inline)) {
         constexpr int b = decltype(par)::value;
         Blk b2[2];
