@@ -161,6 +161,20 @@ __device__ __forceinline__ int scalar_entry(const int32_t* table, int i) {
     return ((prefill_const_i32*)table)[__builtin_amdgcn_readfirstlane(i)];
 }
 
+// The larger of two scores.  IEEE maximum (NaN-propagating) lowers to
+// v_maximum3_f32 with no canonicalising max on inputs the compiler cannot
+// prove canonical (lane exchange results, selects), which fmaxf needs; the
+// scores are never NaN, so the two agree.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// The maximum over the four 16-lane rows' matching lanes (rows_max with smax).
+__device__ __forceinline__ float rows_smax(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = smax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return smax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Headroom of the online softmax's reference maximum (log2 units): weights
 // reach at most 2^8, well inside fp16 and bf16 range.
 constexpr float kLazy = 8.f;
@@ -677,10 +691,11 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // the rescale of O and l).
     auto softmax = [&](int j) __attribute__((always_inline)) {
         // The prefix-causal mask: a key past the row's position scores -inf
-        // (every key of an unmasked iteration is visible to every row).
-        // Branch-free and without compares (whose lane masks would each take
-        // a scalar register pair): the sign of lim - key picks +inf or -inf,
-        // and the score takes the smaller of itself and that.
+        // (every key of an unmasked iteration is visible to every row).  A
+        // bitwise select on the sign of lim - key, which the compiler turns
+        // into a compare and a select through VCC one element at a time
+        // (compares hoisted ahead of their selects would each hold a scalar
+        // register pair).
         if (masked(j)) {
             const int key0 = (kb + j) * STEP;
 #pragma unroll
@@ -690,21 +705,29 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const uint32_t sign = (uint32_t)(lim - (16 * nb + r)) & 0x80000000u;
-                        sc[c][nb][r] = fminf(sc[c][nb][r], __uint_as_float(sign | 0x7f800000u));
+                        const uint32_t msk = (uint32_t)((lim - (16 * nb + r)) >> 31);
+                        sc[c][nb][r] = __uint_as_float((msk & 0xff800000u) | (~msk & __float_as_uint(sc[c][nb][r])));
                     }
             }
         }
+        // each lane's largest score of each row group, as a tree
+        float mx[NQ];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-            float mx = -INFINITY;
+            float t4[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
+                t4[nb] = smax(smax(sc[c][nb][0], sc[c][nb][1]), smax(sc[c][nb][2], sc[c][nb][3]));
+            mx[c] = smax(smax(t4[0], t4[1]), smax(t4[2], t4[3]));
+            static_assert(NB == 4, "the tree above");
+        }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[c][nb][r]);
-            mx = rows_max(mx);
-            const float mn = mx * scale_log2;  // the row's largest scaled score here
-            if (__builtin_amdgcn_ballot_w64(mn > m[c] + kLazy)) {
+        for (int c = 0; c < NQ; ++c) {
+            // The reference moves when some row's largest scaled score passes
+            // it by more than kLazy, i.e. when some lane's does: the row's
+            // maximum over its four lanes is needed only then.
+            if (__builtin_amdgcn_ballot_w64(mx[c] * scale_log2 > m[c] + kLazy)) {
+                const float mn = rows_smax(mx[c]) * scale_log2;  // the row's largest scaled score here
                 const float nm = fmaxf(m[c], mn);
                 const float alpha = __builtin_amdgcn_exp2f(m[c] - (nm == -INFINITY ? 0.f : nm));
                 lsum[c] *= alpha;
