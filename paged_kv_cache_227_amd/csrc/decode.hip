@@ -840,23 +840,30 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     __syncthreads();
     const int T = pre[S];
     const int NT = gridDim.x * (TU::NW / TS);  // teams in the grid
+    // Teams 2j and 2j + 1 share the 2 per tiles [2j per, 2(j + 1) per) of the
+    // stream, the first taking X of them: per each when split_pct is 50.  A
+    // workgroup of 8 waves in two teams of 4 holds teams 2j (waves 0-3) and
+    // 2j + 1 (waves 4-7); the second wave of each SIMD streams more slowly
+    // (the first is older, so it issues first), so the first team takes more.
     const int per = max((T + NT - 1) / NT, p.min_tiles_per_worker);
+    const int P2 = 2 * per;
+    const int X = (int)((int64_t)P2 * p.split_pct / 100);
     if (blockIdx.x == 0) {  // the schedule, for the merge pass
         if (threadIdx.x == 0) {
-            p.ws_hdr[0] = per;
-            p.ws_hdr[1] = T;
+            p.ws_hdr[0] = P2;
+            p.ws_hdr[1] = X;
         }
         for (int i = threadIdx.x; i <= S; i += blockDim.x) p.ws_hdr[2 + i] = pre[i];
     }
 
-    // Team `team` takes tiles [team * per, (team + 1) * per) of the stream; its
-    // wave tj streams head group hb * TS + tj of each tile (sequence, hb, block),
-    // so the team's waves read the same blocks at the same time.
+    // Team `team` takes its share of the stream; its wave tj streams head
+    // group hb * TS + tj of each tile (sequence, hb, block), so the team's
+    // waves read the same blocks at the same time.
     const int w = blockIdx.x * TU::NW + wave_id_uniform();
     const int team = w / TS;
     const int tj = w - team * TS;
-    const int t0 = team * per;
-    const int t1 = min(t0 + per, T);
+    const int t0 = min((team >> 1) * P2 + (team & 1 ? X : 0), T);
+    const int t1 = min((team >> 1) * P2 + (team & 1 ? P2 : X), T);
     if (t0 >= T) return;
 
     const int lane = threadIdx.x % kWave;
@@ -1000,7 +1007,9 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         a.reduce();
         const int nb = (aL + kBlock - 1) / kBlock;
         const int p0 = pre[as] + akvh * nb;  // the pair's tiles are [p0, p0 + nb)
-        const bool whole = p0 / per == (p0 + nb - 1) / per;
+        // the team holding tile t
+        auto piece = [&](int t) { return 2 * (t / P2) + (t % P2 >= X ? 1 : 0); };
+        const bool whole = piece(p0) == piece(p0 + nb - 1);
         // split pairs: record (pair + team) * TS + tj, unique because pair + team
         // grows by at least one from one segment of a wave to the next
         const int64_t dst = whole ? (int64_t)as * Hq + (akvh * TS + tj) * A::HG
@@ -1174,11 +1183,12 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
             if (lane + k * kWave < D) E::store(out_row + (lane + k * kWave) * E::kBytes, 0.f);
         return;
     }
-    const int per = p.ws_hdr[0];
+    const int P2 = p.ws_hdr[0], X = p.ws_hdr[1];  // teams 2j, 2j + 1 hold [2j P2/2 ..), split at X
+    auto piece = [&](int t) { return 2 * (t / P2) + (t % P2 >= X ? 1 : 0); };
     const int nb = (L + kBlock - 1) / kBlock;
     const int p0 = p.ws_hdr[2 + s] + hb * nb;
-    const int w0 = p0 / per;  // teams w0 .. w1 hold the pair's tiles
-    const int w1 = (p0 + nb - 1) / per;
+    const int w0 = piece(p0);  // teams w0 .. w1 hold the pair's tiles
+    const int w1 = piece(p0 + nb - 1);
     if (w0 == w1) return;  // one wave held the whole pair and wrote it
     const int64_t base = (int64_t)s * NGB + hb;  // record of team w is (base + w) * TS + tj
     merge_records<E, D>(p.ws_ml, p.ws_acc, ((base + w0) * TS + tj) * HG + gi, TS * HG, w1 - w0 + 1, out_row);
@@ -1687,16 +1697,24 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 // row, so one load instruction reads two tokens x 512 contiguous bytes at
 // D = 128); fp32 caches one head per wave.  NH1 is the one-head shape used
 // when the KV head count is odd (it must match `type` in everything but NH).
+// Share of a workgroup's tiles taken by its first team (waves 0-3) when its
+// 8 waves form two teams of 4 (see decode_flat_kernel).  Measured on the
+// GQA-8B, copied-prefix and long-context layers: 50 % (equal shares) 5.85,
+// 5.89, 6.39 TB/s; 58 %: 5.95, 6.01, 6.53; 62 %: 6.02, 6.09, 6.65; 66 %: 5.97,
+// 6.10, 6.64; 70 %: 5.90, 6.04, 6.48 (one team of 8 waves: 5.85, 5.86,
+// 6.50).
+constexpr int kSplitPct = 62;
+
 template <class E, int D, int G>
 struct DefaultTune {
     static constexpr bool kMfma = E::kBytes == 2 && G >= 4;
     static constexpr int kCH = D * E::kBytes / 16;
     static constexpr int kR = kCH < 16 ? kCH : 16;
     static constexpr int kNH = E::kBytes == 2 && !kMfma ? 2 : 1;
-    // matrix-core engine: teams of up to 8 waves (one workgroup) stream the
-    // KV heads of the same blocks together
-    using mfma_flat = typename std::conditional<(G >= 8), Tune<8, 8, 1, true, true, 1, 0, 8>,
-                                                Tune<8, 8, 1, true, true, 1, 0, 8>>::type;
+    // matrix-core engine: 8-wave workgroups in two teams of 4 (each team
+    // streams 4 KV heads of the same blocks together), the first taking
+    // kSplitPct of the pair's tiles
+    using mfma_flat = Tune<8, 8, 1, true, true, 1, 0, 4>;
     // fp32 with G >= 4 spreads a head row over more lanes: fewer accumulators per lane
     static constexpr int kRf = E::kBytes == 4 && G >= 4 ? kR : 8;
     // 16-bit, two KV heads a wave: one 4-wave workgroup per CU (one wave per
@@ -1796,6 +1814,8 @@ hipError_t launch_flat_tuned(const DecodeParams& pin, hipStream_t stream) {
     DecodeParams p = pin;
     p.heads_per_wave = A::NH;
     p.team = team_size<TU>(p.n_kv_heads / A::NH);
+    // the first of two teams of a workgroup takes this share of their tiles
+    p.split_pct = TU::NW / p.team == 2 ? kSplitPct : 50;
     // The grid is sized from the kernel without the fused append, and the fused
     // kernel gets the same grid: the tiles are then dealt alike and both give
     // the same bits.  (Its waves do not wait on one another, so a grid larger

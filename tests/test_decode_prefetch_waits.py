@@ -28,9 +28,9 @@ CASES = {
     "flat with the append fused, f16, head_dim 128, one query head per KV head (vector engine)":
         (r"decode_flat_kernelINS_3F16ELi128ELi1ENS_4TuneILi4ELi16ELi1ELb1ELb0ELi2ELi1ELi1ELi1EEELb1E", 16),
     "flat, bf16, head_dim 128, four query heads per KV head (matrix-core engine)":
-        (r"decode_flat_kernelINS_4BF16ELi128ELi4ENS_4TuneILi8ELi8ELi1ELb1ELb1ELi1ELi0ELi8ELi1EEELb0E", 8),
+        (r"decode_flat_kernelINS_4BF16ELi128ELi4ENS_4TuneILi8ELi8ELi1ELb1ELb1ELi1ELi0ELi4ELi1EEELb0E", 8),
     "flat, bf16, head_dim 128, eight query heads per KV head (matrix-core engine)":
-        (r"decode_flat_kernelINS_4BF16ELi128ELi8ENS_4TuneILi8ELi8ELi1ELb1ELb1ELi1ELi0ELi8ELi1EEELb0E", 8),
+        (r"decode_flat_kernelINS_4BF16ELi128ELi8ENS_4TuneILi8ELi8ELi1ELb1ELb1ELi1ELi0ELi4ELi1EEELb0E", 8),
     "fixed partitions, bf16, head_dim 128, eight query heads per KV head (matrix-core engine)":
         (r"decode_partition_persistent_kernelINS_4BF16ELi128ELi8ENS_4TuneILi8ELi8ELi1ELb1ELb1ELi1ELi0ELi4ELi2E", 8),
 }
