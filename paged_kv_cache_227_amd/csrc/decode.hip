@@ -802,6 +802,18 @@ __device__ __forceinline__ void write_staged(const float* slots, int n, const De
 // Flat schedule: a persistent grid deals equal ranges of the tile stream.
 // ============================================================================
 
+// The flat schedule's team offsets in a period of Q = 2 TW teams (the TW
+// teams of two consecutive workgroups) of P tiles: team q takes
+// [flat_offset(q), flat_offset(q + 1)).  Weights: the first workgroup of the
+// pair xcd, the second 100 - xcd; in a workgroup of two teams, the first
+// split and the second 100 - split, else all alike.
+__device__ __forceinline__ int flat_offset(int q, int TW, int P, int split, int xcd) {
+    auto in_wg = [&](int n) { return TW == 2 ? (n <= 0 ? 0 : n == 1 ? split : 100) : 50 * n; };
+    const int64_t cum = (int64_t)xcd * in_wg(min(q, TW)) + (int64_t)(100 - xcd) * in_wg(max(q - TW, 0));
+    const int64_t tot = (int64_t)100 * in_wg(TW);
+    return (int)(P * cum / tot);
+}
+
 template <class E, int D, int G, class TU, bool FUSED, class A = Engine<E, D, G, TU>>
 __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParams p) {
     constexpr int NS = A::NS;
@@ -840,19 +852,25 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     __syncthreads();
     const int T = pre[S];
     const int NT = gridDim.x * (TU::NW / TS);  // teams in the grid
-    // Teams 2j and 2j + 1 share the 2 per tiles [2j per, 2(j + 1) per) of the
-    // stream, the first taking X of them: per each when split_pct is 50.  A
-    // workgroup of 8 waves in two teams of 4 holds teams 2j (waves 0-3) and
-    // 2j + 1 (waves 4-7); the second wave of each SIMD streams more slowly
-    // (the first is older, so it issues first), so the first team takes more.
+    // The stream is dealt out in periods of Q = 2 NW / TS teams, the teams of
+    // two consecutive workgroups: period j holds tiles [j P, (j + 1) P) and
+    // team j Q + q takes [j P + off[q], j P + off[q + 1]) of it, off in
+    // proportion to integer weights.  Waves given equal shares do not finish
+    // together: workgroups are dealt to the XCDs round-robin, and the odd
+    // XCDs stream more slowly than the even ones (xcd_pct: the even
+    // workgroup's share of a pair); and in a workgroup of two teams of 4 the
+    // second wave of each SIMD (waves 4-7) streams more slowly than the first,
+    // which is older and issues first (split_pct: the first team's share).
+    const int TW = TU::NW / TS;  // teams per workgroup
+    const int Q = 2 * TW;
     const int per = max((T + NT - 1) / NT, p.min_tiles_per_worker);
-    const int P2 = 2 * per;
-    const int X = (int)((int64_t)P2 * p.split_pct / 100);
+    const int P = Q * per;
     if (blockIdx.x == 0) {  // the schedule, for the merge pass
         if (threadIdx.x == 0) {
-            p.ws_hdr[0] = P2;
-            p.ws_hdr[1] = X;
+            p.ws_hdr[0] = P;
+            p.ws_hdr[1] = Q;
         }
+        if ((int)threadIdx.x <= Q) p.ws_hdr[S + 3 + threadIdx.x] = flat_offset(threadIdx.x, TW, P, p.split_pct, p.xcd_pct);
         for (int i = threadIdx.x; i <= S; i += blockDim.x) p.ws_hdr[2 + i] = pre[i];
     }
 
@@ -862,9 +880,9 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
     const int w = blockIdx.x * TU::NW + wave_id_uniform();
     const int team = w / TS;
     const int tj = w - team * TS;
-    const int t0 = min((team >> 1) * P2 + (team & 1 ? X : 0), T);
-    const int t1 = min((team >> 1) * P2 + (team & 1 ? P2 : X), T);
-    if (t0 >= T) return;
+    const int t0 = min((team / Q) * P + flat_offset(team % Q, TW, P, p.split_pct, p.xcd_pct), T);
+    const int t1 = min((team / Q) * P + flat_offset(team % Q + 1, TW, P, p.split_pct, p.xcd_pct), T);
+    if (t0 >= t1) return;
 
     const int lane = threadIdx.x % kWave;
     const uint32_t row_stride = (uint32_t)Hkv * A::RB;
@@ -1007,9 +1025,8 @@ __global__ __launch_bounds__(TU::NW * kWave) void decode_flat_kernel(DecodeParam
         a.reduce();
         const int nb = (aL + kBlock - 1) / kBlock;
         const int p0 = pre[as] + akvh * nb;  // the pair's tiles are [p0, p0 + nb)
-        // the team holding tile t
-        auto piece = [&](int t) { return 2 * (t / P2) + (t % P2 >= X ? 1 : 0); };
-        const bool whole = piece(p0) == piece(p0 + nb - 1);
+        // the ranges are contiguous, so the pair is whole here when it lies in this team's
+        const bool whole = p0 >= t0 && p0 + nb <= t1;
         // split pairs: record (pair + team) * TS + tj, unique because pair + team
         // grows by at least one from one segment of a wave to the next
         const int64_t dst = whole ? (int64_t)as * Hq + (akvh * TS + tj) * A::HG
@@ -1183,8 +1200,16 @@ __global__ __launch_bounds__(256) void decode_flat_merge_kernel(DecodeParams p) 
             if (lane + k * kWave < D) E::store(out_row + (lane + k * kWave) * E::kBytes, 0.f);
         return;
     }
-    const int P2 = p.ws_hdr[0], X = p.ws_hdr[1];  // teams 2j, 2j + 1 hold [2j P2/2 ..), split at X
-    auto piece = [&](int t) { return 2 * (t / P2) + (t % P2 >= X ? 1 : 0); };
+    // team j Q + q holds tiles [j P + off[q], j P + off[q + 1]) (see decode_flat_kernel)
+    const int S = p.num_seqs;
+    const int P = p.ws_hdr[0], Q = p.ws_hdr[1];
+    const int32_t* off = p.ws_hdr + S + 3;
+    auto piece = [&](int t) {
+        const int r = t % P;
+        int q = 0;
+        for (int i = 1; i < Q; ++i) q += off[i] <= r ? 1 : 0;
+        return (t / P) * Q + q;
+    };
     const int nb = (L + kBlock - 1) / kBlock;
     const int p0 = p.ws_hdr[2 + s] + hb * nb;
     const int w0 = piece(p0);  // teams w0 .. w1 hold the pair's tiles
@@ -1704,6 +1729,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 // 6.10, 6.64; 70 %: 5.90, 6.04, 6.48 (one team of 8 waves: 5.85, 5.86,
 // 6.50).
 constexpr int kSplitPct = 62;
+// Share of two consecutive workgroups' tiles taken by the first, which runs on
+// an even XCD (see decode_flat_kernel).  Matrix-core engine, GQA-8B layer: 50 %
+// 6.03 TB/s, 52 %: 6.11, 54 %: 6.04, 56 %: 5.95; vector engine, Llama-2-7B
+// layer: 50 % 6.23, 52 %: 6.33, 54 %: 6.37, 56 %: 6.32.
+constexpr int kXcdPctMfma = 52;
+constexpr int kXcdPctValu = 54;
 
 template <class E, int D, int G>
 struct DefaultTune {
@@ -1814,8 +1845,10 @@ hipError_t launch_flat_tuned(const DecodeParams& pin, hipStream_t stream) {
     DecodeParams p = pin;
     p.heads_per_wave = A::NH;
     p.team = team_size<TU>(p.n_kv_heads / A::NH);
-    // the first of two teams of a workgroup takes this share of their tiles
+    // the first of two teams of a workgroup takes this share of their tiles,
+    // a workgroup on an even XCD this share of a pair's
     p.split_pct = TU::NW / p.team == 2 ? kSplitPct : 50;
+    p.xcd_pct = TU::MFMA ? kXcdPctMfma : kXcdPctValu;
     // The grid is sized from the kernel without the fused append, and the fused
     // kernel gets the same grid: the tiles are then dealt alike and both give
     // the same bits.  (Its waves do not wait on one another, so a grid larger

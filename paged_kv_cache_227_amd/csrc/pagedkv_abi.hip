@@ -125,7 +125,7 @@ Plan make_plan(int32_t num_seqs, int32_t n_q_heads, int32_t max_blocks, const pk
         const size_t NH = (size_t)pkv::decode_heads_per_wave(L->dtype, L->head_dim, G, L->n_kv_heads);
         const size_t recs = (size_t)num_seqs * L->n_kv_heads + (size_t)pkv::kMaxFlatWorkers * NH;
         pl.n_parts_max = 1;
-        pl.hdr_bytes = round_up((size_t)(num_seqs + 3) * sizeof(int32_t));
+        pl.hdr_bytes = round_up((size_t)(num_seqs + 4 + pkv::kMaxFlatPeriod) * sizeof(int32_t));
         pl.acc_bytes = round_up(recs * G * L->head_dim * sizeof(float));
         pl.ws_bytes = pl.hdr_bytes + pl.acc_bytes + recs * G * 2 * sizeof(float);
         return pl;

@@ -83,6 +83,9 @@ struct CopyParams {
 // The flat schedule's grid never has more waves than this; its workspace is
 // sized for it.
 constexpr int kMaxFlatWorkers = 8192;
+// Most teams in a period of the flat schedule (two workgroups of at most 8
+// waves); the schedule header holds their offsets.
+constexpr int kMaxFlatPeriod = 16;
 // Largest batch the flat schedule serves (its per-workgroup LDS holds two
 // int32 per sequence); larger batches use fixed partitions.
 constexpr int kMaxFlatSeqs = 8000;
@@ -99,8 +102,8 @@ struct DecodeParams {
     // Split-K workspace.  Fixed partitions: ws_acc [num_seqs][n_q_heads][n_parts_max][head_dim],
     // ws_ml [..][2] (running max in log2 units, sum).  Flat schedule: records
     // [num_seqs * n_kv_heads + kMaxFlatWorkers][G][head_dim] and [..][G][2], and
-    // ws_hdr = {tiles per pair of teams, the first team's tiles of them, tile
-    // prefix per sequence [num_seqs + 1]}.
+    // ws_hdr = {tiles per period, teams per period Q, tile prefix per sequence
+    // [num_seqs + 1], the teams' offsets in a period [Q + 1]}.
     float* ws_acc;
     float* ws_ml;
     int32_t* ws_hdr;
@@ -114,7 +117,8 @@ struct DecodeParams {
     int32_t min_tiles_per_worker;
     int32_t heads_per_wave;  // adjacent KV heads one wave streams together (see decode_heads_per_wave)
     int32_t team;            // waves walking the same blocks, one head group each (set by the launchers)
-    int32_t split_pct;       // flat schedule: the first team of a pair's share of its tiles (set by the launcher)
+    int32_t split_pct;       // flat schedule: the first team of a workgroup's share of its tiles (set by the launcher)
+    int32_t xcd_pct;         // flat schedule: an even workgroup's share of it and the next one's tiles (set by the launcher)
     int32_t block_shift;     // log2 of the cache block size (8, 16, 32 or 64 tokens)
     float scale_log2;  // scale * log2(e): scores are kept in base-2 units
     // A fused append (flat schedule only; positions == nullptr otherwise): the
