@@ -16,11 +16,14 @@
 // Attention: unlike decode, a chunk makes QK^T and PV real matrix products
 // (n x G query rows against every key), so the work runs on the matrix cores.
 // A query row is one (chunk token, head of the KV head's group) pair; rows of
-// one (sequence, KV head) are ordered token-major.  A workgroup holds one tile
-// of 128 consecutive rows in two key groups of four waves, 32 rows per wave:
-//   * tiles are launched longest first (by the position of their last row),
-//     so that the compute units take the long tiles at once and the short
-//     ones fill in behind them;
+// one (sequence, KV head) are ordered token-major.  A tile is 128 consecutive
+// rows; a workgroup (one per compute unit, persistent) works through its
+// share of the tiles one at a time, in two key groups of four waves, 32 rows
+// per wave:
+//   * the tiles are ranked longest first (by the position of their last row)
+//     and dealt to the workgroups in rounds, alternating in direction, so
+//     that every workgroup starts on a long tile and the short ones even out
+//     the totals;
 //   * each key group takes half of the tile's key iterations (64 keys each),
 //     whose K and V tiles go from memory straight into LDS (two buffers for
 //     K, two for V, 16-byte chunks XOR-swizzled by row);
@@ -33,12 +36,13 @@
 //     wave's products overlap the other's softmax;
 //   * the row sums come from the matrix core too, from the same rounded
 //     weights as the outputs;
-//   * the key groups' softmax states meet in LDS at the end (the decode merge's
-//     rule), and group 0 writes the rows.
+//   * at a tile's end the key groups' softmax states meet in LDS (the decode
+//     merge's rule), each group writing half of the tile's output columns.
 // Rows past L in a sequence's last block are loaded as zeros, so whatever
 // those slots hold never reaches the output.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -133,13 +137,14 @@ struct PrefillShape {
     static constexpr int RG = kBlock / RPR;      // load instructions per 16-token tile
     static constexpr int PER_W = NB * RG / NW;   // load instructions per wave, iteration and cache
     static constexpr int STEP = NB * kBlock;     // keys per iteration
-    static constexpr int STATE = TT * 4 + 2;     // floats of one lane's row state (acc, m, l)
-    static constexpr int SQ = (STATE + 3) / 4;   // of them in each of the four buffers
+    static constexpr int TH = TT / 2;            // output tiles each key group writes
+    static constexpr int HSTATE = TH * 4 + 2;    // floats a lane hands the other group (half of acc, m, l)
+    static constexpr int HSQ = (HSTATE + 3) / 4; // of them in each of the four buffers
     static_assert(ROWS == kPrefillRows, "the grid's tile height");
     static_assert(CH == 4 * KK && D % 32 == 0, "head_dim a multiple of 32");
     static_assert(RPR * RB == 1024 && 8 % RPR == 0 && (NB * RG) % NW == 0,
                   "whole 1 KiB slices inside one block of 8 to 64, the same count per wave");
-    static_assert(NW * NQ * SQ * kWave * 4 <= ARR, "group 1's final state fits the four buffers");
+    static_assert(KS * NW * NQ * HSQ * kWave * 4 <= ARR, "both groups' handed-over state fits the four buffers");
 };
 
 // Word 3 of a raw buffer resource: 32-bit data format, no swizzle; with a
@@ -239,11 +244,10 @@ __device__ __forceinline__ int wave_max_i32(int x) {
 
 // ---- tile order: longest first ----------------------------------------------
 //
-// Workgroups are handed to the compute units in launch order, each to the
-// first one free, so launching tiles in decreasing key count is the
-// longest-first list schedule: the long tiles start at once and the short
-// ones fill in behind them, where the launch order (sequence, tile) of the
-// batch could leave a long tile for the end.  Tile t of a sequence covers
+// Dealing tiles in decreasing key count approximates the longest-first list
+// schedule: the long tiles start at once and the short ones fill in behind
+// them, where the batch's order (sequence, tile) could leave a long tile for
+// the end.  Tile t of a sequence covers
 // chunk tokens [tQ, min((t+1)Q, n)) (Q = kPrefillRows / G) and reads keys 0 ..
 // its last token's position.  The order sorts tiles by that last position,
 // descending, ties by sequence; a sequence's tiles end at distinct positions,
@@ -266,10 +270,10 @@ struct TileRef {
     int n;      // its chunk length (the chunk's last n positions of L)
 };
 
-// The rank-th tile in that order, found by the wave alone (every wave of the
-// workgroup computes the same answer): a search for the last position of
-// that tile, counting the tiles that reach a position over all sequences,
-// then its place among the tiles ending there, in sequence order.  Up to 64
+// The rank-th tile in that order, found by one wave alone: a search for the
+// last position of that tile, counting the tiles that reach a position over
+// all sequences, then its place among the tiles ending there, in sequence
+// order.  Up to 64
 // sequences the lanes test 64 positions per round; beyond, the lanes take
 // sequences lane, lane + 64, ... and the search is four-way (three counts
 // per round, their reductions interleaved).
@@ -479,462 +483,506 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     // which leaves room to read the V and K fragments well ahead.
     __shared__ __attribute__((aligned(16))) char lds_q[SH::ROWS * RB];
 
-    // Grid (KV head x sequence slot, tile slot), KV head fastest: the
-    // workgroup of rank i and head h is the (h + Hkv i)-th launched, so every
-    // rank goes out to all heads before the next; the XCDs take workgroups
-    // round-robin, and a head's tiles all land on one XCD (its K and V stay in
-    // that XCD's L2) when Hkv is a multiple of 8.
+    // A persistent grid: W workgroups per KV head, KV head fastest, so the
+    // XCDs (which take workgroups round-robin) each get the same mix, and a
+    // head's tiles all run on one XCD (its K and V stay in that XCD's L2)
+    // when Hkv is a multiple of 8.  Slot j of a head takes the tiles of ranks
+    // j, 2W - 1 - j, 2W + j, 4W - 1 - j, ... in the longest-first order: the
+    // first round deals the W longest tiles one each, the second gives the
+    // shortest of the next W to the slot that got the longest, and so on.
     const int Hkv = p.n_kv_heads;
     const int kvh = blockIdx.x % Hkv;
-    const int rank = blockIdx.x / Hkv + p.num_seqs * blockIdx.y;
+    const int W = gridDim.x / Hkv;
+    const int sj = blockIdx.x / Hkv;
+    const int R = p.num_seqs * ((p.max_q_len * G + SH::ROWS - 1) / SH::ROWS);  // ranks, at most
     const int lane = threadIdx.x % kWave;
     const int max_len = p.max_blocks << p.block_shift;
-    // One wave finds the tile (two waves share each SIMD, so eight copies of
-    // the search would take twice as long) and hands it to the others through
-    // LDS: the start of the last V buffer, whose first load comes phases later.
-    TileRef tr;
-    {
-        int* sh = reinterpret_cast<int*>(lds_v1);
-        if (wave_id_uniform() == 0) {
-            tr = pick_tile<Q>(p, rank, lane, max_len);
-            if (lane == 0) {
-                sh[0] = tr.s;
-                sh[1] = tr.t;
-                sh[2] = tr.q0;
-                sh[3] = tr.L;
-                sh[4] = tr.n;
-            }
+    // The slot's tiles are found SH::WAVES at a time, one per wave, and handed
+    // over through LDS (the start of the last V buffer, whose first load
+    // comes phases later); lane k holds the round's k-th tile as sequence
+    // << 16 | tile, unsigned (all ones: none; a tile index stays below
+    // kMaxPrefillTiles = 65535), and the sequence's offsets and length are
+    // read again when its turn comes.
+    static_assert(kMaxPrefillTiles <= 65535, "the tile index fits 16 bits, below 0xffff");
+    int ref = -1;
+    for (int item = 0;; ++item) {
+        // the last tile's state reads (all four K/V buffers) are done before
+        // this tile's loads go into them; its output stores need not be (a
+        // __syncthreads would also wait for those)
+        if (item > 0) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+            phase_barrier();
         }
-        __syncthreads();
-        tr.s = __builtin_amdgcn_readfirstlane(sh[0]);
-        tr.t = __builtin_amdgcn_readfirstlane(sh[1]);
-        tr.q0 = __builtin_amdgcn_readfirstlane(sh[2]);
-        tr.L = __builtin_amdgcn_readfirstlane(sh[3]);
-        tr.n = __builtin_amdgcn_readfirstlane(sh[4]);
-    }
-    if (tr.s < 0) return;
-    const int s = tr.s;
-    const int q0 = tr.q0;
-    const int n = tr.n;
-    const int L = tr.L;
-    const int Hq = p.n_q_heads;
-    const int nrows = min(n, p.max_q_len) * G;  // rows computed
-    const int r0 = tr.t * SH::ROWS;
-    const int ctx = L - n;  // tokens before the chunk
-    const int wg_last_pos = ctx + (min(r0 + SH::ROWS, nrows) - 1) / G;
-    const int nblk = wg_last_pos / kBlock + 1;  // 16-token tiles the workgroup reads
-    const int nit = (nblk + NB - 1) / NB;
-    const int NJ = (nit + 1) / 2;                // phase pairs of either group
-
-    const int kg = wave_id_uniform() / SH::NW;  // key group
-    const int w = wave_id_uniform() % SH::NW;   // row wave within the group
-    const int kb = kg == 0 ? 0 : NJ;            // the group's first iteration
-    const int nj = kg == 0 ? NJ : nit - NJ;     // and its count
-    const int gq = lane / 16;  // MFMA lane coordinates
-    const int jq = lane % 16;
-    const int wr0 = r0 + w * SH::ROWS_W;  // this wave's first row
-    const int wave_first_pos = ctx + wr0 / G;
-    // Iteration j of the group is masked unless every key of it is visible to
-    // every row of the wave.  A wave computes every phase of its group, also
-    // for an iteration none of its rows sees (or one past the group's range,
-    // loaded as zeros): the mask makes all its weights 0, and skipping it
-    // would not shorten the phase, which waits for every wave at its barrier.
-    auto masked = [&](int j) __attribute__((always_inline)) { return (kb + j + 1) * STEP - 1 > wave_first_pos; };
-
-    // The softmax below needs a positive scale: a negative one moves into q's
-    // sign bits (exact), and a zero one becomes the smallest normal float,
-    // which leaves every weight at exactly 1 as zero would (|score| x 2^-126
-    // is far below half an ulp of 1 for any 16-bit q and K).
-    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-    const float scale_log2 = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
-    // q rows of this wave: group c, column jq is row wr0 + 16c + jq (row
-    // 32w + 16c + jq of the tile); group 0's waves load them here and put
-    // them in LDS in the prologue (rows past the chunk as zeros), once the
-    // first K and V loads are under way; the first barrier publishes them.
-    int qpos[NQ];
-    Vec16 qv[NQ][KK];
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-        const int row = wr0 + 16 * c + jq;
-        const bool ok = row < nrows;
-        const int tok = row / G;
-        qpos[c] = ok ? ctx + tok : -1;
-        const char* qrow = static_cast<const char*>(p.q) + (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qv[c][kk] = ok && kg == 0 ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
-    }
-    // Row state: reference maximum m, output acc and the weights' sum, which
-    // the matrix core accumulates too (the product with a V^T of ones puts
-    // row jq's sum in every element of lane column jq).
-    float m[NQ];
-    f32x4_t acc[NQ][TT], lsum[NQ];
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-        m[c] = -INFINITY;
-        lsum[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[c][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    const op4_t ones = Weights<E>::ones();
-
-    // K and V go from memory straight into LDS (buffer loads with an LDS
-    // destination).  One such instruction of a wave fills a contiguous 1 KiB
-    // of LDS, lane i bytes 16i .. 16i+15: RPR rows of one 16-token tile of one
-    // cache, which lie in one cache block whatever the block size (RPR divides
-    // 8).  Lane i fetches the global chunk that the row's XOR swizzle puts in
-    // its slot.  The block's base address and the bytes of its rows inside the
-    // sequence make the buffer resource, so rows past the context and invalid
-    // table entries arrive as zeros (out-of-range buffer reads return 0).
-    // Slice g = w + k NW of an iteration (per cache): tile g / RG, rows
-    // RPR (g % RG) ..; an iteration spans a whole number of blocks, so the
-    // slice's row offset inside its block is the same in every iteration and
-    // goes into the lane offsets.
-    // Wave w of a key group loads tile w of each iteration (K and V): slice
-    // k is rows RPR k .. RPR k + RPR - 1 of it, inside the tile's first eight
-    // rows (half 0) or its last eight (half 1); with blocks of 16 tokens or
-    // more the two halves are one block.
-    static_assert(SH::NW == NB && SH::PER_W == SH::RG, "one 16-token tile per row wave");
-    const uint32_t row_stride = (uint32_t)Hkv * RB;
-    const int bshift = p.block_shift;
-    const int bsize = 1 << bshift;
-    const uint32_t blk_bytes = row_stride << bshift;  // below 2^32: 64 x Hkv x 256 bytes at most
-    const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
-    const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
-    const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
-    const int tt0 = kb * STEP + w * kBlock;  // first token of the wave's tile in the group's iteration 0
-    uint32_t voff[PER_W];
-#pragma unroll
-    for (int k = 0; k < PER_W; ++k) {
-        const int row = k * SH::RPR + lane / CH;  // row in the tile
-        voff[k] = (uint32_t)(((tt0 + k * SH::RPR) & (bsize - 1)) + lane / CH) * row_stride +
-                  (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
-    }
-    // halves past the workgroup's last tile, or past the sequence's last table entry, load nothing
-    const int tok_lim = min(nblk * kBlock, (L + bsize - 1) & -bsize);
-    typedef int Ents[2];
-    struct Blk {
-        uint64_t off;  // byte offset of the half's block in a cache
-        int size;      // bytes of its rows inside the sequence (0: load zeros)
-    };
-    // Table entries of the two halves of the group's iteration j, read a
-    // phase before their loads.  The read index is clamped into the table and
-    // nothing depends on the value until then, so no read waits or branches.
-    auto entries = [&](int j, Ents& e) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) e[h] = scalar_entry(table, min(j * STEP + tt0 + 8 * h, tok_lim - 1) >> bshift);
-    };
-    // Where the halves of iteration j come from; a half past the workgroup's
-    // keys, or of an iteration past the group's range, loads zeros (its loads
-    // still run, so that every phase issues the same number of loads and the
-    // waits are static).
-    auto place = [&](int j, const Ents& e, Blk (&bl)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int tok = j * STEP + tt0 + 8 * h;
-            const bool ok = j < nj && tok < tok_lim && (uint32_t)e[h] < (uint32_t)p.num_blocks;
-            bl[h].off = (uint64_t)(uint32_t)(ok ? e[h] : 0) * blk_bytes;
-            bl[h].size = ok ? min(L - (tok & -bsize), bsize) * (int)row_stride : 0;
+        const int k_round = item % SH::WAVES;
+        if (k_round == 0) {
+            int* sh = reinterpret_cast<int*>(lds_v1);
+            const int wv = wave_id_uniform();
+            const int it = item + wv;
+            const int rank = it * W + ((it & 1) ? W - 1 - sj : sj);
+            // (an opaque lane index: hoisted out of the loop, the search's
+            // per-lane addresses would hold registers through every tile)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const TileRef t = rank < R ? pick_tile<Q>(p, rank, ln, max_len) : TileRef{-1, 0, 0, 0, 0};
+            if (lane == 0) sh[wv] = t.s < 0 ? -1 : (int)((uint32_t)t.s << 16 | (uint32_t)t.t);
+            __syncthreads();
+            ref = lane < SH::WAVES ? sh[lane] : -1;
         }
-    };
-    // (The slice's LDS offset is formed at each use from one opaque value:
-    // left to itself the compiler would keep an offset per buffer and slice
-    // in scalar registers, which it has too few of here.)
-    const uint32_t wslot = (uint32_t)(kg * SH::SPAN + w * SH::TILE);
-    auto issue = [&](char* buf, const char* base, const Blk (&bl)[2]) __attribute__((always_inline)) {
-        uint32_t ws = wslot;
-        asm volatile("" : "+s"(ws));
-#pragma unroll
-        for (int k = 0; k < PER_W; ++k) {
-            const Blk& b = bl[(k * SH::RPR) / 8];
-            lds_load_1k(base + b.off, b.size, buf + ws + k * 1024, voff[k]);
-        }
-    };
+        const int cur = __builtin_amdgcn_readlane(ref, k_round);
+        if (cur == -1) break;  // ranks past the batch's tiles: so are the slot's later ones
+        TileRef tr;
+        tr.s = (int)((uint32_t)cur >> 16);
+        tr.t = cur & 0xffff;
+        tr.q0 = __builtin_amdgcn_readfirstlane(p.cu_q[tr.s]);
+        tr.n = __builtin_amdgcn_readfirstlane(p.cu_q[tr.s + 1]) - tr.q0;
+        tr.L = min(max(__builtin_amdgcn_readfirstlane(p.context_lens[tr.s]), 0), max_len);
+        const int s = tr.s;
+        const int q0 = tr.q0;
+        const int n = tr.n;
+        const int L = tr.L;
+        const int Hq = p.n_q_heads;
+        const int nrows = min(n, p.max_q_len) * G;  // rows computed
+        const int r0 = tr.t * SH::ROWS;
+        const int ctx = L - n;  // tokens before the chunk
+        const int wg_last_pos = ctx + (min(r0 + SH::ROWS, nrows) - 1) / G;
+        const int nblk = wg_last_pos / kBlock + 1;  // 16-token tiles the workgroup reads
+        const int nit = (nblk + NB - 1) / NB;
+        const int NJ = (nit + 1) / 2;                // phase pairs of either group
 
-    f32x4_t sc[NQ][NB];            // scores of an iteration, from its M phase to its V phase
-    op4_t ph[NQ][NB];              // its weights, from its V phase to the next M
-    // S^T = K Q^T of iteration j: lane (gq, jq) holds keys 16 nb + 4 gq + r of
-    // row column jq.  Every block gets its products, those past the wave's
-    // rows included (the softmax masks them): a branch around them would put
-    // the first reads of a product's result right after it, closer than its
-    // latency.
-    auto scores = [&](const char* kl) __attribute__((always_inline)) {
-        Vec16 qf[NQ][KK];
+        const int kg = wave_id_uniform() / SH::NW;  // key group
+        const int w = wave_id_uniform() % SH::NW;   // row wave within the group
+        const int kb = kg == 0 ? 0 : NJ;            // the group's first iteration
+        const int nj = kg == 0 ? NJ : nit - NJ;     // and its count
+        const int gq = lane / 16;  // MFMA lane coordinates
+        const int jq = lane % 16;
+        const int wr0 = r0 + w * SH::ROWS_W;  // this wave's first row
+        const int wave_first_pos = ctx + wr0 / G;
+        // Iteration j of the group is masked unless every key of it is visible to
+        // every row of the wave.  A wave computes every phase of its group, also
+        // for an iteration none of its rows sees (or one past the group's range,
+        // loaded as zeros): the mask makes all its weights 0, and skipping it
+        // would not shorten the phase, which waits for every wave at its barrier.
+        auto masked = [&](int j) __attribute__((always_inline)) { return (kb + j + 1) * STEP - 1 > wave_first_pos; };
+
+        // The softmax below needs a positive scale: a negative one moves into q's
+        // sign bits (exact), and a zero one becomes the smallest normal float,
+        // which leaves every weight at exactly 1 as zero would (|score| x 2^-126
+        // is far below half an ulp of 1 for any 16-bit q and K).
+        const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+        const float scale_log2 = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
+        // q rows of this wave: group c, column jq is row wr0 + 16c + jq (row
+        // 32w + 16c + jq of the tile); group 0's waves load them here and put
+        // them in LDS in the prologue (rows past the chunk as zeros), once the
+        // first K and V loads are under way; the first barrier publishes them.
+        int qpos[NQ];
+        Vec16 qv[NQ][KK];
 #pragma unroll
-        for (int c = 0; c < NQ; ++c)
+        for (int c = 0; c < NQ; ++c) {
+            const int row = wr0 + 16 * c + jq;
+            const bool ok = row < nrows;
+            const int tok = row / G;
+            qpos[c] = ok ? ctx + tok : -1;
+            const char* qrow = static_cast<const char*>(p.q) + (((int64_t)(q0 + tok) * Hq + kvh * G + row % G) * D) * 2;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                qf[c][kk] = lds_load16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq));
-        // block nb's K fragments are read a block before its products
-        constexpr int AHEAD = 1;
-        Vec16 ka[NB][KK];
-        auto fetch = [&](int nb) __attribute__((always_inline)) {
+                qv[c][kk] = ok && kg == 0 ? load16(qrow + (4 * kk + gq) * 16) : Vec16{{0u, 0u, 0u, 0u}};
+        }
+        // Row state: reference maximum m, output acc and the weights' sum, which
+        // the matrix core accumulates too (the product with a V^T of ones puts
+        // row jq's sum in every element of lane column jq).
+        float m[NQ];
+        f32x4_t acc[NQ][TT], lsum[NQ];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) ka[nb][kk] = lds_load16(kl + nb * SH::TILE, tile_pos<RB>(jq, 4 * kk + gq));
+        for (int c = 0; c < NQ; ++c) {
+            m[c] = -INFINITY;
+            lsum[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[c][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        const op4_t ones = Weights<E>::ones();
+
+        // K and V go from memory straight into LDS (buffer loads with an LDS
+        // destination).  One such instruction of a wave fills a contiguous 1 KiB
+        // of LDS, lane i bytes 16i .. 16i+15: RPR rows of one 16-token tile of one
+        // cache, which lie in one cache block whatever the block size (RPR divides
+        // 8).  Lane i fetches the global chunk that the row's XOR swizzle puts in
+        // its slot.  The block's base address and the bytes of its rows inside the
+        // sequence make the buffer resource, so rows past the context and invalid
+        // table entries arrive as zeros (out-of-range buffer reads return 0).
+        // Slice g = w + k NW of an iteration (per cache): tile g / RG, rows
+        // RPR (g % RG) ..; an iteration spans a whole number of blocks, so the
+        // slice's row offset inside its block is the same in every iteration and
+        // goes into the lane offsets.
+        // Wave w of a key group loads tile w of each iteration (K and V): slice
+        // k is rows RPR k .. RPR k + RPR - 1 of it, inside the tile's first eight
+        // rows (half 0) or its last eight (half 1); with blocks of 16 tokens or
+        // more the two halves are one block.
+        static_assert(SH::NW == NB && SH::PER_W == SH::RG, "one 16-token tile per row wave");
+        const uint32_t row_stride = (uint32_t)Hkv * RB;
+        const int bshift = p.block_shift;
+        const int bsize = 1 << bshift;
+        const uint32_t blk_bytes = row_stride << bshift;  // below 2^32: 64 x Hkv x 256 bytes at most
+        const char* kbase = static_cast<const char*>(p.k_cache) + (int64_t)kvh * RB;
+        const char* vbase = static_cast<const char*>(p.v_cache) + (int64_t)kvh * RB;
+        const int32_t* table = p.block_tables + (int64_t)s * p.max_blocks;
+        const int tt0 = kb * STEP + w * kBlock;  // first token of the wave's tile in the group's iteration 0
+        uint32_t voff[PER_W];
+#pragma unroll
+        for (int k = 0; k < PER_W; ++k) {
+            const int row = k * SH::RPR + lane / CH;  // row in the tile
+            voff[k] = (uint32_t)(((tt0 + k * SH::RPR) & (bsize - 1)) + lane / CH) * row_stride +
+                      (uint32_t)(((lane % CH) ^ (row % CH)) * 16);
+        }
+        // halves past the workgroup's last tile, or past the sequence's last table entry, load nothing
+        const int tok_lim = min(nblk * kBlock, (L + bsize - 1) & -bsize);
+        typedef int Ents[2];
+        struct Blk {
+            uint64_t off;  // byte offset of the half's block in a cache
+            int size;      // bytes of its rows inside the sequence (0: load zeros)
         };
+        // Table entries of the two halves of the group's iteration j, read a
+        // phase before their loads.  The read index is clamped into the table and
+        // nothing depends on the value until then, so no read waits or branches.
+        auto entries = [&](int j, Ents& e) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nb = 0; nb < AHEAD; ++nb) fetch(nb);
+            for (int h = 0; h < 2; ++h) e[h] = scalar_entry(table, min(j * STEP + tt0 + 8 * h, tok_lim - 1) >> bshift);
+        };
+        // Where the halves of iteration j come from; a half past the workgroup's
+        // keys, or of an iteration past the group's range, loads zeros (its loads
+        // still run, so that every phase issues the same number of loads and the
+        // waits are static).
+        auto place = [&](int j, const Ents& e, Blk (&bl)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            if (nb + AHEAD < NB) fetch(nb + AHEAD);
-#pragma unroll
-            for (int c = 0; c < NQ; ++c) {
-                sc[c][nb] = OPS::qk(ka[nb][0], qf[c][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int kk = 1; kk < KK; ++kk) sc[c][nb] = OPS::qk(ka[nb][kk], qf[c][kk], sc[c][nb]);
+            for (int h = 0; h < 2; ++h) {
+                const int tok = j * STEP + tt0 + 8 * h;
+                const bool ok = j < nj && tok < tok_lim && (uint32_t)e[h] < (uint32_t)p.num_blocks;
+                bl[h].off = (uint64_t)(uint32_t)(ok ? e[h] : 0) * blk_bytes;
+                bl[h].size = ok ? min(L - (tok & -bsize), bsize) * (int)row_stride : 0;
             }
-        }
-    };
-    // Online softmax of the scores: weights in base-2 units against a lazily
-    // moved reference maximum m (it moves only when a row's scores pass it by
-    // more than kLazy, so weights stay below 2^kLazy and most iterations skip
-    // the rescale of O and l).
-    auto softmax = [&](int j) __attribute__((always_inline)) {
-        // The prefix-causal mask: a key past the row's position scores -inf
-        // (every key of an unmasked iteration is visible to every row).  A
-        // bitwise select on the sign of lim - key, which the compiler turns
-        // into a compare and a select through VCC one element at a time
-        // (compares hoisted ahead of their selects would each hold a scalar
-        // register pair).
-        if (masked(j)) {
-            const int key0 = (kb + j) * STEP;
+        };
+        // (The slice's LDS offset is formed at each use from one opaque value:
+        // left to itself the compiler would keep an offset per buffer and slice
+        // in scalar registers, which it has too few of here.)
+        const uint32_t wslot = (uint32_t)(kg * SH::SPAN + w * SH::TILE);
+        auto issue = [&](char* buf, const char* base, const Blk (&bl)[2]) __attribute__((always_inline)) {
+            uint32_t ws = wslot;
+            asm volatile("" : "+s"(ws));
 #pragma unroll
-            for (int c = 0; c < NQ; ++c) {
-                const int lim = qpos[c] - key0 - 4 * gq;  // last visible key offset of this lane
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t msk = (uint32_t)((lim - (16 * nb + r)) >> 31);
-                        sc[c][nb][r] = __uint_as_float((msk & 0xff800000u) | (~msk & __float_as_uint(sc[c][nb][r])));
-                    }
+            for (int k = 0; k < PER_W; ++k) {
+                const Blk& b = bl[(k * SH::RPR) / 8];
+                lds_load_1k(base + b.off, b.size, buf + ws + k * 1024, voff[k]);
             }
-        }
-        // each lane's largest score of each row group, as a tree
-        float mx[NQ];
+        };
+
+        f32x4_t sc[NQ][NB];            // scores of an iteration, from its M phase to its V phase
+        op4_t ph[NQ][NB];              // its weights, from its V phase to the next M
+        // S^T = K Q^T of iteration j: lane (gq, jq) holds keys 16 nb + 4 gq + r of
+        // row column jq.  Every block gets its products, those past the wave's
+        // rows included (the softmax masks them): a branch around them would put
+        // the first reads of a product's result right after it, closer than its
+        // latency.
+        auto scores = [&](const char* kl) __attribute__((always_inline)) {
+            Vec16 qf[NQ][KK];
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            float t4[NB];
+            for (int c = 0; c < NQ; ++c)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                t4[nb] = smax(smax(sc[c][nb][0], sc[c][nb][1]), smax(sc[c][nb][2], sc[c][nb][3]));
-            mx[c] = smax(smax(t4[0], t4[1]), smax(t4[2], t4[3]));
-            static_assert(NB == 4, "the tree above");
-        }
+                for (int kk = 0; kk < KK; ++kk)
+                    qf[c][kk] = lds_load16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq));
+            // block nb's K fragments are read a block before its products
+            constexpr int AHEAD = 1;
+            Vec16 ka[NB][KK];
+            auto fetch = [&](int nb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            // The reference moves when some row's largest scaled score passes
-            // it by more than kLazy, i.e. when some lane's does: the row's
-            // maximum over its four lanes is needed only then.
-            if (__builtin_amdgcn_ballot_w64(mx[c] * scale_log2 > m[c] + kLazy)) {
-                const float mn = rows_smax(mx[c]) * scale_log2;  // the row's largest scaled score here
-                const float nm = fmaxf(m[c], mn);
-                const float alpha = __builtin_amdgcn_exp2f(m[c] - (nm == -INFINITY ? 0.f : nm));
-                lsum[c] *= alpha;
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[nb][kk] = lds_load16(kl + nb * SH::TILE, tile_pos<RB>(jq, 4 * kk + gq));
+            };
 #pragma unroll
-                for (int t = 0; t < TT; ++t) acc[c][t] *= alpha;
-                m[c] = nm;
-            }
-            const float ms = m[c] == -INFINITY ? 0.f : m[c];
+            for (int nb = 0; nb < AHEAD; ++nb) fetch(nb);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                float pr[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[c][nb][r], scale_log2, -ms));
-                ph[c][nb] = Weights<E>::pack(pr);
-                pin(ph[c][nb]);
-            }
-        }
-    };
-    // O^T += V^T P^T of iteration j.  V^T is read transposed: lane (gq, jq)
-    // takes key row 4gq + jq/4, bytes 32t + 8(jq%4).  Blocks nb and nb + 1 make
-    // one 16x16x32 product: contraction slots 0-3 are keys 4gq + r of block
-    // nb, slots 4-7 those of block nb + 1, in V^T and P^T alike.  The
-    // fragments of step u (pair u / TT, output tile u % TT) are read AHEAD
-    // steps ahead of their products, so that the reads' latency hides behind
-    // them.  Also the weights' row sums (a V^T of ones).
-    auto products = [&](const char* vl) __attribute__((always_inline)) {
-        constexpr int U = PV_STEPS, AHEAD = PV_AHEAD;
-        const int trow = 4 * gq + jq / 4;
-        op4_t fa[U], fb[U];
-        auto fetch = [&](int u) __attribute__((always_inline)) {
-            const int nb = 2 * (u / TT), t = u % TT;
-            const uint32_t off = tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2);
-            fa[u] = OPS::read_tr(vl + nb * SH::TILE + off);
-            fb[u] = OPS::read_tr(vl + (nb + 1) * SH::TILE + off);
-        };
-#pragma unroll
-        for (int u = 0; u < AHEAD; ++u) fetch(u);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (u + AHEAD < U) fetch(u + AHEAD);
-            const int nb = 2 * (u / TT), t = u % TT;
-#pragma unroll
-            for (int c = 0; c < NQ; ++c) {
-                acc[c][t] = OPS::pv2(fa[u], fb[u], ph[c][nb], ph[c][nb + 1], acc[c][t]);
-            }
-            if (t == TT - 1) {
+                if (nb + AHEAD < NB) fetch(nb + AHEAD);
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
-                    lsum[c] = OPS::pv2(ones, ones, ph[c][nb], ph[c][nb + 1], lsum[c]);
+                    sc[c][nb] = OPS::qk(ka[nb][0], qf[c][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int kk = 1; kk < KK; ++kk) sc[c][nb] = OPS::qk(ka[nb][kk], qf[c][kk], sc[c][nb]);
                 }
             }
-        }
-    };
-
-    // Phase M_j (buffer parity b = j % 2): the products of j - 1 from V
-    // buffer 1 - b (their weights die there), then the scores of j from K
-    // buffer b (born there), so weights and scores never hold registers
-    // together.
-    Ents ec;     // table entries of iteration j + 2 when V_j starts
-    Blk bl[2];   // where iteration j + 1's halves come from when V_j starts
-    // (M_0 has no products, the last M phase, M_NJ, no scores)
-    auto mphase = [&](int j, auto par, auto pv, auto qk) __attribute__((always_inline)) {
-        constexpr int b = decltype(par)::value;
-        // The products are the phase's critical path: this wave issues first
-        // (the SIMD otherwise favours the older wave, group 0's), and its
-        // partner's softmax fills the cycles between the products.
-        __builtin_amdgcn_s_setprio(1);
-        if constexpr (decltype(pv)::value) products((b ? lds_v0 : lds_v1) + kg * SH::SPAN);
-        if constexpr (decltype(qk)::value) {
-            scores((b ? lds_k1 : lds_k0) + kg * SH::SPAN);
+        };
+        // Online softmax of the scores: weights in base-2 units against a lazily
+        // moved reference maximum m (it moves only when a row's scores pass it by
+        // more than kLazy, so weights stay below 2^kLazy and most iterations skip
+        // the rescale of O and l).
+        auto softmax = [&](int j) __attribute__((always_inline)) {
+            // The prefix-causal mask: a key past the row's position scores -inf
+            // (every key of an unmasked iteration is visible to every row).  A
+            // bitwise select on the sign of lim - key, which the compiler turns
+            // into a compare and a select through VCC one element at a time
+            // (compares hoisted ahead of their selects would each hold a scalar
+            // register pair).
+            if (masked(j)) {
+                const int key0 = (kb + j) * STEP;
 #pragma unroll
-            for (int c = 0; c < NQ; ++c)
+                for (int c = 0; c < NQ; ++c) {
+                    const int lim = qpos[c] - key0 - 4 * gq;  // last visible key offset of this lane
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) pin(sc[c][nb]);
-        }
-        // The phase's order through scheduling: the products' first fragment
-        // reads, then per products step the reads PV_AHEAD steps on (in the
-        // last steps, the scores' q and first K reads) and the step's
-        // products; then per scores block the next block's K reads and the
-        // block's products.
-        m_schedule<decltype(pv)::value, decltype(qk)::value, PV_STEPS, PV_AHEAD, TT, NQ, NB, KK>(
-            std::make_integer_sequence<int, PV_STEPS>{}, std::make_integer_sequence<int, NB>{});
-        __builtin_amdgcn_s_setprio(0);
-    };
-    // Phase V_j: the loads of K_{j+2} into K buffer b (last read by the
-    // group's scores in M_j) and of V_{j+1} into V buffer 1 - b (last read by
-    // the products in M_j), the table entries of j + 3, the softmax of j;
-    // then this wave's loads of K_{j+1} and V_j, issued in V_{j-1}, land
-    // (this phase's stay in flight), so that after the barrier the whole
-    // group's K_{j+1} and V_j are in LDS.
-    auto vphase = [&](int j, auto par) __attribute__((always_inline)) {
-        constexpr int b = decltype(par)::value;
-        Blk b2[2];
-        place(j + 2, ec, b2);
-        issue(b ? lds_k1 : lds_k0, kbase, b2);
-        issue(b ? lds_v0 : lds_v1, vbase, bl);
+                    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) bl[h] = b2[h];
-        entries(j + 3, ec);
-        softmax(j);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_W));
-    };
-
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    // Prologue: the loads of K_0, V_0 and K_1, then q into LDS; K_0 (and q)
-    // land before the first barrier.
-    {
-        Ents e1;
-        entries(0, ec);
-        entries(1, e1);
-        place(0, ec, bl);
-        issue(lds_k0, kbase, bl);
-        issue(lds_v0, vbase, bl);
-        place(1, e1, bl);
-        issue(lds_k1, kbase, bl);
-        entries(2, ec);
-        if (kg == 0) {
-#pragma unroll
-            for (int c = 0; c < NQ; ++c)
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    Vec16 v = qv[c][kk];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v.w[e] ^= qsign;
-                    lds_store16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq), v);
+                        for (int r = 0; r < 4; ++r) {
+                            const uint32_t msk = (uint32_t)((lim - (16 * nb + r)) >> 31);
+                            sc[c][nb][r] =
+                                __uint_as_float((msk & 0xff800000u) | (~msk & __float_as_uint(sc[c][nb][r])));
+                        }
                 }
-        }
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_W));
-    }
-    phase_barrier();
-    if (kg == 1) phase_barrier();  // group 1 runs one phase behind
-    using T = std::true_type;
-    using F = std::false_type;
-    mphase(0, B0{}, F{}, T{});
-    phase_barrier();
-    vphase(0, B0{});
-    phase_barrier();
-    int j = 1;
-    for (; j + 1 < NJ; j += 2) {
-        mphase(j, B1{}, T{}, T{});
-        phase_barrier();
-        vphase(j, B1{});
-        phase_barrier();
-        mphase(j + 1, B0{}, T{}, T{});
-        phase_barrier();
-        vphase(j + 1, B0{});
-        phase_barrier();
-    }
-    if (j < NJ) {  // j odd
-        mphase(j, B1{}, T{}, T{});
-        phase_barrier();
-        vphase(j, B1{});
-        phase_barrier();
-    }
-    // M_NJ: the last products; then the last phases' zero fills land before
-    // the buffers take group 1's state.
-    if (NJ & 1) mphase(NJ, B1{}, T{}, F{});
-    else mphase(NJ, B0{}, T{}, F{});
-    __builtin_amdgcn_s_waitcnt(0);
-    phase_barrier();
-    if (kg == 0) phase_barrier();
+            }
+            // each lane's largest score of each row group, as a tree
+            float mx[NQ];
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                float t4[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    t4[nb] = smax(smax(sc[c][nb][0], sc[c][nb][1]), smax(sc[c][nb][2], sc[c][nb][3]));
+                mx[c] = smax(smax(t4[0], t4[1]), smax(t4[2], t4[3]));
+                static_assert(NB == 4, "the tree above");
+            }
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                // The reference moves when some row's largest scaled score passes
+                // it by more than kLazy, i.e. when some lane's does: the row's
+                // maximum over its four lanes is needed only then.
+                if (__builtin_amdgcn_ballot_w64(mx[c] * scale_log2 > m[c] + kLazy)) {
+                    const float mn = rows_smax(mx[c]) * scale_log2;  // the row's largest scaled score here
+                    const float nm = fmaxf(m[c], mn);
+                    const float alpha = __builtin_amdgcn_exp2f(m[c] - (nm == -INFINITY ? 0.f : nm));
+                    lsum[c] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) acc[c][t] *= alpha;
+                    m[c] = nm;
+                }
+                const float ms = m[c] == -INFINITY ? 0.f : m[c];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    float pr[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(sc[c][nb][r], scale_log2, -ms));
+                    ph[c][nb] = Weights<E>::pack(pr);
+                    pin(ph[c][nb]);
+                }
+            }
+        };
+        // O^T += V^T P^T of iteration j.  V^T is read transposed: lane (gq, jq)
+        // takes key row 4gq + jq/4, bytes 32t + 8(jq%4).  Blocks nb and nb + 1 make
+        // one 16x16x32 product: contraction slots 0-3 are keys 4gq + r of block
+        // nb, slots 4-7 those of block nb + 1, in V^T and P^T alike.  The
+        // fragments of step u (pair u / TT, output tile u % TT) are read AHEAD
+        // steps ahead of their products, so that the reads' latency hides behind
+        // them.  Also the weights' row sums (a V^T of ones).
+        auto products = [&](const char* vl) __attribute__((always_inline)) {
+            constexpr int U = PV_STEPS, AHEAD = PV_AHEAD;
+            const int trow = 4 * gq + jq / 4;
+            op4_t fa[U], fb[U];
+            auto fetch = [&](int u) __attribute__((always_inline)) {
+                const int nb = 2 * (u / TT), t = u % TT;
+                const uint32_t off = tile_pos<RB>(trow, 2 * t + (jq % 4) / 2) + 8 * (jq % 2);
+                fa[u] = OPS::read_tr(vl + nb * SH::TILE + off);
+                fb[u] = OPS::read_tr(vl + (nb + 1) * SH::TILE + off);
+            };
+#pragma unroll
+            for (int u = 0; u < AHEAD; ++u) fetch(u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (u + AHEAD < U) fetch(u + AHEAD);
+                const int nb = 2 * (u / TT), t = u % TT;
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    acc[c][t] = OPS::pv2(fa[u], fb[u], ph[c][nb], ph[c][nb + 1], acc[c][t]);
+                }
+                if (t == TT - 1) {
+#pragma unroll
+                    for (int c = 0; c < NQ; ++c) {
+                        lsum[c] = OPS::pv2(ones, ones, ph[c][nb], ph[c][nb + 1], lsum[c]);
+                    }
+                }
+            }
+        };
 
-    float l[NQ];
+        // Phase M_j (buffer parity b = j % 2): the products of j - 1 from V
+        // buffer 1 - b (their weights die there), then the scores of j from K
+        // buffer b (born there), so weights and scores never hold registers
+        // together.
+        Ents ec;     // table entries of iteration j + 2 when V_j starts
+        Blk bl[2];   // where iteration j + 1's halves come from when V_j starts
+        // (M_0 has no products, the last M phase, M_NJ, no scores)
+        auto mphase = [&](int j, auto par, auto pv, auto qk) __attribute__((always_inline)) {
+            constexpr int b = decltype(par)::value;
+            // The products are the phase's critical path: this wave issues first
+            // (the SIMD otherwise favours the older wave, group 0's), and its
+            // partner's softmax fills the cycles between the products.
+            __builtin_amdgcn_s_setprio(1);
+            if constexpr (decltype(pv)::value) products((b ? lds_v0 : lds_v1) + kg * SH::SPAN);
+            if constexpr (decltype(qk)::value) {
+                scores((b ? lds_k1 : lds_k0) + kg * SH::SPAN);
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) l[c] = lsum[c][0];
-    // Group 1 leaves its state in LDS (every load has landed and every read
-    // finished before the last barriers); group 0 folds it into its own with
-    // the decode merge's rule.  State element e of row group c (acc[t][r] at
-    // e = 4t + r, then m, l) goes to buffer e % 4, lane-major, so each store
-    // and load is one conflict-free row of 64 words.
-    auto slot = [&](int c, int e) __attribute__((always_inline)) -> float* {
-        char* arr = e % 4 == 0 ? lds_k0 : e % 4 == 1 ? lds_k1 : e % 4 == 2 ? lds_v0 : lds_v1;
-        return reinterpret_cast<float*>(arr) + (((w * NQ + c) * SH::SQ + e / 4) * kWave + lane);
-    };
-    if (kg == 1) {
+                for (int c = 0; c < NQ; ++c)
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
+                    for (int nb = 0; nb < NB; ++nb) pin(sc[c][nb]);
+            }
+            // The phase's order through scheduling: the products' first fragment
+            // reads, then per products step the reads PV_AHEAD steps on (in the
+            // last steps, the scores' q and first K reads) and the step's
+            // products; then per scores block the next block's K reads and the
+            // block's products.
+            m_schedule<decltype(pv)::value, decltype(qk)::value, PV_STEPS, PV_AHEAD, TT, NQ, NB, KK>(
+                std::make_integer_sequence<int, PV_STEPS>{}, std::make_integer_sequence<int, NB>{});
+            __builtin_amdgcn_s_setprio(0);
+        };
+        // Phase V_j: the loads of K_{j+2} into K buffer b (last read by the
+        // group's scores in M_j) and of V_{j+1} into V buffer 1 - b (last read by
+        // the products in M_j), the table entries of j + 3, the softmax of j;
+        // then this wave's loads of K_{j+1} and V_j, issued in V_{j-1}, land
+        // (this phase's stay in flight), so that after the barrier the whole
+        // group's K_{j+1} and V_j are in LDS.
+        auto vphase = [&](int j, auto par) __attribute__((always_inline)) {
+            constexpr int b = decltype(par)::value;
+            Blk b2[2];
+            place(j + 2, ec, b2);
+            issue(b ? lds_k1 : lds_k0, kbase, b2);
+            issue(b ? lds_v0 : lds_v1, vbase, bl);
 #pragma unroll
-            for (int t = 0; t < TT; ++t)
+            for (int h = 0; h < 2; ++h) bl[h] = b2[h];
+            entries(j + 3, ec);
+            softmax(j);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_W));
+        };
+
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        // Prologue: the loads of K_0, V_0 and K_1, then q into LDS; K_0 (and q)
+        // land before the first barrier.
+        {
+            Ents e1;
+            entries(0, ec);
+            entries(1, e1);
+            place(0, ec, bl);
+            issue(lds_k0, kbase, bl);
+            issue(lds_v0, vbase, bl);
+            place(1, e1, bl);
+            issue(lds_k1, kbase, bl);
+            entries(2, ec);
+            if (kg == 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) *slot(c, 4 * t + r) = acc[c][t][r];
-            *slot(c, 4 * TT) = m[c];
-            *slot(c, 4 * TT + 1) = l[c];
+                for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) {
+                        Vec16 v = qv[c][kk];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v.w[e] ^= qsign;
+                        lds_store16(lds_q, tile_pos<RB>(w * SH::ROWS_W + 16 * c + jq, 4 * kk + gq), v);
+                    }
+            }
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_W));
         }
-    }
-    __syncthreads();
-    if (kg == 1) return;
+        phase_barrier();
+        if (kg == 1) phase_barrier();  // group 1 runs one phase behind
+        using T = std::true_type;
+        using F = std::false_type;
+        mphase(0, B0{}, F{}, T{});
+        phase_barrier();
+        vphase(0, B0{});
+        phase_barrier();
+        int j = 1;
+        for (; j + 1 < NJ; j += 2) {
+            mphase(j, B1{}, T{}, T{});
+            phase_barrier();
+            vphase(j, B1{});
+            phase_barrier();
+            mphase(j + 1, B0{}, T{}, T{});
+            phase_barrier();
+            vphase(j + 1, B0{});
+            phase_barrier();
+        }
+        if (j < NJ) {  // j odd
+            mphase(j, B1{}, T{}, T{});
+            phase_barrier();
+            vphase(j, B1{});
+            phase_barrier();
+        }
+        // M_NJ: the last products; then the last phases' zero fills land before
+        // the buffers take group 1's state.
+        if (NJ & 1) mphase(NJ, B1{}, T{}, F{});
+        else mphase(NJ, B0{}, T{}, F{});
+        __builtin_amdgcn_s_waitcnt(0);
+        phase_barrier();
+        if (kg == 0) phase_barrier();
+
+        float l[NQ];
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-        const float m1 = *slot(c, 4 * TT);
-        const float l1 = *slot(c, 4 * TT + 1);
-        const float mm = fmaxf(m[c], m1);
-        const float mr = mm == -INFINITY ? 0.f : mm;
-        const float a0 = __builtin_amdgcn_exp2f(m[c] - mr);
-        const float a1 = __builtin_amdgcn_exp2f(m1 - mr);
-        const float lt = l[c] * a0 + l1 * a1;
-        const int row = wr0 + 16 * c + jq;
-        if (row >= nrows) continue;
-        const float inv = 1.f / lt;
-        char* orow = static_cast<char*>(p.out) + (((int64_t)(q0 + row / G) * Hq + kvh * G + row % G) * D) * 2;
+        for (int c = 0; c < NQ; ++c) l[c] = lsum[c][0];
+        // The key groups' states meet in LDS (every load has landed and every read
+        // finished before the last barriers): each group hands the other the half
+        // of its accumulator that the other writes out (group 0 writes output
+        // tiles 0 .. TH - 1, group 1 the rest) with its m and l, and both fold the
+        // two states with the decode merge's rule, the same arithmetic in either
+        // group.  Element e of group g's handed-over state for row group c goes to
+        // buffer e % 4, lane-major, so each store and load is one conflict-free
+        // row of 64 words.
+        constexpr int TH = SH::TH;
+        auto slot = [&](int g, int c, int e) __attribute__((always_inline)) -> float* {
+            char* arr = e % 4 == 0 ? lds_k0 : e % 4 == 1 ? lds_k1 : e % 4 == 2 ? lds_v0 : lds_v1;
+            return reinterpret_cast<float*>(arr) + ((((g * SH::NW + w) * NQ + c) * SH::HSQ + e / 4) * kWave + lane);
+        };
+        auto hand_over = [&](auto kgc) __attribute__((always_inline)) {
+            constexpr int KG = decltype(kgc)::value;
+            constexpr int GIVE = KG == 0 ? TH : 0;  // first output tile handed over
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
+            for (int c = 0; c < NQ; ++c) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                E::store(orow + (16 * t + 4 * gq + r) * 2, (acc[c][t][r] * a0 + *slot(c, 4 * t + r) * a1) * inv);
-    }
+                for (int h = 0; h < TH; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) *slot(KG, c, 4 * h + r) = acc[c][GIVE + h][r];
+                *slot(KG, c, 4 * TH) = m[c];
+                *slot(KG, c, 4 * TH + 1) = l[c];
+            }
+        };
+        auto fold = [&](auto kgc) __attribute__((always_inline)) {
+            constexpr int KG = decltype(kgc)::value;
+            constexpr int KEEP = KG == 0 ? 0 : TH;  // first output tile written here
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                // group 0's and group 1's m and l
+                const float mo = *slot(1 - KG, c, 4 * TH), lo = *slot(1 - KG, c, 4 * TH + 1);
+                const float m0 = KG == 0 ? m[c] : mo, m1 = KG == 0 ? mo : m[c];
+                const float l0 = KG == 0 ? l[c] : lo, l1 = KG == 0 ? lo : l[c];
+                const float mm = fmaxf(m0, m1);
+                const float mr = mm == -INFINITY ? 0.f : mm;
+                const float a0 = __builtin_amdgcn_exp2f(m0 - mr);
+                const float a1 = __builtin_amdgcn_exp2f(m1 - mr);
+                const float lt = fmaf(l1, a1, l0 * a0);
+                const int row = wr0 + 16 * c + jq;
+                if (row >= nrows) continue;
+                const float inv = 1.f / lt;
+                char* orow = static_cast<char*>(p.out) + (((int64_t)(q0 + row / G) * Hq + kvh * G + row % G) * D) * 2;
+#pragma unroll
+                for (int h = 0; h < TH; ++h) {
+                    float o[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float own = acc[c][KEEP + h][r], oth = *slot(1 - KG, c, 4 * h + r);
+                        o[r] = fmaf(KG == 0 ? oth : own, a1, (KG == 0 ? own : oth) * a0) * inv;
+                    }
+                    store4<E>(orow + (16 * (KEEP + h) + 4 * gq) * 2, o[0], o[1], o[2], o[3]);
+                }
+            }
+        };
+        using K0 = std::integral_constant<int, 0>;
+        using K1 = std::integral_constant<int, 1>;
+        if (kg == 0) hand_over(K0{});
+        else hand_over(K1{});
+        __syncthreads();
+        if (kg == 0) fold(K0{});
+        else fold(K1{});
+    }  // the slot's next tile
 }
 
 // Launch shape: 8 waves (two key groups of four) over 128-row tiles, 32 rows
@@ -948,8 +996,23 @@ static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
     if (tiles > kMaxPrefillTiles || p.num_seqs > 65535 || tiles * p.num_seqs > INT32_MAX ||
         slots * SH::WAVES * kWave > UINT32_MAX)
         return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)slots, (unsigned)tiles);
-    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ>), grid, dim3(SH::WAVES * kWave), 0, stream, p);
+    // W workgroups per KV head, one per compute unit (a workgroup takes the
+    // whole LDS), at most one per rank.
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev != cached_dev) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    const int64_t ranks = tiles * p.num_seqs;
+    const int64_t W = std::max<int64_t>(1, std::min<int64_t>(ranks, cached_cus / p.n_kv_heads));
+    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ>), dim3((unsigned)(W * p.n_kv_heads)),
+                       dim3(SH::WAVES * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
