@@ -278,6 +278,23 @@ def test_prefill_many_sequences_mixed():
     _check(w)
 
 
+def test_prefill_many_tiles_per_workgroup():
+    """64 KV heads and long chunks: with one workgroup per compute unit each
+    workgroup walks about 20 tiles of its head, found eight at a time, so the
+    tile search runs several rounds in one workgroup and the tiles of a round
+    follow one another; every sampled row must come out right and the caches
+    whole."""
+    w = W.build_prefill("many_tiles", [0, 100, 500, 37], [2560, 2000, 2560, 1500], 64, 64, 64, "f16", 3850)
+    rng = np.random.default_rng(3850)
+    ids = set()
+    for s in range(w.num_seqs):
+        a, b = int(w.cu_q[s]), int(w.cu_q[s + 1])
+        for t0 in range(a, b, 128):  # the first and last rows of every tile (G = 1: 128 tokens a tile)
+            ids.update([t0, min(t0 + 127, b - 1)])
+        ids.update(rng.integers(a, b, 8).tolist())
+    _check(w, row_ids=sorted(ids))
+
+
 def test_prefill_rows_past_max_q_len_untouched():
     """max_q_len caps the chunk tokens computed: a chunk longer than it gets its
     first max_q_len tokens' rows (right), the rest stay as they were, and the
