@@ -1732,7 +1732,8 @@ constexpr int kSplitPct = 62;
 // Share of two consecutive workgroups' tiles taken by the first, which runs on
 // an even XCD (see decode_flat_kernel).  Matrix-core engine, GQA-8B layer: 50 %
 // 6.03 TB/s, 52 %: 6.11, 54 %: 6.04, 56 %: 5.95; vector engine, Llama-2-7B
-// layer: 50 % 6.23, 52 %: 6.33, 54 %: 6.37, 56 %: 6.32.
+// layer (four runs each, back to back): 53 % 6.37, 54 %: 6.42, 55 %: 6.39,
+// 56 %: 6.34, 57 %: 6.28.
 constexpr int kXcdPctMfma = 52;
 constexpr int kXcdPctValu = 54;
 
