@@ -460,8 +460,10 @@ __device__ __forceinline__ void m_schedule(std::integer_sequence<int, I...>, std
 // buffers each per group: K_j lives in K buffer j % 2 from V_{j-2} to M_j,
 // V_j in V buffer j % 2 from V_{j-1} to M_{j+1}, so every load is issued
 // three phases before its first reader; each wave waits (vmcnt) for its own
-// loads at the end of the V phase before their reader.
-template <class E, int D, int G, int NW, int NQ>
+// loads at the end of the V phase before their reader.  B16: cache blocks of
+// 16 tokens or more, so both halves of a wave's 16-token tile lie in one
+// block and need one table entry and one placement.
+template <class E, int D, int G, int NW, int NQ, bool B16>
 __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(PrefillParams p) {
     using SH = PrefillShape<D, NW, NQ>;
     static_assert(SH::WAVES == 2 * NW && SH::PER_SIMD == NW / 2, "the launch bounds above");
@@ -645,7 +647,9 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
         // nothing depends on the value until then, so no read waits or branches.
         auto entries = [&](int j, Ents& e) __attribute__((always_inline)) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) e[h] = scalar_entry(table, min(j * STEP + tt0 + 8 * h, tok_lim - 1) >> bshift);
+            for (int h = 0; h < (B16 ? 1 : 2); ++h)
+                e[h] = scalar_entry(table, min(j * STEP + tt0 + 8 * h, tok_lim - 1) >> bshift);
+            if constexpr (B16) e[1] = e[0];
         };
         // Where the halves of iteration j come from; a half past the workgroup's
         // keys, or of an iteration past the group's range, loads zeros (its loads
@@ -653,12 +657,15 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
         // waits are static).
         auto place = [&](int j, const Ents& e, Blk (&bl)[2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < (B16 ? 1 : 2); ++h) {
                 const int tok = j * STEP + tt0 + 8 * h;
                 const bool ok = j < nj && tok < tok_lim && (uint32_t)e[h] < (uint32_t)p.num_blocks;
                 bl[h].off = (uint64_t)(uint32_t)(ok ? e[h] : 0) * blk_bytes;
                 bl[h].size = ok ? min(L - (tok & -bsize), bsize) * (int)row_stride : 0;
             }
+            // (the second half's token is 8 past the first, in the same block, and
+            // tok_lim is a multiple of 16, so its placement is the first's)
+            if constexpr (B16) bl[1] = bl[0];
         };
         // (The slice's LDS offset is formed at each use from one opaque value:
         // left to itself the compiler would keep an offset per buffer and slice
@@ -992,9 +999,7 @@ template <class E, int D, int G, int NW = 4, int NQ = 2>
 static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
     using SH = PrefillShape<D, NW, NQ>;
     const int64_t tiles = ((int64_t)p.max_q_len * G + SH::ROWS - 1) / SH::ROWS;
-    const int64_t slots = (int64_t)p.n_kv_heads * p.num_seqs;
-    if (tiles > kMaxPrefillTiles || p.num_seqs > 65535 || tiles * p.num_seqs > INT32_MAX ||
-        slots * SH::WAVES * kWave > UINT32_MAX)
+    if (tiles > kMaxPrefillTiles || p.num_seqs > 65535 || tiles * p.num_seqs > INT32_MAX)
         return hipErrorInvalidConfiguration;
     // W workgroups per KV head, one per compute unit (a workgroup takes the
     // whole LDS), at most one per rank.
@@ -1011,8 +1016,8 @@ static hipError_t launch_prefill_g(const PrefillParams& p, hipStream_t stream) {
     }
     const int64_t ranks = tiles * p.num_seqs;
     const int64_t W = std::max<int64_t>(1, std::min<int64_t>(ranks, cached_cus / p.n_kv_heads));
-    hipLaunchKernelGGL((prefill_kernel<E, D, G, NW, NQ>), dim3((unsigned)(W * p.n_kv_heads)),
-                       dim3(SH::WAVES * kWave), 0, stream, p);
+    auto kern = p.block_shift >= 4 ? prefill_kernel<E, D, G, NW, NQ, true> : prefill_kernel<E, D, G, NW, NQ, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(W * p.n_kv_heads)), dim3(SH::WAVES * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
