@@ -501,12 +501,13 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
     const int max_len = p.max_blocks << p.block_shift;
     // The slot's tiles are found SH::WAVES at a time, one per wave, and handed
     // over through LDS (the start of the last V buffer, whose first load
-    // comes phases later); lane k holds the round's k-th tile as sequence
-    // << 16 | tile, unsigned (all ones: none; a tile index stays below
-    // kMaxPrefillTiles = 65535), and the sequence's offsets and length are
-    // read again when its turn comes.
+    // comes phases later); lane k of `ref` holds the round's k-th tile as
+    // sequence << 16 | tile, unsigned (all ones: none; a tile index stays
+    // below kMaxPrefillTiles = 65535), and lane k of ref_q0, ref_n and ref_L
+    // its sequence's first query row, chunk length and (clamped) context
+    // length, so a tile starts without another memory round trip.
     static_assert(kMaxPrefillTiles <= 65535, "the tile index fits 16 bits, below 0xffff");
-    int ref = -1;
+    int ref = -1, ref_q0 = 0, ref_n = 0, ref_L = 0;
     for (int item = 0;; ++item) {
         // the last tile's state reads (all four K/V buffers) are done before
         // this tile's loads go into them; its output stores need not be (a
@@ -526,18 +527,27 @@ __global__ __launch_bounds__(2 * NW * kWave, NW / 2) void prefill_kernel(Prefill
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const TileRef t = rank < R ? pick_tile<Q>(p, rank, ln, max_len) : TileRef{-1, 0, 0, 0, 0};
-            if (lane == 0) sh[wv] = t.s < 0 ? -1 : (int)((uint32_t)t.s << 16 | (uint32_t)t.t);
+            if (lane == 0) {
+                sh[wv] = t.s < 0 ? -1 : (int)((uint32_t)t.s << 16 | (uint32_t)t.t);
+                sh[SH::WAVES + wv] = t.q0;
+                sh[2 * SH::WAVES + wv] = t.n;
+                sh[3 * SH::WAVES + wv] = t.L;
+            }
             __syncthreads();
-            ref = lane < SH::WAVES ? sh[lane] : -1;
+            const bool in = lane < SH::WAVES;
+            ref = in ? sh[lane] : -1;
+            ref_q0 = in ? sh[SH::WAVES + lane] : 0;
+            ref_n = in ? sh[2 * SH::WAVES + lane] : 0;
+            ref_L = in ? sh[3 * SH::WAVES + lane] : 0;
         }
         const int cur = __builtin_amdgcn_readlane(ref, k_round);
         if (cur == -1) break;  // ranks past the batch's tiles: so are the slot's later ones
         TileRef tr;
         tr.s = (int)((uint32_t)cur >> 16);
         tr.t = cur & 0xffff;
-        tr.q0 = __builtin_amdgcn_readfirstlane(p.cu_q[tr.s]);
-        tr.n = __builtin_amdgcn_readfirstlane(p.cu_q[tr.s + 1]) - tr.q0;
-        tr.L = min(max(__builtin_amdgcn_readfirstlane(p.context_lens[tr.s]), 0), max_len);
+        tr.q0 = __builtin_amdgcn_readlane(ref_q0, k_round);
+        tr.n = __builtin_amdgcn_readlane(ref_n, k_round);
+        tr.L = __builtin_amdgcn_readlane(ref_L, k_round);
         const int s = tr.s;
         const int q0 = tr.q0;
         const int n = tr.n;
