@@ -90,6 +90,10 @@ CASES = [
     ("bf16", 4, 1, 64, [1000], [300]),
     ("f16", 4, 2, 64, [10, 5, 0], [0, 20, 7]),     # an empty chunk
     ("bf16", 8, 8, 64, [15, 16, 17], [1, 16, 15]),  # chunks at block edges
+    # KV head counts that do not divide the compute units: the grid's slots
+    # per head are rounded down, some compute units idle
+    ("f16", 6, 3, 64, [5, 40, 0], [300, 37, 129]),
+    ("bf16", 40, 5, 128, [64, 0], [257, 200]),
 ]
 
 
